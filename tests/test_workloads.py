@@ -1,0 +1,40 @@
+"""The seeded input generator: bf16 rounding and the named shapes."""
+
+import numpy as np
+
+from long_context_serving_amd import workloads as wl
+
+
+def test_bf16_round_to_nearest_even():
+    # 1 + 2^-8 is exactly half way between 1 and 1 + 2^-7: ties go to even (1.0)
+    x = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -20, -2.5, 3.0e-39], dtype=np.float32)
+    b = wl.to_bf16_bits(x)
+    assert b[0] == 0x3F80
+    assert b[1] == 0x3F80                 # tie -> even mantissa
+    assert b[2] == 0x3F82                 # tie -> even (odd 0x3F81 loses)
+    assert b[3] == 0x3F81                 # above half way -> up
+    assert b[4] == 0xC020
+    # subnormal float32 rounds like any other value
+    assert b[5] == (np.array([3.0e-39], dtype=np.float32).view(np.uint32)[0] + 0x7FFF
+                    + ((np.array([3.0e-39], dtype=np.float32).view(np.uint32)[0] >> 16) & 1)) >> 16
+
+
+def test_named_workload_shapes():
+    assert wl.LLAMA70B_VARLEN_PREFILL.kv_lens == (29127, 12589, 8841, 23919)
+    assert wl.DECODE_32K.fill_lens() == (32767,) * 31
+    assert wl.CHUNKED_PREFILL_128K.fill_lens() == (122880,)
+    assert wl.TINY_MHA.windows == (0, 64, 64, 64)
+    assert wl.MISTRAL7B_PREFILL.all_global().windows == (0,) * 8
+
+
+def test_inputs_are_seeded_and_shaped():
+    w = wl.small_workload("t", (10, 3), (4, 3), 4, 2, 8, 16, (0, 3), seed=42)
+    a = wl.make_inputs(w)
+    b = wl.make_inputs(w)
+    assert a.q.shape == (7, 4, 8) and a.k.shape == (13, 2, 8) and a.v.shape == (13, 2, 8)
+    assert a.q.dtype == np.uint16
+    np.testing.assert_array_equal(a.q, b.q)
+    np.testing.assert_array_equal(a.cu_q, [0, 4, 7])
+    np.testing.assert_array_equal(a.cu_kv, [0, 10, 13])
+    c = wl.make_inputs(w, seed=43)
+    assert not np.array_equal(a.k, c.k)
