@@ -1,0 +1,184 @@
+/*
+ * segkv.h -- C ABI of the segmented paged KV attention library (libsegkv.so).
+ *
+ * What the library computes.  Every (layer, KV head) has a class fixed
+ * offline: a global head attends to the full causal context, a local head
+ * only to a sliding window of the most recent tokens ("Xiaohongshu
+ * Open-Sources RedKnot" page, section "What Happened", item 1).  The KV cache
+ * is kept in pages per (layer, sequence, KV head) and per segment, so each
+ * head stores and reads only the tokens it needs, and every head runs the
+ * same fused variable-length attention with no attention mask built (same
+ * page, item 3; "RedKnot: Head-Aware KV Reuse and SegPagedAttention" page,
+ * section "The Three Core Mechanisms in Detail", third mechanism).
+ *
+ * Visibility (the reading this library implements): key j is visible to the
+ * query at absolute position p iff j <= p and, for a local head with window
+ * W, p - W < j.  Queries are the last tokens of their sequence: query t of a
+ * sequence with kv_len cached tokens and q_len queries sits at
+ * kv_len - q_len + t.  Query head h uses KV head h / (num_q_heads /
+ * num_kv_heads).  Q and K are taken after any position encoding.
+ *
+ * Outputs: o = softmax(scale * q k^T restricted to visible keys) v, rounded
+ * once to bf16, and lse = ln(sum over visible keys of exp(scale * q.k)) in
+ * fp32.
+ *
+ * Memory.  Every device pointer is owned by the caller and must stay valid
+ * until the work enqueued on the context's stream has completed.  Calls are
+ * asynchronous on that stream; outputs are valid after the stream is
+ * synchronised.  The context owns its host allocator state and its small
+ * device tables.  A context is not thread-safe; use one per stream.
+ *
+ * Errors.  Every call validates its arguments and plans its allocation on the
+ * host before anything is enqueued; a call that fails changes no state
+ * (all-or-nothing).  segkv_last_error() returns a message for the last
+ * failure.  After SEGKV_E_DEVICE the context must be destroyed.
+ */
+#ifndef SEGKV_H
+#define SEGKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum segkv_status {
+  SEGKV_OK = 0,
+  SEGKV_E_INVAL = -1,  /* bad argument or shape */
+  SEGKV_E_NOMEM = -2,  /* page pool or a fixed capacity exhausted */
+  SEGKV_E_RANGE = -3,  /* unknown layer or sequence id */
+  SEGKV_E_DEVICE = -4, /* HIP runtime error; destroy the context */
+  SEGKV_E_STATE = -5   /* call not valid in this context or sequence state */
+};
+
+/* Kernel identifiers for segkv_read_timing(). */
+enum segkv_kernel {
+  SEGKV_KERNEL_SCATTER = 0,       /* KV append: writes new rows into pages   */
+  SEGKV_KERNEL_PREFILL = 1,       /* varlen prefill attention                */
+  SEGKV_KERNEL_DECODE_SPLIT = 2,  /* split-KV decode, partial (o, lse)      */
+  SEGKV_KERNEL_COMBINE = 3,       /* log-sum-exp combine of split partials   */
+  SEGKV_KERNEL_COUNT = 4
+};
+
+typedef struct segkv_ctx segkv_ctx;
+
+typedef struct segkv_config {
+  int32_t num_layers;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;   /* num_q_heads % num_kv_heads == 0 */
+  int32_t head_dim;       /* 64 or 128 */
+  int32_t page_size;      /* tokens per page: 16, 32 or 64 */
+  int32_t max_seqs;       /* sequence ids are 0 .. max_seqs-1 */
+  int64_t num_pages;      /* pool capacity in pages, shared by every layer, sequence and KV head (< 2^31) */
+  const int32_t *head_window; /* host [num_layers][num_kv_heads]: 0 = global, W >= 1 = local window of W tokens.
+                                 Copied at create. */
+  float softmax_scale;    /* 0 => 1/sqrt(head_dim) */
+  uint64_t page_order_seed; /* 0 => free list hands out pages in index order; else a seeded permutation */
+  void *k_pool;           /* device bf16 [num_pages][page_size][head_dim]: one page = page_size K rows of one
+                             (layer, sequence, KV head) */
+  void *v_pool;           /* device bf16 [num_pages][head_dim][page_size]: each V page is stored transposed */
+  void *stream;           /* hipStream_t for all device work; NULL = the default stream */
+} segkv_config;
+
+/*
+ * Create a context.  k_pool and v_pool both NULL gives a planning-only
+ * context: it keeps the page allocator and tables on the host and makes no
+ * HIP call at all (appends take k_new = v_new = NULL; prefill and decode
+ * return SEGKV_E_STATE).  Returns SEGKV_OK and *out, or an error with *out =
+ * NULL (message: segkv_last_error(NULL)).
+ */
+int segkv_create(const segkv_config *cfg, segkv_ctx **out);
+
+/* Destroy a context (waits for its stream).  NULL is a no-op. */
+void segkv_destroy(segkv_ctx *ctx);
+
+/*
+ * Append new KV rows to n_seqs sequences of one layer and allocate their
+ * pages.
+ *   seq_ids  host int32 [n_seqs], distinct, each in [0, max_seqs)
+ *   cu_new   host int32 [n_seqs + 1], prefix sums of the new-token counts
+ *   n_query  host int32 [n_seqs]: the last n_query[b] appended tokens of
+ *            sequence b are the queries of the next prefill/decode call
+ *            (0 <= n_query[b] <= new count; 0 = cache fill, no queries).
+ *   k_new, v_new  device bf16 [cu_new[n_seqs]][num_kv_heads][head_dim]
+ * For each KV head the segment keeps the tokens a pending or later query
+ * can see: all tokens for a global head; for a local head of window W the
+ * tokens from max(0, p_q - W + 1) rounded down to a page, where p_q =
+ * kv_len - n_query is the earliest pending query.  Pages wholly below that
+ * start return to the pool and new tokens below it are never stored.  The
+ * segment start never moves back.  Fails with SEGKV_E_NOMEM (no change) if
+ * the pool cannot hold the whole batch.
+ */
+int segkv_append_pages(segkv_ctx *ctx, int32_t layer, int32_t n_seqs, const int32_t *seq_ids,
+                       const int32_t *cu_new, const int32_t *n_query, const void *k_new,
+                       const void *v_new);
+
+/*
+ * Varlen prefill attention of n_seqs sequences of one layer.
+ *   seq_ids  host int32 [n_seqs]
+ *   cu_q     host int32 [n_seqs + 1], prefix sums of q_len; q_len may be 0;
+ *            each q_len must not reach before that sequence's earliest
+ *            pending query (kv_len - q_len >= p_q).
+ *   q        device bf16 [cu_q[n_seqs]][num_q_heads][head_dim]
+ *   o        device bf16 [cu_q[n_seqs]][num_q_heads][head_dim]
+ *   lse      device fp32 [cu_q[n_seqs]][num_q_heads], or NULL
+ */
+int segkv_prefill(segkv_ctx *ctx, int32_t layer, int32_t n_seqs, const int32_t *seq_ids,
+                  const int32_t *cu_q, const void *q, void *o, float *lse);
+
+/*
+ * One-token decode of n_seqs sequences of one layer (the query is the last
+ * cached token of each sequence), by split-KV over the visible pages and a
+ * log-sum-exp combine.  num_q_heads / num_kv_heads must be <= 16.
+ *   q, o     device bf16 [n_seqs][num_q_heads][head_dim]
+ *   lse      device fp32 [n_seqs][num_q_heads], or NULL
+ */
+int segkv_decode(segkv_ctx *ctx, int32_t layer, int32_t n_seqs, const int32_t *seq_ids,
+                 const void *q, void *o, float *lse);
+
+/* Return every page of a sequence (all layers, all heads) to the pool and
+ * reset its length to 0. */
+int segkv_release(segkv_ctx *ctx, int32_t seq_id);
+
+/*
+ * Introspection of one segment.  Writes the logical index of the first token
+ * the segment holds, the sequence length and the page count; copies up to
+ * cap physical page ids (page i holds tokens first_token + i*page_size ...)
+ * into page_ids when it is not NULL.
+ */
+int segkv_page_table(const segkv_ctx *ctx, int32_t layer, int32_t seq_id, int32_t kv_head,
+                     int32_t *first_token, int32_t *kv_len, int32_t *n_pages, int32_t *page_ids,
+                     int32_t cap);
+
+/* Pages currently on the free list, or a negative status. */
+int64_t segkv_free_pages(const segkv_ctx *ctx);
+
+/*
+ * Kernel timing with HIP events recorded on the context's stream around each
+ * launch.  Enabling clears the counters.  segkv_read_timing synchronises the
+ * recorded events and returns the summed duration (ms) and launch count of
+ * one kernel (enum segkv_kernel).
+ */
+int segkv_set_timing(segkv_ctx *ctx, int32_t enable);
+int segkv_read_timing(segkv_ctx *ctx, int32_t kernel, double *total_ms, int64_t *launches);
+
+/*
+ * Tuning knobs (values <= 0 restore the default):
+ *   SEGKV_TUNE_DECODE_PAGES_PER_SPLIT  pages one decode work item streams
+ *   SEGKV_TUNE_PREFILL_SPLIT_TILES     a prefill work item covering more KV
+ *                                      tiles than this is split across
+ *                                      workgroups and merged by the combine
+ *                                      kernel (0 = never split)
+ */
+enum segkv_tune { SEGKV_TUNE_DECODE_PAGES_PER_SPLIT = 0, SEGKV_TUNE_PREFILL_SPLIT_TILES = 1 };
+int segkv_set_tuning(segkv_ctx *ctx, int32_t knob, int64_t value);
+
+/* Message for the last failure on ctx (ctx = NULL: the last failed create). */
+const char *segkv_last_error(const segkv_ctx *ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SEGKV_H */

@@ -1,0 +1,868 @@
+// Host side of libsegkv: the C ABI, the per-head segment page allocator and
+// the per-call device table builder.  Device work is in kernels.hip.
+//
+// The allocator follows the storage rule of SegPagedAttention: KV pages are
+// kept per (layer, head) and per segment, and a head stores only the tokens
+// it needs ("Xiaohongshu Open-Sources RedKnot" page, section "What
+// Happened", item 3; "RedKnot: Head-Aware KV Reuse and SegPagedAttention"
+// page, section "The Three Core Mechanisms in Detail", third mechanism).  A
+// local head keeps the pages that a pending or later query can still see;
+// everything below its window returns to the pool and is never written.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <limits>
+#include <random>
+#include <string>
+#include <vector>
+
+#include "segkv.h"
+#include "segkv_internal.h"
+
+using namespace segkv;
+
+namespace {
+
+thread_local std::string g_create_error;
+
+constexpr int kStages = 4;
+constexpr int kDefaultDecodePagesPerSplit = 16;
+constexpr int kDefaultPrefillSplitTiles = 0;
+
+struct Segment {
+  int32_t first_token = 0;
+  std::vector<int32_t> pages;  // live pages are pages[head, size)
+  size_t head = 0;
+  int32_t n_live() const { return static_cast<int32_t>(pages.size() - head); }
+  const int32_t *live() const { return pages.data() + head; }
+  void drop_front(int32_t n) {
+    head += static_cast<size_t>(n);
+    if (head == pages.size()) {
+      pages.clear();
+      head = 0;
+    } else if (head >= 256 && head * 2 >= pages.size()) {
+      pages.erase(pages.begin(), pages.begin() + static_cast<std::ptrdiff_t>(head));
+      head = 0;
+    }
+  }
+};
+
+struct SeqLayer {
+  int32_t kv_len = 0;
+  int32_t pending_from = 0;  // earliest query position a later call may use
+};
+
+struct TimedLaunch {
+  int kernel;
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+struct segkv_ctx {
+  // configuration
+  int32_t L = 0, Hq = 0, Hkv = 0, D = 0, P = 0, S = 0, G = 0;
+  int64_t num_pages = 0;
+  float scale = 0.f;
+  std::vector<int32_t> window;  // [L][Hkv]
+  uint16_t *k_pool = nullptr;
+  uint16_t *v_pool = nullptr;
+  hipStream_t stream = nullptr;
+  bool planning = false;
+
+  // allocator state
+  std::vector<int32_t> free_list;  // stack; back() is handed out first
+  std::vector<Segment> segs;       // [L][S][Hkv]
+  std::vector<SeqLayer> seq_layer; // [L][S]
+
+  // device metadata and staging
+  char *d_meta = nullptr;
+  size_t d_meta_cap = 0;
+  char *h_stage[kStages] = {};
+  size_t h_stage_cap[kStages] = {};
+  hipEvent_t stage_ev[kStages] = {};
+  bool stage_used[kStages] = {};
+  int stage_next = 0;
+  float *d_part = nullptr;
+  size_t d_part_cap = 0;  // bytes
+
+  // tuning
+  int32_t decode_pps = kDefaultDecodePagesPerSplit;
+  int64_t prefill_split_tiles = kDefaultPrefillSplitTiles;
+
+  // timing
+  bool timing = false;
+  std::vector<TimedLaunch> pending;
+  std::vector<hipEvent_t> event_pool;
+  double tot_ms[SEGKV_KERNEL_COUNT] = {};
+  int64_t launches[SEGKV_KERNEL_COUNT] = {};
+
+  // scratch reused across calls
+  std::vector<int32_t> scratch_i32;
+  std::vector<PrefillItem> scratch_pitems;
+  std::vector<CombineItem> scratch_citems;
+
+  std::string err;
+
+  Segment &seg(int32_t layer, int32_t s, int32_t g) {
+    return segs[(static_cast<size_t>(layer) * S + s) * Hkv + g];
+  }
+  const Segment &seg(int32_t layer, int32_t s, int32_t g) const {
+    return segs[(static_cast<size_t>(layer) * S + s) * Hkv + g];
+  }
+  SeqLayer &sl(int32_t layer, int32_t s) { return seq_layer[static_cast<size_t>(layer) * S + s]; }
+  const SeqLayer &sl(int32_t layer, int32_t s) const {
+    return seq_layer[static_cast<size_t>(layer) * S + s];
+  }
+  int32_t win(int32_t layer, int32_t g) const { return window[static_cast<size_t>(layer) * Hkv + g]; }
+
+  int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    err = buf;
+    return code;
+  }
+  int device_fail(hipError_t e, const char *what) {
+    return fail(SEGKV_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
+  }
+};
+
+namespace {
+
+// Segment start rule for a local head: keep keys a pending or later query
+// can see, i.e. from max(0, p_q - W + 1), rounded down to a page.
+int32_t local_segment_start(int32_t kv_len, int32_t n_query, int32_t window, int32_t page) {
+  int64_t p_q = static_cast<int64_t>(kv_len) - n_query;
+  int64_t lo = std::max<int64_t>(0, p_q - window + 1);
+  return static_cast<int32_t>(page * (lo / page));
+}
+
+// ---- staging / upload --------------------------------------------------
+
+int acquire_stage(segkv_ctx *c, size_t bytes, char **out, int *slot_out) {
+  int slot = c->stage_next;
+  c->stage_next = (c->stage_next + 1) % kStages;
+  if (c->stage_used[slot]) {
+    hipError_t e = hipEventSynchronize(c->stage_ev[slot]);
+    if (e != hipSuccess) return c->device_fail(e, "hipEventSynchronize(stage)");
+  }
+  if (c->h_stage_cap[slot] < bytes) {
+    if (c->h_stage[slot]) {
+      hipError_t e = hipHostFree(c->h_stage[slot]);
+      if (e != hipSuccess) return c->device_fail(e, "hipHostFree");
+      c->h_stage[slot] = nullptr;
+      c->h_stage_cap[slot] = 0;
+    }
+    size_t cap = std::max<size_t>(align_up(bytes, 1 << 16), 1 << 16);
+    hipError_t e = hipHostMalloc(reinterpret_cast<void **>(&c->h_stage[slot]), cap, hipHostMallocDefault);
+    if (e != hipSuccess) return c->device_fail(e, "hipHostMalloc(stage)");
+    c->h_stage_cap[slot] = cap;
+  }
+  *out = c->h_stage[slot];
+  *slot_out = slot;
+  return SEGKV_OK;
+}
+
+int ensure_device_buffer(segkv_ctx *c, char **buf, size_t *cap, size_t bytes, const char *what) {
+  if (*cap >= bytes) return SEGKV_OK;
+  hipError_t e;
+  if (*buf) {
+    e = hipStreamSynchronize(c->stream);  // the old buffer may still be read
+    if (e != hipSuccess) return c->device_fail(e, "hipStreamSynchronize");
+    e = hipFree(*buf);
+    if (e != hipSuccess) return c->device_fail(e, "hipFree");
+    *buf = nullptr;
+    *cap = 0;
+  }
+  size_t ncap = std::max<size_t>(align_up(bytes + bytes / 2, 1 << 16), 1 << 16);
+  e = hipMalloc(reinterpret_cast<void **>(buf), ncap);
+  if (e != hipSuccess) return c->device_fail(e, what);
+  *cap = ncap;
+  return SEGKV_OK;
+}
+
+int upload(segkv_ctx *c, int slot, size_t bytes) {
+  hipError_t e = hipMemcpyAsync(c->d_meta, c->h_stage[slot], bytes, hipMemcpyHostToDevice, c->stream);
+  if (e != hipSuccess) return c->device_fail(e, "hipMemcpyAsync(tables)");
+  e = hipEventRecord(c->stage_ev[slot], c->stream);
+  if (e != hipSuccess) return c->device_fail(e, "hipEventRecord(stage)");
+  c->stage_used[slot] = true;
+  return SEGKV_OK;
+}
+
+// ---- timing --------------------------------------------------------------
+
+int timed_begin(segkv_ctx *c, TimedLaunch *t, int kernel) {
+  if (!c->timing) return SEGKV_OK;
+  t->kernel = kernel;
+  for (hipEvent_t *ev : {&t->start, &t->stop}) {
+    if (!c->event_pool.empty()) {
+      *ev = c->event_pool.back();
+      c->event_pool.pop_back();
+    } else {
+      hipError_t e = hipEventCreate(ev);
+      if (e != hipSuccess) return c->device_fail(e, "hipEventCreate");
+    }
+  }
+  hipError_t e = hipEventRecord(t->start, c->stream);
+  if (e != hipSuccess) return c->device_fail(e, "hipEventRecord");
+  return SEGKV_OK;
+}
+
+int timed_end(segkv_ctx *c, TimedLaunch *t) {
+  if (!c->timing) return SEGKV_OK;
+  hipError_t e = hipEventRecord(t->stop, c->stream);
+  if (e != hipSuccess) return c->device_fail(e, "hipEventRecord");
+  c->pending.push_back(*t);
+  return SEGKV_OK;
+}
+
+int drain_timing(segkv_ctx *c) {
+  for (const TimedLaunch &t : c->pending) {
+    hipError_t e = hipEventSynchronize(t.stop);
+    if (e != hipSuccess) return c->device_fail(e, "hipEventSynchronize(timing)");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, t.start, t.stop);
+    if (e != hipSuccess) return c->device_fail(e, "hipEventElapsedTime");
+    c->tot_ms[t.kernel] += ms;
+    c->launches[t.kernel] += 1;
+    c->event_pool.push_back(t.start);
+    c->event_pool.push_back(t.stop);
+  }
+  c->pending.clear();
+  return SEGKV_OK;
+}
+
+// ---- shared validation ---------------------------------------------------
+
+int check_layer_seqs(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_ids) {
+  if (layer < 0 || layer >= c->L) return c->fail(SEGKV_E_RANGE, "layer %d out of range [0, %d)", layer, c->L);
+  if (n_seqs < 0) return c->fail(SEGKV_E_INVAL, "n_seqs < 0");
+  if (n_seqs > c->S) return c->fail(SEGKV_E_INVAL, "n_seqs %d exceeds max_seqs %d", n_seqs, c->S);
+  if (n_seqs > 0 && !seq_ids) return c->fail(SEGKV_E_INVAL, "seq_ids is NULL");
+  for (int32_t b = 0; b < n_seqs; ++b)
+    if (seq_ids[b] < 0 || seq_ids[b] >= c->S)
+      return c->fail(SEGKV_E_RANGE, "seq id %d out of range [0, %d)", seq_ids[b], c->S);
+  return SEGKV_OK;
+}
+
+// Lays out SeqDesc / SegDesc / page ids for a batch into `dst` (when not
+// null) and returns the byte size of that block.
+size_t seq_tables_bytes(const segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_ids,
+                        int64_t *total_pages) {
+  int64_t pages = 0;
+  for (int32_t b = 0; b < n_seqs; ++b)
+    for (int32_t g = 0; g < c->Hkv; ++g) pages += c->seg(layer, seq_ids[b], g).n_live();
+  *total_pages = pages;
+  size_t bytes = align_up(sizeof(SeqDesc) * n_seqs, 16);
+  bytes += align_up(sizeof(SegDesc) * static_cast<size_t>(n_seqs) * c->Hkv, 16);
+  bytes += align_up(sizeof(int32_t) * static_cast<size_t>(pages), 16);
+  return bytes;
+}
+
+void write_seq_tables(const segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_ids,
+                      const int32_t *q_start, const int32_t *q_len, int64_t total_pages, char *dst) {
+  SeqDesc *sd = reinterpret_cast<SeqDesc *>(dst);
+  SegDesc *gd = reinterpret_cast<SegDesc *>(dst + align_up(sizeof(SeqDesc) * n_seqs, 16));
+  int32_t *pid = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(gd) +
+                                             align_up(sizeof(SegDesc) * static_cast<size_t>(n_seqs) * c->Hkv, 16));
+  int32_t off = 0;
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    const SeqLayer &s = c->sl(layer, seq_ids[b]);
+    sd[b] = SeqDesc{s.kv_len, q_start ? q_start[b] : b, q_len ? q_len[b] : 1, 0};
+    for (int32_t g = 0; g < c->Hkv; ++g) {
+      const Segment &sg = c->seg(layer, seq_ids[b], g);
+      gd[static_cast<size_t>(b) * c->Hkv + g] = SegDesc{sg.first_token, off, sg.n_live(), c->win(layer, g)};
+      std::memcpy(pid + off, sg.live(), sizeof(int32_t) * sg.n_live());
+      off += sg.n_live();
+    }
+  }
+  (void)total_pages;
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+
+extern "C" {
+
+int segkv_create(const segkv_config *cfg, segkv_ctx **out) {
+  g_create_error.clear();
+  auto bad = [](int code, const char *msg) {
+    g_create_error = msg;
+    return code;
+  };
+  if (!out) return bad(SEGKV_E_INVAL, "out is NULL");
+  *out = nullptr;
+  if (!cfg) return bad(SEGKV_E_INVAL, "cfg is NULL");
+  if (cfg->num_layers <= 0) return bad(SEGKV_E_INVAL, "num_layers must be > 0");
+  if (cfg->num_q_heads <= 0 || cfg->num_kv_heads <= 0) return bad(SEGKV_E_INVAL, "head counts must be > 0");
+  if (cfg->num_q_heads % cfg->num_kv_heads)
+    return bad(SEGKV_E_INVAL, "num_q_heads must be a multiple of num_kv_heads");
+  if (cfg->num_q_heads / cfg->num_kv_heads > kPrefillRows)
+    return bad(SEGKV_E_INVAL, "num_q_heads / num_kv_heads must be <= 128");
+  if (cfg->head_dim != 64 && cfg->head_dim != 128) return bad(SEGKV_E_INVAL, "head_dim must be 64 or 128");
+  if (cfg->page_size != 16 && cfg->page_size != 32 && cfg->page_size != 64)
+    return bad(SEGKV_E_INVAL, "page_size must be 16, 32 or 64");
+  if (cfg->max_seqs <= 0) return bad(SEGKV_E_INVAL, "max_seqs must be > 0");
+  if (cfg->num_pages <= 0 || cfg->num_pages > std::numeric_limits<int32_t>::max())
+    return bad(SEGKV_E_INVAL, "num_pages must be in [1, 2^31)");
+  if (!cfg->head_window) return bad(SEGKV_E_INVAL, "head_window is NULL");
+  if ((cfg->k_pool == nullptr) != (cfg->v_pool == nullptr))
+    return bad(SEGKV_E_INVAL, "k_pool and v_pool must both be set or both be NULL");
+  if (!(cfg->softmax_scale >= 0.f) || std::isinf(cfg->softmax_scale))
+    return bad(SEGKV_E_INVAL, "softmax_scale must be finite and >= 0");
+  size_t nwin = static_cast<size_t>(cfg->num_layers) * cfg->num_kv_heads;
+  for (size_t i = 0; i < nwin; ++i)
+    if (cfg->head_window[i] < 0) return bad(SEGKV_E_INVAL, "head_window entries must be >= 0");
+
+  segkv_ctx *c = new (std::nothrow) segkv_ctx();
+  if (!c) return bad(SEGKV_E_NOMEM, "out of host memory");
+  c->L = cfg->num_layers;
+  c->Hq = cfg->num_q_heads;
+  c->Hkv = cfg->num_kv_heads;
+  c->G = c->Hq / c->Hkv;
+  c->D = cfg->head_dim;
+  c->P = cfg->page_size;
+  c->S = cfg->max_seqs;
+  c->num_pages = cfg->num_pages;
+  c->scale = cfg->softmax_scale > 0.f ? cfg->softmax_scale : 1.0f / std::sqrt(static_cast<float>(cfg->head_dim));
+  c->window.assign(cfg->head_window, cfg->head_window + nwin);
+  c->k_pool = static_cast<uint16_t *>(cfg->k_pool);
+  c->v_pool = static_cast<uint16_t *>(cfg->v_pool);
+  c->stream = static_cast<hipStream_t>(cfg->stream);
+  c->planning = cfg->k_pool == nullptr;
+  try {
+    c->segs.resize(static_cast<size_t>(c->L) * c->S * c->Hkv);
+    c->seq_layer.resize(static_cast<size_t>(c->L) * c->S);
+    c->free_list.resize(static_cast<size_t>(c->num_pages));
+  } catch (...) {
+    delete c;
+    return bad(SEGKV_E_NOMEM, "out of host memory for allocator state");
+  }
+  // back() is handed out first: index order for seed 0, else a seeded shuffle.
+  for (int64_t i = 0; i < c->num_pages; ++i) c->free_list[static_cast<size_t>(i)] = static_cast<int32_t>(c->num_pages - 1 - i);
+  if (cfg->page_order_seed) {
+    std::mt19937_64 rng(cfg->page_order_seed);
+    for (size_t i = c->free_list.size(); i > 1; --i) {
+      size_t j = static_cast<size_t>(rng() % i);
+      std::swap(c->free_list[i - 1], c->free_list[j]);
+    }
+  }
+  if (!c->planning) {
+    for (int i = 0; i < kStages; ++i) {
+      hipError_t e = hipEventCreateWithFlags(&c->stage_ev[i], hipEventDisableTiming);
+      if (e != hipSuccess) {
+        g_create_error = std::string("hipEventCreate: ") + hipGetErrorString(e);
+        segkv_destroy(c);
+        return SEGKV_E_DEVICE;
+      }
+    }
+  }
+  *out = c;
+  return SEGKV_OK;
+}
+
+void segkv_destroy(segkv_ctx *c) {
+  if (!c) return;
+  if (!c->planning) {
+    (void)hipStreamSynchronize(c->stream);
+    for (const TimedLaunch &t : c->pending) {
+      (void)hipEventDestroy(t.start);
+      (void)hipEventDestroy(t.stop);
+    }
+    for (hipEvent_t e : c->event_pool) (void)hipEventDestroy(e);
+    for (int i = 0; i < kStages; ++i) {
+      if (c->stage_ev[i]) (void)hipEventDestroy(c->stage_ev[i]);
+      if (c->h_stage[i]) (void)hipHostFree(c->h_stage[i]);
+    }
+    if (c->d_meta) (void)hipFree(c->d_meta);
+    if (c->d_part) (void)hipFree(c->d_part);
+  }
+  delete c;
+}
+
+const char *segkv_last_error(const segkv_ctx *c) { return c ? c->err.c_str() : g_create_error.c_str(); }
+
+int64_t segkv_free_pages(const segkv_ctx *c) {
+  if (!c) return SEGKV_E_INVAL;
+  return static_cast<int64_t>(c->free_list.size());
+}
+
+int segkv_page_table(const segkv_ctx *cc, int32_t layer, int32_t seq_id, int32_t kv_head, int32_t *first_token,
+                     int32_t *kv_len, int32_t *n_pages, int32_t *page_ids, int32_t cap) {
+  segkv_ctx *c = const_cast<segkv_ctx *>(cc);
+  if (!c) return SEGKV_E_INVAL;
+  if (layer < 0 || layer >= c->L) return c->fail(SEGKV_E_RANGE, "layer %d out of range", layer);
+  if (seq_id < 0 || seq_id >= c->S) return c->fail(SEGKV_E_RANGE, "seq id %d out of range", seq_id);
+  if (kv_head < 0 || kv_head >= c->Hkv) return c->fail(SEGKV_E_RANGE, "kv head %d out of range", kv_head);
+  if (cap < 0) return c->fail(SEGKV_E_INVAL, "cap < 0");
+  const Segment &s = c->seg(layer, seq_id, kv_head);
+  if (first_token) *first_token = s.first_token;
+  if (kv_len) *kv_len = c->sl(layer, seq_id).kv_len;
+  if (n_pages) *n_pages = s.n_live();
+  if (page_ids) std::memcpy(page_ids, s.live(), sizeof(int32_t) * std::min<int32_t>(cap, s.n_live()));
+  return SEGKV_OK;
+}
+
+int segkv_release(segkv_ctx *c, int32_t seq_id) {
+  if (!c) return SEGKV_E_INVAL;
+  if (seq_id < 0 || seq_id >= c->S) return c->fail(SEGKV_E_RANGE, "seq id %d out of range", seq_id);
+  for (int32_t layer = 0; layer < c->L; ++layer) {
+    for (int32_t g = 0; g < c->Hkv; ++g) {
+      Segment &s = c->seg(layer, seq_id, g);
+      for (int32_t i = 0; i < s.n_live(); ++i) c->free_list.push_back(s.live()[i]);
+      s.pages.clear();
+      s.head = 0;
+      s.first_token = 0;
+    }
+    c->sl(layer, seq_id) = SeqLayer{};
+  }
+  return SEGKV_OK;
+}
+
+int segkv_append_pages(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_ids, const int32_t *cu_new,
+                       const int32_t *n_query, const void *k_new, const void *v_new) {
+  if (!c) return SEGKV_E_INVAL;
+  int rc = check_layer_seqs(c, layer, n_seqs, seq_ids);
+  if (rc) return rc;
+  if (n_seqs == 0) return SEGKV_OK;
+  if (!cu_new || !n_query) return c->fail(SEGKV_E_INVAL, "cu_new / n_query is NULL");
+  if (cu_new[0] != 0) return c->fail(SEGKV_E_INVAL, "cu_new[0] must be 0");
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    int32_t n = cu_new[b + 1] - cu_new[b];
+    if (cu_new[b + 1] < cu_new[b]) return c->fail(SEGKV_E_INVAL, "cu_new must be non-decreasing");
+    if (n_query[b] < 0 || n_query[b] > n)
+      return c->fail(SEGKV_E_INVAL, "n_query[%d] = %d must be in [0, %d]", b, n_query[b], n);
+    if (static_cast<int64_t>(c->sl(layer, seq_ids[b]).kv_len) + n > std::numeric_limits<int32_t>::max() / 2)
+      return c->fail(SEGKV_E_INVAL, "sequence length overflow");
+    for (int32_t b2 = 0; b2 < b; ++b2)
+      if (seq_ids[b2] == seq_ids[b]) return c->fail(SEGKV_E_INVAL, "duplicate seq id %d in one append", seq_ids[b]);
+  }
+  const int32_t total_new = cu_new[n_seqs];
+  if (c->planning) {
+    if (k_new || v_new) return c->fail(SEGKV_E_STATE, "planning-only context takes k_new = v_new = NULL");
+  } else if (total_new > 0 && (!k_new || !v_new)) {
+    return c->fail(SEGKV_E_INVAL, "k_new / v_new is NULL");
+  }
+
+  // Plan: per (b, g) the new segment start, pages freed and pages needed.
+  const int32_t P = c->P;
+  std::vector<int32_t> &plan = c->scratch_i32;  // [n_seqs*Hkv][4]: new_first, n_free, n_keep, n_add
+  plan.assign(static_cast<size_t>(n_seqs) * c->Hkv * 4, 0);
+  int64_t need = 0, freed = 0;
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    const SeqLayer &s = c->sl(layer, seq_ids[b]);
+    const int32_t new_kv = s.kv_len + (cu_new[b + 1] - cu_new[b]);
+    for (int32_t g = 0; g < c->Hkv; ++g) {
+      const Segment &sg = c->seg(layer, seq_ids[b], g);
+      const int32_t w = c->win(layer, g);
+      int32_t new_first = sg.first_token;
+      if (w > 0) new_first = std::max(new_first, local_segment_start(new_kv, n_query[b], w, P));
+      int32_t n_free = std::min<int32_t>(sg.n_live(), (new_first - sg.first_token) / P);
+      int32_t n_keep = sg.n_live() - n_free;
+      int32_t n_total = new_kv > new_first ? static_cast<int32_t>(ceil_div(new_kv - new_first, P)) : 0;
+      int32_t n_add = std::max(0, n_total - n_keep);
+      int32_t *pl = &plan[(static_cast<size_t>(b) * c->Hkv + g) * 4];
+      pl[0] = new_first;
+      pl[1] = n_free;
+      pl[2] = n_keep;
+      pl[3] = n_add;
+      need += n_add;
+      freed += n_free;
+    }
+  }
+  if (need > static_cast<int64_t>(c->free_list.size()) + freed)
+    return c->fail(SEGKV_E_NOMEM, "page pool exhausted: need %lld pages, %lld free (+%lld reclaimable)",
+                   static_cast<long long>(need), static_cast<long long>(c->free_list.size()),
+                   static_cast<long long>(freed));
+
+  // Count scatter items (pages touched) and size the upload before changing state.
+  int64_t n_items = 0;
+  if (!c->planning) {
+    for (int32_t b = 0; b < n_seqs; ++b) {
+      const SeqLayer &s = c->sl(layer, seq_ids[b]);
+      const int32_t new_kv = s.kv_len + (cu_new[b + 1] - cu_new[b]);
+      for (int32_t g = 0; g < c->Hkv; ++g) {
+        const int32_t *pl = &plan[(static_cast<size_t>(b) * c->Hkv + g) * 4];
+        int32_t tok_lo = std::max(s.kv_len, pl[0]);
+        if (tok_lo >= new_kv) continue;
+        n_items += (new_kv - 1 - pl[0]) / P - (tok_lo - pl[0]) / P + 1;
+      }
+    }
+  }
+  char *stage = nullptr;
+  int slot = 0;
+  const size_t bytes = sizeof(ScatterItem) * static_cast<size_t>(n_items);
+  if (!c->planning && n_items > 0) {
+    rc = acquire_stage(c, bytes, &stage, &slot);
+    if (rc) return rc;
+    rc = ensure_device_buffer(c, &c->d_meta, &c->d_meta_cap, bytes, "hipMalloc(tables)");
+    if (rc) return rc;
+  }
+
+  // Commit: trim, then allocate, then record scatter work.
+  ScatterItem *items = reinterpret_cast<ScatterItem *>(stage);
+  int64_t it = 0;
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    SeqLayer &s = c->sl(layer, seq_ids[b]);
+    const int32_t old_kv = s.kv_len;
+    const int32_t new_kv = old_kv + (cu_new[b + 1] - cu_new[b]);
+    for (int32_t g = 0; g < c->Hkv; ++g) {
+      Segment &sg = c->seg(layer, seq_ids[b], g);
+      const int32_t *pl = &plan[(static_cast<size_t>(b) * c->Hkv + g) * 4];
+      for (int32_t i = 0; i < pl[1]; ++i) c->free_list.push_back(sg.live()[i]);
+      sg.drop_front(pl[1]);
+      sg.first_token = pl[0];
+      for (int32_t i = 0; i < pl[3]; ++i) {
+        sg.pages.push_back(c->free_list.back());
+        c->free_list.pop_back();
+      }
+      if (c->planning) continue;
+      const int32_t tok_lo = std::max(old_kv, pl[0]);
+      if (tok_lo >= new_kv) continue;
+      const int32_t first_idx = (tok_lo - pl[0]) / P;
+      const int32_t last_idx = (new_kv - 1 - pl[0]) / P;
+      for (int32_t pi = first_idx; pi <= last_idx; ++pi) {
+        const int32_t ps = pl[0] + pi * P;
+        const int32_t t0 = std::max(ps, tok_lo);
+        const int32_t t1 = std::min(ps + P, new_kv);
+        ScatterItem &si = items[it++];
+        si.page_id = sg.live()[pi];
+        si.kv_head = g;
+        si.slot_begin = t0 - ps;
+        si.slot_end = t1 - ps;
+        si.src_row = cu_new[b] + (t0 - old_kv);
+        si.zero_tail = pi >= pl[2] ? 1 : 0;
+        si.pad0 = si.pad1 = 0;
+      }
+    }
+    s.kv_len = new_kv;
+    s.pending_from = new_kv - n_query[b];
+  }
+  if (c->planning || n_items == 0) return SEGKV_OK;
+
+  rc = upload(c, slot, bytes);
+  if (rc) return rc;
+  ScatterArgs a;
+  a.k_new = static_cast<const uint16_t *>(k_new);
+  a.v_new = static_cast<const uint16_t *>(v_new);
+  a.k_pool = c->k_pool;
+  a.v_pool = c->v_pool;
+  a.items = reinterpret_cast<const ScatterItem *>(c->d_meta);
+  a.num_kv_heads = c->Hkv;
+  TimedLaunch t{};
+  rc = timed_begin(c, &t, SEGKV_KERNEL_SCATTER);
+  if (rc) return rc;
+  hipError_t e = launch_scatter(a, static_cast<int>(n_items), c->D, c->P, c->stream);
+  if (e != hipSuccess) return c->device_fail(e, "scatter launch");
+  return timed_end(c, &t);
+}
+
+int segkv_prefill(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_ids, const int32_t *cu_q,
+                  const void *q, void *o, float *lse) {
+  if (!c) return SEGKV_E_INVAL;
+  if (c->planning) return c->fail(SEGKV_E_STATE, "prefill needs device pools (planning-only context)");
+  int rc = check_layer_seqs(c, layer, n_seqs, seq_ids);
+  if (rc) return rc;
+  if (n_seqs == 0) return SEGKV_OK;
+  if (!cu_q) return c->fail(SEGKV_E_INVAL, "cu_q is NULL");
+  if (cu_q[0] != 0) return c->fail(SEGKV_E_INVAL, "cu_q[0] must be 0");
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    const int32_t ql = cu_q[b + 1] - cu_q[b];
+    const SeqLayer &s = c->sl(layer, seq_ids[b]);
+    if (ql < 0) return c->fail(SEGKV_E_INVAL, "cu_q must be non-decreasing");
+    if (ql > s.kv_len) return c->fail(SEGKV_E_INVAL, "q_len %d > kv_len %d (seq %d)", ql, s.kv_len, seq_ids[b]);
+    if (ql > 0 && s.kv_len - ql < s.pending_from)
+      return c->fail(SEGKV_E_INVAL,
+                     "seq %d: queries start at %d, before the earliest pending query %d declared at append",
+                     seq_ids[b], s.kv_len - ql, s.pending_from);
+  }
+  const int32_t total_q = cu_q[n_seqs];
+  if (total_q == 0) return SEGKV_OK;
+  if (!q || !o) return c->fail(SEGKV_E_INVAL, "q / o is NULL");
+
+  // Work items: (seq, kv head, q tile) over the KV tiles the rows can see.
+  const int32_t G = c->G;
+  const int32_t rows = kPrefillRows / G;  // query positions per workgroup
+  std::vector<PrefillItem> &items = c->scratch_pitems;
+  std::vector<CombineItem> &citems = c->scratch_citems;
+  items.clear();
+  citems.clear();
+  int32_t n_parts = 0;
+  int64_t max_cost = 0;
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    const int32_t ql = cu_q[b + 1] - cu_q[b];
+    const SeqLayer &s = c->sl(layer, seq_ids[b]);
+    for (int32_t g = 0; g < c->Hkv; ++g) {
+      const int32_t w = c->win(layer, g);
+      for (int32_t qt = 0; qt * rows < ql; ++qt) {
+        const int32_t p_min = s.kv_len - ql + qt * rows;
+        const int32_t p_max = s.kv_len - ql + std::min((qt + 1) * rows, ql) - 1;
+        const int32_t lo = w > 0 ? std::max(0, p_min - w + 1) : 0;
+        const int32_t tb = lo / kTileKeys;
+        const int32_t te = p_max / kTileKeys + 1;
+        const int64_t cost = te - tb;
+        if (c->prefill_split_tiles > 0 && cost > c->prefill_split_tiles) {
+          const int32_t ns = static_cast<int32_t>(ceil_div(cost, c->prefill_split_tiles));
+          const int32_t per = static_cast<int32_t>(ceil_div(cost, ns));
+          const int32_t part0 = n_parts;
+          int32_t k = 0;
+          for (int32_t t0 = tb; t0 < te; t0 += per, ++k)
+            items.push_back(PrefillItem{b, g, qt, t0, std::min(te, t0 + per), n_parts++, 0, 0});
+          citems.push_back(CombineItem{part0, k, cu_q[b] + qt * rows, std::min(rows, ql - qt * rows), g * G, G, 0, 0});
+          max_cost = std::max<int64_t>(max_cost, per);
+        } else {
+          items.push_back(PrefillItem{b, g, qt, tb, te, -1, 0, 0});
+          max_cost = std::max(max_cost, cost);
+        }
+      }
+    }
+  }
+  // Longest first (counting sort on tile count, stable).
+  {
+    std::vector<int32_t> &cnt = c->scratch_i32;
+    cnt.assign(static_cast<size_t>(max_cost) + 2, 0);
+    for (const PrefillItem &x : items) cnt[static_cast<size_t>(max_cost - (x.tile_end - x.tile_begin))]++;
+    int32_t acc = 0;
+    for (int32_t &v : cnt) {
+      int32_t t = v;
+      v = acc;
+      acc += t;
+    }
+    std::vector<PrefillItem> sorted(items.size());
+    for (const PrefillItem &x : items) sorted[static_cast<size_t>(cnt[static_cast<size_t>(max_cost - (x.tile_end - x.tile_begin))]++)] = x;
+    items.swap(sorted);
+  }
+
+  int64_t total_pages = 0;
+  const size_t tbytes = seq_tables_bytes(c, layer, n_seqs, seq_ids, &total_pages);
+  const size_t ibytes = align_up(sizeof(PrefillItem) * items.size(), 16);
+  const size_t cbytes = sizeof(CombineItem) * citems.size();
+  const size_t bytes = tbytes + ibytes + cbytes;
+  char *stage = nullptr;
+  int slot = 0;
+  rc = acquire_stage(c, bytes, &stage, &slot);
+  if (rc) return rc;
+  rc = ensure_device_buffer(c, &c->d_meta, &c->d_meta_cap, bytes, "hipMalloc(tables)");
+  if (rc) return rc;
+  const size_t part_bytes = static_cast<size_t>(n_parts) * kPrefillRows * (c->D + 1) * sizeof(float);
+  if (n_parts > 0) {
+    rc = ensure_device_buffer(c, reinterpret_cast<char **>(&c->d_part), &c->d_part_cap, part_bytes,
+                              "hipMalloc(partials)");
+    if (rc) return rc;
+  }
+  std::vector<int32_t> qs(n_seqs), ql(n_seqs);
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    qs[b] = cu_q[b];
+    ql[b] = cu_q[b + 1] - cu_q[b];
+  }
+  write_seq_tables(c, layer, n_seqs, seq_ids, qs.data(), ql.data(), total_pages, stage);
+  std::memcpy(stage + tbytes, items.data(), sizeof(PrefillItem) * items.size());
+  if (cbytes) std::memcpy(stage + tbytes + ibytes, citems.data(), cbytes);
+  rc = upload(c, slot, bytes);
+  if (rc) return rc;
+
+  PrefillArgs a;
+  a.q = static_cast<const uint16_t *>(q);
+  a.o = static_cast<uint16_t *>(o);
+  a.lse = lse;
+  a.k_pool = c->k_pool;
+  a.v_pool = c->v_pool;
+  a.seqs = reinterpret_cast<const SeqDesc *>(c->d_meta);
+  a.segs = reinterpret_cast<const SegDesc *>(c->d_meta + align_up(sizeof(SeqDesc) * n_seqs, 16));
+  a.page_ids = reinterpret_cast<const int32_t *>(reinterpret_cast<const char *>(a.segs) +
+                                                 align_up(sizeof(SegDesc) * static_cast<size_t>(n_seqs) * c->Hkv, 16));
+  a.items = reinterpret_cast<const PrefillItem *>(c->d_meta + tbytes);
+  a.part_o = c->d_part;
+  a.part_lse = c->d_part ? c->d_part + static_cast<size_t>(n_parts) * kPrefillRows * c->D : nullptr;
+  a.num_q_heads = c->Hq;
+  a.num_kv_heads = c->Hkv;
+  a.group = G;
+  a.rows_per_tile = rows;
+  a.scale = c->scale;
+  a.scale_log2 = c->scale * 1.4426950408889634f;
+  TimedLaunch t{};
+  rc = timed_begin(c, &t, SEGKV_KERNEL_PREFILL);
+  if (rc) return rc;
+  hipError_t e = launch_prefill(a, static_cast<int>(items.size()), c->D, c->P, c->stream);
+  if (e != hipSuccess) return c->device_fail(e, "prefill launch");
+  rc = timed_end(c, &t);
+  if (rc) return rc;
+  if (!citems.empty()) {
+    CombineArgs ca;
+    ca.part_o = a.part_o;
+    ca.part_lse = a.part_lse;
+    ca.items = reinterpret_cast<const CombineItem *>(c->d_meta + tbytes + ibytes);
+    ca.o = static_cast<uint16_t *>(o);
+    ca.lse = lse;
+    ca.num_q_heads = c->Hq;
+    ca.slot_rows = kPrefillRows;
+    TimedLaunch t2{};
+    rc = timed_begin(c, &t2, SEGKV_KERNEL_COMBINE);
+    if (rc) return rc;
+    e = launch_combine(ca, static_cast<int>(citems.size()), c->D, c->stream);
+    if (e != hipSuccess) return c->device_fail(e, "combine launch");
+    rc = timed_end(c, &t2);
+    if (rc) return rc;
+  }
+  return SEGKV_OK;
+}
+
+int segkv_decode(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_ids, const void *q, void *o,
+                 float *lse) {
+  if (!c) return SEGKV_E_INVAL;
+  if (c->planning) return c->fail(SEGKV_E_STATE, "decode needs device pools (planning-only context)");
+  int rc = check_layer_seqs(c, layer, n_seqs, seq_ids);
+  if (rc) return rc;
+  if (n_seqs == 0) return SEGKV_OK;
+  if (c->G > kDecodeCols) return c->fail(SEGKV_E_INVAL, "decode supports num_q_heads / num_kv_heads <= %d", kDecodeCols);
+  if (!q || !o) return c->fail(SEGKV_E_INVAL, "q / o is NULL");
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    const SeqLayer &s = c->sl(layer, seq_ids[b]);
+    if (s.kv_len < 1) return c->fail(SEGKV_E_STATE, "seq %d is empty", seq_ids[b]);
+    if (s.pending_from > s.kv_len - 1)
+      return c->fail(SEGKV_E_INVAL, "seq %d: the last token was not appended as a query (n_query >= 1)", seq_ids[b]);
+  }
+  const int32_t P = c->P;
+  const int32_t pps = c->decode_pps;
+  std::vector<DecodeItem> ditems;
+  std::vector<CombineItem> &citems = c->scratch_citems;
+  citems.clear();
+  ditems.reserve(static_cast<size_t>(n_seqs) * c->Hkv * 4);
+  int32_t n_parts = 0;
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    const SeqLayer &s = c->sl(layer, seq_ids[b]);
+    const int32_t p = s.kv_len - 1;
+    for (int32_t g = 0; g < c->Hkv; ++g) {
+      const Segment &sg = c->seg(layer, seq_ids[b], g);
+      const int32_t w = c->win(layer, g);
+      const int32_t lo = w > 0 ? std::max(0, p - w + 1) : 0;
+      const int32_t pg_lo = (lo - sg.first_token) / P;
+      const int32_t pg_hi = (p - sg.first_token) / P + 1;
+      const int32_t part0 = n_parts;
+      for (int32_t p0 = pg_lo; p0 < pg_hi; p0 += pps)
+        ditems.push_back(DecodeItem{b, g, p0, std::min(pg_hi, p0 + pps), n_parts++, 0, 0, 0});
+      citems.push_back(CombineItem{part0, n_parts - part0, b, 1, g * c->G, c->G, 0, 0});
+    }
+  }
+  // Longer items (full splits) first.
+  std::stable_sort(ditems.begin(), ditems.end(), [](const DecodeItem &x, const DecodeItem &y) {
+    return (x.page_end - x.page_begin) > (y.page_end - y.page_begin);
+  });
+
+  int64_t total_pages = 0;
+  const size_t tbytes = seq_tables_bytes(c, layer, n_seqs, seq_ids, &total_pages);
+  const size_t ibytes = align_up(sizeof(DecodeItem) * ditems.size(), 16);
+  const size_t cbytes = sizeof(CombineItem) * citems.size();
+  const size_t bytes = tbytes + ibytes + cbytes;
+  char *stage = nullptr;
+  int slot = 0;
+  rc = acquire_stage(c, bytes, &stage, &slot);
+  if (rc) return rc;
+  rc = ensure_device_buffer(c, &c->d_meta, &c->d_meta_cap, bytes, "hipMalloc(tables)");
+  if (rc) return rc;
+  const size_t part_bytes = static_cast<size_t>(n_parts) * kDecodeCols * (c->D + 1) * sizeof(float);
+  rc = ensure_device_buffer(c, reinterpret_cast<char **>(&c->d_part), &c->d_part_cap, part_bytes,
+                            "hipMalloc(partials)");
+  if (rc) return rc;
+  write_seq_tables(c, layer, n_seqs, seq_ids, nullptr, nullptr, total_pages, stage);
+  std::memcpy(stage + tbytes, ditems.data(), sizeof(DecodeItem) * ditems.size());
+  std::memcpy(stage + tbytes + ibytes, citems.data(), cbytes);
+  rc = upload(c, slot, bytes);
+  if (rc) return rc;
+
+  DecodeArgs a;
+  a.q = static_cast<const uint16_t *>(q);
+  a.k_pool = c->k_pool;
+  a.v_pool = c->v_pool;
+  a.seqs = reinterpret_cast<const SeqDesc *>(c->d_meta);
+  a.segs = reinterpret_cast<const SegDesc *>(c->d_meta + align_up(sizeof(SeqDesc) * n_seqs, 16));
+  a.page_ids = reinterpret_cast<const int32_t *>(reinterpret_cast<const char *>(a.segs) +
+                                                 align_up(sizeof(SegDesc) * static_cast<size_t>(n_seqs) * c->Hkv, 16));
+  a.items = reinterpret_cast<const DecodeItem *>(c->d_meta + tbytes);
+  a.part_o = c->d_part;
+  a.part_lse = c->d_part + static_cast<size_t>(n_parts) * kDecodeCols * c->D;
+  a.num_q_heads = c->Hq;
+  a.num_kv_heads = c->Hkv;
+  a.group = c->G;
+  a.scale = c->scale;
+  a.scale_log2 = c->scale * 1.4426950408889634f;
+  TimedLaunch t{};
+  rc = timed_begin(c, &t, SEGKV_KERNEL_DECODE_SPLIT);
+  if (rc) return rc;
+  hipError_t e = launch_decode(a, static_cast<int>(ditems.size()), c->D, c->P, c->stream);
+  if (e != hipSuccess) return c->device_fail(e, "decode launch");
+  rc = timed_end(c, &t);
+  if (rc) return rc;
+
+  CombineArgs ca;
+  ca.part_o = a.part_o;
+  ca.part_lse = a.part_lse;
+  ca.items = reinterpret_cast<const CombineItem *>(c->d_meta + tbytes + ibytes);
+  ca.o = static_cast<uint16_t *>(o);
+  ca.lse = lse;
+  ca.num_q_heads = c->Hq;
+  ca.slot_rows = kDecodeCols;
+  TimedLaunch t2{};
+  rc = timed_begin(c, &t2, SEGKV_KERNEL_COMBINE);
+  if (rc) return rc;
+  e = launch_combine(ca, static_cast<int>(citems.size()), c->D, c->stream);
+  if (e != hipSuccess) return c->device_fail(e, "combine launch");
+  return timed_end(c, &t2);
+}
+
+int segkv_set_timing(segkv_ctx *c, int32_t enable) {
+  if (!c) return SEGKV_E_INVAL;
+  if (c->planning) return c->fail(SEGKV_E_STATE, "timing needs a device context");
+  int rc = drain_timing(c);
+  if (rc) return rc;
+  for (int k = 0; k < SEGKV_KERNEL_COUNT; ++k) {
+    c->tot_ms[k] = 0.0;
+    c->launches[k] = 0;
+  }
+  c->timing = enable != 0;
+  return SEGKV_OK;
+}
+
+int segkv_read_timing(segkv_ctx *c, int32_t kernel, double *total_ms, int64_t *launches) {
+  if (!c) return SEGKV_E_INVAL;
+  if (kernel < 0 || kernel >= SEGKV_KERNEL_COUNT) return c->fail(SEGKV_E_INVAL, "unknown kernel id %d", kernel);
+  int rc = drain_timing(c);
+  if (rc) return rc;
+  if (total_ms) *total_ms = c->tot_ms[kernel];
+  if (launches) *launches = c->launches[kernel];
+  return SEGKV_OK;
+}
+
+int segkv_set_tuning(segkv_ctx *c, int32_t knob, int64_t value) {
+  if (!c) return SEGKV_E_INVAL;
+  switch (knob) {
+    case SEGKV_TUNE_DECODE_PAGES_PER_SPLIT:
+      if (value > (1 << 20)) return c->fail(SEGKV_E_INVAL, "pages per split too large");
+      c->decode_pps = value > 0 ? static_cast<int32_t>(value) : kDefaultDecodePagesPerSplit;
+      return SEGKV_OK;
+    case SEGKV_TUNE_PREFILL_SPLIT_TILES:
+      c->prefill_split_tiles = value > 0 ? value : kDefaultPrefillSplitTiles;
+      return SEGKV_OK;
+    default:
+      return c->fail(SEGKV_E_INVAL, "unknown tuning knob %d", knob);
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,153 @@
+// Internal layout shared by the host library and its HIP kernels.
+//
+// Device tables are rebuilt on the host for every call and uploaded with
+// one host-to-device copy into the context's metadata buffer, in this order:
+//   SeqDesc  [n_seqs]
+//   SegDesc  [n_seqs * num_kv_heads]
+//   int32    page ids of every listed segment (SegDesc::page_off indexes here)
+//   work items of the call (ScatterItem, PrefillItem or DecodeItem)
+//   combine items (CombineItem), when the call has split work
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace segkv {
+
+constexpr int kTileKeys = 64;      // keys per prefill KV tile (one LDS stage)
+constexpr int kPrefillRows = 128;  // (query position, query head) rows per prefill workgroup
+constexpr int kPrefillThreads = 256;
+constexpr int kDecodeThreads = 256;
+constexpr int kDecodeCols = 16;    // query heads handled by one decode work item (GQA group, padded)
+constexpr int kScatterThreads = 256;
+
+struct SeqDesc {
+  int32_t kv_len;   // tokens in the sequence (this layer)
+  int32_t q_start;  // first row of this sequence in q / o
+  int32_t q_len;    // queries (the last q_len tokens)
+  int32_t pad;
+};
+
+struct SegDesc {
+  int32_t first_token;  // logical index of the first token on page 0 (multiple of page_size)
+  int32_t page_off;     // index of page 0 in the page id table
+  int32_t n_pages;
+  int32_t window;       // 0 = global, W >= 1 = local
+};
+
+// One page touched by an append: K rows [slot_begin, slot_end) come from
+// new-token rows src_row ..; when zero_tail is set the page is new and slots
+// [slot_end, page_size) are cleared so that no live page holds stale bits.
+struct ScatterItem {
+  int32_t page_id;
+  int32_t kv_head;
+  int32_t slot_begin;
+  int32_t slot_end;
+  int32_t src_row;
+  int32_t zero_tail;
+  int32_t pad0, pad1;
+};
+
+// One prefill workgroup: rows [qtile*rows_per_tile ...) of (sequence, KV head
+// group) over KV tiles [tile_begin, tile_end).  part >= 0 writes fp32
+// partial results to partial slot `part` instead of the final output.
+struct PrefillItem {
+  int32_t seq;
+  int32_t kv_head;
+  int32_t qtile;
+  int32_t tile_begin;
+  int32_t tile_end;
+  int32_t part;
+  int32_t pad0, pad1;
+};
+
+// One decode workgroup: pages [page_begin, page_end) of segment (seq, kv_head),
+// partial results to slot `part`.
+struct DecodeItem {
+  int32_t seq;
+  int32_t kv_head;
+  int32_t page_begin;
+  int32_t page_end;
+  int32_t part;
+  int32_t pad0, pad1, pad2;
+};
+
+// One combine workgroup: merge partial slots [part_begin, part_begin+n_parts)
+// for `rows` output rows starting at row `out_row` (row = query token), each
+// row holding `heads` query heads starting at head `head0`.
+struct CombineItem {
+  int32_t part_begin;
+  int32_t n_parts;
+  int32_t out_row;
+  int32_t rows;
+  int32_t head0;
+  int32_t heads;
+  int32_t pad0, pad1;
+};
+
+struct ScatterArgs {
+  const uint16_t *k_new;
+  const uint16_t *v_new;
+  uint16_t *k_pool;
+  uint16_t *v_pool;
+  const ScatterItem *items;
+  int32_t num_kv_heads;
+};
+
+struct PrefillArgs {
+  const uint16_t *q;
+  uint16_t *o;
+  float *lse;
+  const uint16_t *k_pool;
+  const uint16_t *v_pool;
+  const SeqDesc *seqs;
+  const SegDesc *segs;
+  const int32_t *page_ids;
+  const PrefillItem *items;
+  float *part_o;    // [parts][kPrefillRows][head_dim] fp32, normalised
+  float *part_lse;  // [parts][kPrefillRows] natural log
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;          // num_q_heads / num_kv_heads
+  int32_t rows_per_tile;  // query positions per workgroup = kPrefillRows / group
+  float scale_log2;       // softmax scale * log2(e)
+  float scale;
+};
+
+struct DecodeArgs {
+  const uint16_t *q;
+  const uint16_t *k_pool;
+  const uint16_t *v_pool;
+  const SeqDesc *seqs;
+  const SegDesc *segs;
+  const int32_t *page_ids;
+  const DecodeItem *items;
+  float *part_o;    // [parts][kDecodeCols][head_dim]
+  float *part_lse;  // [parts][kDecodeCols]
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;
+  float scale_log2;
+  float scale;
+};
+
+// Partial slot layout for combine: slot s holds `slot_rows` rows of
+// head_dim fp32 values and slot_rows lse values; row r of a slot maps to
+// output (token row out_row + r / heads, head head0 + r % heads).
+struct CombineArgs {
+  const float *part_o;
+  const float *part_lse;
+  const CombineItem *items;
+  uint16_t *o;
+  float *lse;
+  int32_t num_q_heads;
+  int32_t slot_rows;
+};
+
+// Launchers (kernels.hip).  Return the launch status.
+hipError_t launch_scatter(const ScatterArgs &a, int n_items, int head_dim, int page_size, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs &a, int n_items, int head_dim, int page_size, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs &a, int n_items, int head_dim, int page_size, hipStream_t s);
+hipError_t launch_combine(const CombineArgs &a, int n_items, int head_dim, hipStream_t s);
+
+}  // namespace segkv

@@ -1,0 +1,306 @@
+"""Thin ctypes binding of libsegkv (include/segkv.h).
+
+Argument marshalling only: every step of the attention path runs in the HIP
+library.  PyTorch supplies device memory (tensors) and the stream.  The
+binding never computes attention itself, and raises if the library has not
+been built.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+from .build import LIB_PATH
+
+SEGKV_OK = 0
+SEGKV_E_INVAL = -1
+SEGKV_E_NOMEM = -2
+SEGKV_E_RANGE = -3
+SEGKV_E_DEVICE = -4
+SEGKV_E_STATE = -5
+
+KERNEL_SCATTER = 0
+KERNEL_PREFILL = 1
+KERNEL_DECODE_SPLIT = 2
+KERNEL_COMBINE = 3
+
+TUNE_DECODE_PAGES_PER_SPLIT = 0
+TUNE_PREFILL_SPLIT_TILES = 1
+
+# Every entry point include/segkv.h declares.
+EXPORTED = (
+    "segkv_create", "segkv_destroy", "segkv_append_pages", "segkv_prefill", "segkv_decode",
+    "segkv_release", "segkv_page_table", "segkv_free_pages", "segkv_set_timing",
+    "segkv_read_timing", "segkv_set_tuning", "segkv_last_error",
+)
+
+
+class SegKVError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"segkv error {code}: {msg}")
+        self.code = code
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [
+        ("num_layers", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("max_seqs", ctypes.c_int32),
+        ("num_pages", ctypes.c_int64),
+        ("head_window", ctypes.POINTER(ctypes.c_int32)),
+        ("softmax_scale", ctypes.c_float),
+        ("page_order_seed", ctypes.c_uint64),
+        ("k_pool", ctypes.c_void_p),
+        ("v_pool", ctypes.c_void_p),
+        ("stream", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None):
+    """Load libsegkv.so (built in-tree by long_context_serving_amd.build)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"{p} is missing: build it with `python -m long_context_serving_amd.build` "
+                          "(there is no fallback path)")
+    lib = ctypes.CDLL(p)
+    i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    pi32 = ctypes.POINTER(ctypes.c_int32)
+    lib.segkv_create.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(vp)]
+    lib.segkv_create.restype = ctypes.c_int
+    lib.segkv_destroy.argtypes = [vp]
+    lib.segkv_destroy.restype = None
+    lib.segkv_append_pages.argtypes = [vp, i32, i32, pi32, pi32, pi32, vp, vp]
+    lib.segkv_append_pages.restype = ctypes.c_int
+    lib.segkv_prefill.argtypes = [vp, i32, i32, pi32, pi32, vp, vp, vp]
+    lib.segkv_prefill.restype = ctypes.c_int
+    lib.segkv_decode.argtypes = [vp, i32, i32, pi32, vp, vp, vp]
+    lib.segkv_decode.restype = ctypes.c_int
+    lib.segkv_release.argtypes = [vp, i32]
+    lib.segkv_release.restype = ctypes.c_int
+    lib.segkv_page_table.argtypes = [vp, i32, i32, i32, pi32, pi32, pi32, pi32, i32]
+    lib.segkv_page_table.restype = ctypes.c_int
+    lib.segkv_free_pages.argtypes = [vp]
+    lib.segkv_free_pages.restype = i64
+    lib.segkv_set_timing.argtypes = [vp, i32]
+    lib.segkv_set_timing.restype = ctypes.c_int
+    lib.segkv_read_timing.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
+    lib.segkv_read_timing.restype = ctypes.c_int
+    lib.segkv_set_tuning.argtypes = [vp, i32, i64]
+    lib.segkv_set_tuning.restype = ctypes.c_int
+    lib.segkv_last_error.argtypes = [vp]
+    lib.segkv_last_error.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _i32(xs) -> "ctypes.Array":
+    arr = np.ascontiguousarray(np.asarray(xs, dtype=np.int32))
+    return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def bf16_tensor(bits: np.ndarray, device="cuda"):
+    """uint16 bf16 bit patterns -> torch.bfloat16 tensor on ``device``."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+    return t.to(device) if device is not None else t
+
+
+def bf16_bits(t) -> np.ndarray:
+    """torch.bfloat16 tensor -> uint16 bit patterns on the host."""
+    import torch
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _check_dev(t, name, dtype=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+class SegKV:
+    """One libsegkv context.
+
+    ``planning=True`` builds a host-only context (allocator and page tables,
+    no device pools, no HIP call).  Otherwise K/V pools are allocated with
+    torch on the current device unless given: K [num_pages][page][D], V
+    [num_pages][D][page] (each V page transposed).
+    """
+
+    def __init__(self, num_layers: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                 page_size: int, max_seqs: int, num_pages: int, head_window: Sequence[int],
+                 softmax_scale: float = 0.0, page_order_seed: int = 0, planning: bool = False,
+                 k_pool=None, v_pool=None, stream=None):
+        self._lib = load_library()
+        self.num_layers, self.num_q_heads, self.num_kv_heads = num_layers, num_q_heads, num_kv_heads
+        self.head_dim, self.page_size, self.max_seqs, self.num_pages = head_dim, page_size, max_seqs, num_pages
+        self._win, win_p = _i32(np.asarray(head_window, dtype=np.int32).reshape(-1))
+        self.k_pool = self.v_pool = None
+        self.stream = None
+        cfg = _Config()
+        cfg.num_layers, cfg.num_q_heads, cfg.num_kv_heads = num_layers, num_q_heads, num_kv_heads
+        cfg.head_dim, cfg.page_size, cfg.max_seqs, cfg.num_pages = head_dim, page_size, max_seqs, num_pages
+        cfg.head_window = win_p
+        cfg.softmax_scale = softmax_scale
+        cfg.page_order_seed = page_order_seed
+        if not planning:
+            import torch
+            if k_pool is None:
+                k_pool = torch.empty((num_pages, page_size, head_dim), dtype=torch.bfloat16, device="cuda")
+            if v_pool is None:
+                v_pool = torch.empty((num_pages, head_dim, page_size), dtype=torch.bfloat16, device="cuda")
+            _check_dev(k_pool, "k_pool", torch.bfloat16)
+            _check_dev(v_pool, "v_pool", torch.bfloat16)
+            if k_pool.numel() != num_pages * page_size * head_dim or v_pool.numel() != k_pool.numel():
+                raise ValueError("pool sizes do not match num_pages * page_size * head_dim")
+            self.k_pool, self.v_pool = k_pool, v_pool
+            self.stream = stream if stream is not None else torch.cuda.current_stream()
+            cfg.k_pool = k_pool.data_ptr()
+            cfg.v_pool = v_pool.data_ptr()
+            cfg.stream = self.stream.cuda_stream
+        self._cfg = cfg
+        h = ctypes.c_void_p()
+        rc = self._lib.segkv_create(ctypes.byref(cfg), ctypes.byref(h))
+        if rc != SEGKV_OK:
+            raise SegKVError(rc, self._lib.segkv_last_error(None).decode())
+        self._h = h
+
+    # -- plumbing ----------------------------------------------------------
+    def _check(self, rc: int):
+        if rc != SEGKV_OK:
+            raise SegKVError(rc, self.last_error())
+        return rc
+
+    def last_error(self) -> str:
+        return self._lib.segkv_last_error(self._h).decode()
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.segkv_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    # -- C ABI mirrors -----------------------------------------------------
+    def append_pages(self, layer: int, seq_ids, new_lens, n_query, k_new=None, v_new=None) -> int:
+        """Append new_lens[b] K/V rows to seq_ids[b]; the last n_query[b]
+        become pending queries.  k_new/v_new: bf16 [sum new][Hkv][D] (None in
+        a planning-only context)."""
+        ids, ids_p = _i32(seq_ids)
+        cu, cu_p = _i32(np.concatenate([[0], np.cumsum(np.asarray(new_lens, dtype=np.int64))]))
+        nq, nq_p = _i32(n_query)
+        if len(nq) != len(ids) or len(cu) != len(ids) + 1:
+            raise ValueError("seq_ids, new_lens and n_query must have the same length")
+        kp = vp = None
+        if k_new is not None or v_new is not None:
+            import torch
+            for t, name in ((k_new, "k_new"), (v_new, "v_new")):
+                _check_dev(t, name, torch.bfloat16)
+                if tuple(t.shape) != (int(cu[-1]), self.num_kv_heads, self.head_dim):
+                    raise ValueError(f"{name} must be [{int(cu[-1])}, {self.num_kv_heads}, {self.head_dim}]")
+            kp, vp = k_new.data_ptr(), v_new.data_ptr()
+        return self._check(self._lib.segkv_append_pages(self._h, layer, len(ids), ids_p, cu_p, nq_p, kp, vp))
+
+    def prefill(self, layer: int, seq_ids, q_lens, q, o=None, lse=None, want_lse: bool = True):
+        """Varlen prefill; q bf16 [sum q_lens][Hq][D].  Returns (o, lse)."""
+        import torch
+        ids, ids_p = _i32(seq_ids)
+        cu, cu_p = _i32(np.concatenate([[0], np.cumsum(np.asarray(q_lens, dtype=np.int64))]))
+        if len(cu) != len(ids) + 1:
+            raise ValueError("seq_ids and q_lens must have the same length")
+        nq = int(cu[-1])
+        _check_dev(q, "q", torch.bfloat16)
+        if tuple(q.shape) != (nq, self.num_q_heads, self.head_dim):
+            raise ValueError(f"q must be [{nq}, {self.num_q_heads}, {self.head_dim}]")
+        if o is None:
+            o = torch.empty_like(q)
+        _check_dev(o, "o", torch.bfloat16)
+        if o.shape != q.shape:
+            raise ValueError("o must have q's shape")
+        if lse is None and want_lse:
+            lse = torch.empty((nq, self.num_q_heads), dtype=torch.float32, device=q.device)
+        if lse is not None:
+            _check_dev(lse, "lse", torch.float32)
+            if tuple(lse.shape) != (nq, self.num_q_heads):
+                raise ValueError("lse must be [sum q_lens, Hq]")
+        self._check(self._lib.segkv_prefill(self._h, layer, len(ids), ids_p, cu_p, q.data_ptr(), o.data_ptr(),
+                                            lse.data_ptr() if lse is not None else None))
+        return o, lse
+
+    def decode(self, layer: int, seq_ids, q, o=None, lse=None, want_lse: bool = True):
+        """One-token decode; q bf16 [n_seqs][Hq][D].  Returns (o, lse)."""
+        import torch
+        ids, ids_p = _i32(seq_ids)
+        _check_dev(q, "q", torch.bfloat16)
+        if tuple(q.shape) != (len(ids), self.num_q_heads, self.head_dim):
+            raise ValueError(f"q must be [{len(ids)}, {self.num_q_heads}, {self.head_dim}]")
+        if o is None:
+            o = torch.empty_like(q)
+        _check_dev(o, "o", torch.bfloat16)
+        if lse is None and want_lse:
+            lse = torch.empty((len(ids), self.num_q_heads), dtype=torch.float32, device=q.device)
+        if lse is not None:
+            _check_dev(lse, "lse", torch.float32)
+        self._check(self._lib.segkv_decode(self._h, layer, len(ids), ids_p, q.data_ptr(), o.data_ptr(),
+                                           lse.data_ptr() if lse is not None else None))
+        return o, lse
+
+    def release(self, seq_id: int):
+        return self._check(self._lib.segkv_release(self._h, seq_id))
+
+    def page_table(self, layer: int, seq_id: int, kv_head: int):
+        """(first_token, kv_len, page ids as int32 numpy array)."""
+        ft, kl, n = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        self._check(self._lib.segkv_page_table(self._h, layer, seq_id, kv_head, ctypes.byref(ft),
+                                               ctypes.byref(kl), ctypes.byref(n), None, 0))
+        ids = np.zeros(n.value, dtype=np.int32)
+        self._check(self._lib.segkv_page_table(self._h, layer, seq_id, kv_head, None, None, None,
+                                               ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n.value))
+        return ft.value, kl.value, ids
+
+    def free_pages(self) -> int:
+        v = self._lib.segkv_free_pages(self._h)
+        if v < 0:
+            raise SegKVError(int(v), self.last_error())
+        return int(v)
+
+    def set_timing(self, enable: bool):
+        return self._check(self._lib.segkv_set_timing(self._h, 1 if enable else 0))
+
+    def read_timing(self, kernel: int):
+        """(total milliseconds, launches) of one kernel since timing was enabled."""
+        ms, n = ctypes.c_double(), ctypes.c_int64()
+        self._check(self._lib.segkv_read_timing(self._h, kernel, ctypes.byref(ms), ctypes.byref(n)))
+        return ms.value, n.value
+
+    def set_tuning(self, knob: int, value: int):
+        return self._check(self._lib.segkv_set_tuning(self._h, knob, int(value)))

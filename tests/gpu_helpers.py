@@ -1,0 +1,82 @@
+"""Shared helpers of the GPU parity tests: run a workload through libsegkv
+and compare with the fp64 oracle on the same seeded inputs."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+from long_context_serving_amd import runner as R
+from long_context_serving_amd import segkv as S
+from long_context_serving_amd import workloads as wl
+from oracle import attention as A
+
+O_TOL = 2e-2    # max-abs on bf16 outputs against the unrounded fp64 oracle
+LSE_TOL = 1e-3  # max-abs on fp32 log-sum-exp
+
+
+def say(*msg):
+    print("[gpu]", *msg, file=sys.stderr, flush=True)
+
+
+def gpu_run(w, x, mode="prefill", seed=None, windows=None, split_tiles=None, pps=None, repeat=1):
+    import torch
+    say(f"{mode} {w.name} kv={w.kv_lens[:4]} q={w.q_lens[:4]} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
+        f"D={w.head_dim} P={w.page_size} W={windows or w.windows} seed={seed} split={split_tiles} pps={pps}")
+    dev = R.to_device(w, x)
+    run = R.WorkloadRun(w, dev, page_order_seed=seed, windows=windows)
+    try:
+        if split_tiles is not None:
+            run.ctx.set_tuning(S.TUNE_PREFILL_SPLIT_TILES, split_tiles)
+        if pps is not None:
+            run.ctx.set_tuning(S.TUNE_DECODE_PAGES_PER_SPLIT, pps)
+        run.load()
+        outs = []
+        for _ in range(repeat):
+            o, lse = run.prefill() if mode == "prefill" else run.decode()
+            torch.cuda.synchronize()
+            outs.append((S.bf16_bits(o), lse.cpu().numpy().astype(np.float64)))
+        return outs if repeat > 1 else outs[0]
+    finally:
+        run.close()
+
+
+def compare(w, x, o_bits, lse, rows_per_seq=None, windows=None, o_tol=O_TOL, lse_tol=LSE_TOL):
+    """Oracle rows vs GPU rows; returns (max |do|, max |dlse|)."""
+    ref = A.attend_batch(x.q, x.k, x.v, x.cu_q, x.cu_kv, windows or w.windows, w.scale, rows_per_seq)
+    worst_o = worst_l = 0.0
+    for b, (ro, rl) in enumerate(ref):
+        rows = np.arange(w.q_lens[b]) if rows_per_seq is None else np.asarray(rows_per_seq[b])
+        if len(rows) == 0:
+            continue
+        go = A.bf16_bits_to_f64(o_bits[x.cu_q[b] + rows])
+        gl = lse[x.cu_q[b] + rows]
+        assert np.all(np.isfinite(go)) and np.all(np.isfinite(gl))
+        worst_o = max(worst_o, float(np.max(np.abs(go - ro))))
+        worst_l = max(worst_l, float(np.max(np.abs(gl - rl))))
+    say(f"  max|do|={worst_o:.3e} max|dlse|={worst_l:.3e}")
+    assert worst_o <= o_tol, worst_o
+    assert worst_l <= lse_tol, worst_l
+    return worst_o, worst_l
+
+
+def sample_rows(w, b, n_random=512, seed=0):
+    """Boundary rows (first/last of the chunk, window and page edges) plus
+    seeded random rows of sequence b."""
+    q_len, kv_len = w.q_lens[b], w.kv_lens[b]
+    base = kv_len - q_len
+    rows = {0, 1, q_len - 1, q_len - 2}
+    edges = set()
+    for wdw in set(w.windows) - {0}:
+        for p in (wdw - 2, wdw - 1, wdw, wdw + 1, base + wdw - 1, base + wdw):
+            edges.add(p)
+    for k in range(1, 5):
+        edges.update({k * w.page_size - 1, k * w.page_size, 64 * k - 1, 64 * k})
+    for p in edges:
+        t = p - base
+        if 0 <= t < q_len:
+            rows.add(t)
+    rng = np.random.default_rng(seed + b)
+    rows.update(int(t) for t in rng.integers(0, q_len, size=min(n_random, q_len)))
+    return np.array(sorted(r for r in rows if 0 <= r < q_len), dtype=np.int64)

@@ -1,0 +1,105 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects
+bad configurations on the host (no GPU needed: nothing here reaches HIP)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from long_context_serving_amd import segkv as S
+from long_context_serving_amd.build import LIB_PATH, ROOT
+
+HEADER = os.path.join(ROOT, "include", "segkv.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB_PATH):
+        from long_context_serving_amd.build import build
+        build()
+    return S.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(segkv_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declarations_match_binding():
+    assert declared_functions() == sorted(S.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = os.popen(f"nm -D --defined-only {LIB_PATH}").read()
+    exported = set(re.findall(r" T (segkv_\w+)", out))
+    assert exported == set(declared_functions())
+
+
+def _cfg(**kw):
+    base = dict(num_layers=1, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=64, max_seqs=4,
+                num_pages=100, head_window=[0, 64])
+    base.update(kw)
+    return base
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(num_q_heads=6, num_kv_heads=4), "multiple"),
+    (dict(head_dim=96), "head_dim"),
+    (dict(page_size=48), "page_size"),
+    (dict(max_seqs=0), "max_seqs"),
+    (dict(num_pages=0), "num_pages"),
+    (dict(num_pages=2 ** 31), "num_pages"),
+    (dict(head_window=[0, -1]), "head_window"),
+    (dict(num_layers=0), "num_layers"),
+    (dict(softmax_scale=-1.0), "softmax_scale"),
+])
+def test_create_rejects_bad_config(lib, kw, msg):
+    with pytest.raises(S.SegKVError) as e:
+        S.SegKV(planning=True, **_cfg(**kw))
+    assert e.value.code == S.SEGKV_E_INVAL
+    assert msg in str(e.value)
+
+
+def test_create_rejects_half_set_pools(lib):
+    cfg = S._Config()
+    cfg.num_layers, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim = 1, 2, 2, 64
+    cfg.page_size, cfg.max_seqs, cfg.num_pages = 16, 1, 4
+    win = (ctypes.c_int32 * 2)(0, 0)
+    cfg.head_window = ctypes.cast(win, ctypes.POINTER(ctypes.c_int32))
+    cfg.k_pool = 0x1000  # never dereferenced: rejected before any use
+    h = ctypes.c_void_p()
+    assert lib.segkv_create(ctypes.byref(cfg), ctypes.byref(h)) == S.SEGKV_E_INVAL
+    assert h.value is None
+    assert b"both" in lib.segkv_last_error(None)
+
+
+def test_planning_context_refuses_device_calls(lib):
+    kv = S.SegKV(planning=True, **_cfg())
+    ids = (ctypes.c_int32 * 1)(0)
+    cu = (ctypes.c_int32 * 2)(0, 1)
+    assert lib.segkv_prefill(kv._h, 0, 1, ids, cu, None, None, None) == S.SEGKV_E_STATE
+    assert lib.segkv_decode(kv._h, 0, 1, ids, None, None, None) == S.SEGKV_E_STATE
+    assert lib.segkv_set_timing(kv._h, 1) == S.SEGKV_E_STATE
+    # an append carrying device pointers is refused too, before any state change
+    nq = (ctypes.c_int32 * 1)(0)
+    assert lib.segkv_append_pages(kv._h, 0, 1, ids, cu, nq, 0x1000, 0x1000) == S.SEGKV_E_STATE
+    assert kv.page_table(0, 0, 0)[1] == 0
+
+
+def test_null_context_is_rejected(lib):
+    assert lib.segkv_release(None, 0) == S.SEGKV_E_INVAL
+    assert lib.segkv_free_pages(None) == S.SEGKV_E_INVAL
+    lib.segkv_destroy(None)
+
+
+def test_tuning_knobs(lib):
+    kv = S.SegKV(planning=True, **_cfg())
+    kv.set_tuning(S.TUNE_DECODE_PAGES_PER_SPLIT, 8)
+    kv.set_tuning(S.TUNE_PREFILL_SPLIT_TILES, 0)
+    with pytest.raises(S.SegKVError):
+        kv.set_tuning(7, 1)
