@@ -38,3 +38,21 @@ def test_inputs_are_seeded_and_shaped():
     np.testing.assert_array_equal(a.cu_kv, [0, 10, 13])
     c = wl.make_inputs(w, seed=43)
     assert not np.array_equal(a.k, c.k)
+
+
+def test_product_ledger_matches_oracle_closed_forms():
+    from long_context_serving_amd import metrics as M
+    from oracle import ledger as LG
+    for w in wl.WORKLOADS.values():
+        for windows in (w.windows, (0,) * w.num_kv_heads):
+            if w.decode:
+                assert M.decode_bytes(w, windows) == LG.decode_visible_bytes(
+                    w.kv_lens, windows, w.num_q_heads, w.head_dim)
+            else:
+                assert M.prefill_flops(w, windows) == LG.prefill_visible_flops(
+                    w.kv_lens, w.q_lens, windows, w.num_q_heads, w.head_dim)
+    w = wl.MISTRAL7B_PREFILL
+    assert M.prefill_flops(w) == 181_478_096_896
+    rows = np.arange(0, 8192, 97)
+    assert M.prefill_flops_rows(w, 0, rows) == 4 * 128 * 4 * sum(
+        min(p + 1, x) if x else p + 1 for p in rows for x in w.windows)
