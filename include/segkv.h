@@ -129,8 +129,10 @@ int segkv_prefill(segkv_ctx *ctx, int32_t layer, int32_t n_seqs, const int32_t *
 
 /*
  * One-token decode of n_seqs sequences of one layer (the query is the last
- * cached token of each sequence), by split-KV over the visible pages and a
- * log-sum-exp combine.  num_q_heads / num_kv_heads must be <= 16.
+ * cached token of each sequence).  The visible pages of all (sequence, KV
+ * head) segments are split evenly over the GPU's workgroups (a segment may
+ * be split across several); partial results are merged with a log-sum-exp
+ * combine.  num_q_heads / num_kv_heads must be <= 16.
  *   q, o     device bf16 [n_seqs][num_q_heads][head_dim]
  *   lse      device fp32 [n_seqs][num_q_heads], or NULL
  */
@@ -165,13 +167,30 @@ int segkv_read_timing(segkv_ctx *ctx, int32_t kernel, double *total_ms, int64_t 
 
 /*
  * Tuning knobs (values <= 0 restore the default):
- *   SEGKV_TUNE_DECODE_PAGES_PER_SPLIT  pages one decode work item streams
- *   SEGKV_TUNE_PREFILL_SPLIT_TILES     a prefill work item covering more KV
- *                                      tiles than this is split across
+ *   SEGKV_TUNE_DECODE_MIN_PAGES        decode cuts the batch's visible pages
+ *                                      into equal shares, one per workgroup,
+ *                                      using the GPU's resident workgroup
+ *                                      slots but no share below this many
+ *                                      pages (default 8)
+ *   SEGKV_TUNE_PREFILL_SPLIT_TILES     a prefill work item covering more
+ *                                      64-key tiles than this is split across
  *                                      workgroups and merged by the combine
- *                                      kernel (0 = never split)
+ *                                      kernel.  Default: automatic, the
+ *                                      batch's total tiles over the GPU's
+ *                                      resident workgroup slots (at least
+ *                                      16); a huge value disables splitting.
+ *   SEGKV_TUNE_PREFILL_ORDER           0 (default): longest-first order;
+ *                                      1: XCD-aware order, each XCD (workgroup
+ *                                      i runs on XCD i % 8) gets a
+ *                                      cost-balanced run of the work list
+ *                                      grouped by head, longest first.
+ * Results do not depend on the knobs beyond fp32 rounding of split merges.
  */
-enum segkv_tune { SEGKV_TUNE_DECODE_PAGES_PER_SPLIT = 0, SEGKV_TUNE_PREFILL_SPLIT_TILES = 1 };
+enum segkv_tune {
+  SEGKV_TUNE_DECODE_MIN_PAGES = 0,
+  SEGKV_TUNE_PREFILL_SPLIT_TILES = 1,
+  SEGKV_TUNE_PREFILL_ORDER = 2
+};
 int segkv_set_tuning(segkv_ctx *ctx, int32_t knob, int64_t value);
 
 /* Message for the last failure on ctx (ctx = NULL: the last failed create). */

@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "segkv_internal.h"
 
 namespace segkv {
@@ -31,6 +33,17 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_inff();
+
+// Softmax probabilities are exp2 of scaled, max-shifted scores.  v_exp_f32
+// flushes results below 2^-126 to zero, which only drops terms far below
+// the fp32 resolution of the row sum.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// The running max of a row moves only when a tile's max exceeds it by more
+// than this many powers of two, so most tiles skip rescaling the output
+// accumulators.  Probabilities then stay <= 2^8 (exact in bf16's exponent
+// range, and far from fp32 overflow in the sums).
+constexpr float kRescaleLog2 = 8.0f;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
@@ -117,19 +130,76 @@ __device__ __forceinline__ int st_row_key(int r) {  // S^T row -> key within a 3
   return ((i >> 1) << 4) + (h << 3) + ((i & 1) << 2) + j;
 }
 
+// Max and sum of the 32 scores a lane holds for one column, as trees
+// (3-input max; four independent add chains).
+__device__ __forceinline__ float max32(const f32x16 &x, const f32x16 &y) {
+  float r[11];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) r[i] = fmaxf(fmaxf(x[3 * i], x[3 * i + 1]), x[3 * i + 2]);
+  r[5] = fmaxf(fmaxf(x[15], y[0]), y[1]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[6 + i] = fmaxf(fmaxf(y[2 + 3 * i], y[3 + 3 * i]), y[4 + 3 * i]);
+  r[10] = fmaxf(y[14], y[15]);
+  const float a = fmaxf(fmaxf(r[0], r[1]), r[2]);
+  const float b = fmaxf(fmaxf(r[3], r[4]), r[5]);
+  const float c = fmaxf(fmaxf(r[6], r[7]), r[8]);
+  return fmaxf(fmaxf(a, b), fmaxf(fmaxf(c, r[9]), r[10]));
+}
+
+__device__ __forceinline__ float sum32(const f32x16 &x, const f32x16 &y) {
+  float s0 = x[0] + x[1], s1 = x[2] + x[3], s2 = y[0] + y[1], s3 = y[2] + y[3];
+#pragma unroll
+  for (int i = 4; i < 16; i += 4) {
+    s0 += x[i] + x[i + 1];
+    s1 += x[i + 2] + x[i + 3];
+    s2 += y[i] + y[i + 1];
+    s3 += y[i + 2] + y[i + 3];
+  }
+  return (s0 + s1) + (s2 + s3);
+}
+
+// Direct global->LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4):
+// lane i writes bytes [16 i, 16 i + 16) after the wave-uniform LDS address
+// lds_dst.  Completion is tracked by vmcnt.
+__device__ __forceinline__ void lds_dma16(const void *src, void *lds_dst) {
+  __builtin_amdgcn_global_load_lds(const_cast<void *>(src), lds_dst, 16, 0, 0);
+}
+
+// LDS layout of one prefill stage: the K tile (64 keys x D) and then the V^T
+// tile (D channels x 64 keys), both unpadded with 16-byte chunks XOR-swizzled
+// per row, so that every 16-lane phase of a ds_read_b128 of either MFMA
+// operand touches 16 distinct bank groups, and so that the tiles can be
+// filled by direct global->LDS loads (each lane of a wave writes the next 16
+// bytes of a contiguous 1 KiB run).
+template <int D>
+struct PrefillLds {
+  static constexpr int KCPR = D / 8;                       // 16-byte chunks per K row
+  static constexpr int K_CHUNKS = kTileKeys * KCPR;
+  static constexpr int V_CHUNKS = D * (kTileKeys / 8);
+  static constexpr int STAGE_BYTES = (K_CHUNKS + V_CHUNKS) * 16;
+  // Rows sharing one 256-byte bank cycle differ in their swizzle.
+  static __device__ __forceinline__ int k_swz(int row) { return KCPR == 16 ? (row & 15) : ((row >> 1) & 7); }
+  static __device__ __forceinline__ int v_swz(int row) { return (row >> 1) & 7; }
+  static __device__ __forceinline__ int k_chunk(int key, int c) { return key * KCPR + (c ^ k_swz(key)); }
+  static __device__ __forceinline__ int v_chunk(int d, int c) { return K_CHUNKS + d * 8 + (c ^ v_swz(d)); }
+};
+
 template <int D, int P>
 __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs a) {
-  constexpr int KS = D + 8;          // LDS row stride of the K tile (elements)
-  constexpr int VS = kTileKeys + 8;  // LDS row stride of the V^T tile
-  constexpr int NKK = D / 16;        // k-steps of the QK product
-  constexpr int NDB = D / 32;        // 32-channel blocks of O^T
-  constexpr int KCH = kTileKeys * D / 8;
-  constexpr int KPT = KCH / kPrefillThreads;  // 16-byte K chunks per thread per tile
-  constexpr int VPT = KCH / kPrefillThreads;  // same count for V^T
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kTileKeys * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[D * VS];
+  using L = PrefillLds<D>;
+  constexpr int NKK = D / 16;  // k-steps of the QK product
+  constexpr int NDB = D / 32;  // 32-channel blocks of O^T
+  constexpr int NW = kPrefillThreads / 64;
+  constexpr int K_INSTR = L::K_CHUNKS / kPrefillThreads;  // direct loads per lane per tile (K)
+  constexpr int V_INSTR = L::V_CHUNKS / kPrefillThreads;  // (V^T)
+  constexpr int NSTAGE = 3;
+  static_assert(kPrefillRows == 32 * NW, "one 32-row column block per wave");
+  static_assert(K_INSTR >= 1 && V_INSTR >= 1, "tile smaller than one load per lane");
+  __shared__ __attribute__((aligned(16))) uint4 smem4[NSTAGE * L::STAGE_BYTES / 16];
+  char *smem = reinterpret_cast<char *>(smem4);
 
   const PrefillItem it = a.items[blockIdx.x];
+  if (it.qtile < 0) return;  // empty slot of the XCD-ordered work list (uniform for the workgroup)
   const SeqDesc sd = a.seqs[it.seq];
   const SegDesc sg = a.segs[it.seq * a.num_kv_heads + it.kv_head];
   const int tid = threadIdx.x;
@@ -169,97 +239,110 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
   f32x16 oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
-  float m = kNegInf;  // running max of raw scores of this column
+  float m = kNegInf;  // running (lazy) max of raw scores of this column
   float l = 0.f;      // this lane's share of the running sum
 
-  u32x4 kreg[KPT], vreg[VPT];
-  auto load_tile = [&](int tile) {
+  // Direct global->LDS tile loads.  Load j of wave w fills LDS chunks
+  // (j*NW + w)*64 + lane of the stage's K (or V^T) region; the lane fetches
+  // the global chunk that the swizzle places there.  A key outside the
+  // segment (edge tiles only) reads the nearest live page: its score is
+  // masked and every live slot holds finite data.
+  const int last_page = sg.n_pages - 1;
+  auto page_of = [&](int rel, int *slot) {
+    const int pi = rel >= 0 ? min(rel / P, last_page) : 0;
+    *slot = rel >= 0 && rel / P <= last_page ? rel % P : 0;
+    return a.page_ids[sg.page_off + pi];
+  };
+  auto issue_tile = [&](int tile, int stage) {
     const int k0 = tile * kTileKeys;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int chunk = tid + i * kPrefillThreads;
-      const int key = chunk / (D / 8), dc = chunk % (D / 8);
-      const int rel = k0 + key - sg.first_token;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (rel >= 0 && rel / P < sg.n_pages) {
-        const int page = a.page_ids[sg.page_off + rel / P];
-        x = ld16(a.k_pool + (static_cast<size_t>(page) * P + rel % P) * D + dc * 8);
-      }
-      kreg[i] = x;
+    char *st = smem + stage * L::STAGE_BYTES;
+    int uni_page = 0;
+    if constexpr (P == kTileKeys) {
+      const int pi = min(max((k0 - sg.first_token) / P, 0), last_page);
+      uni_page = a.page_ids[sg.page_off + pi];  // uniform: one page per tile
     }
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int chunk = tid + i * kPrefillThreads;
-      const int d = chunk / (kTileKeys / 8), kc = chunk % (kTileKeys / 8);
-      const int rel = k0 + kc * 8 - sg.first_token;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (rel >= 0 && rel / P < sg.n_pages) {
-        const int page = a.page_ids[sg.page_off + rel / P];
-        x = ld16(a.v_pool + static_cast<size_t>(page) * P * D + static_cast<size_t>(d) * P + rel % P);
+    for (int j = 0; j < K_INSTR; ++j) {
+      const int c = (j * NW + wave) * 64 + lane;
+      const int row = c / L::KCPR;
+      const int logical = (c % L::KCPR) ^ L::k_swz(row);
+      const uint16_t *src;
+      if constexpr (P == kTileKeys) {
+        src = a.k_pool + static_cast<size_t>(uni_page) * (P * D) + row * D + logical * 8;
+      } else {
+        int slot;
+        const int page = page_of(k0 + row - sg.first_token, &slot);
+        src = a.k_pool + (static_cast<size_t>(page) * P + slot) * D + logical * 8;
       }
-      vreg[i] = x;
+      lds_dma16(src, st + (j * NW + wave) * 1024);
+    }
+#pragma unroll
+    for (int j = 0; j < V_INSTR; ++j) {
+      const int c = (j * NW + wave) * 64 + lane;
+      const int d = c / 8;
+      const int logical = (c % 8) ^ L::v_swz(d);
+      const uint16_t *src;
+      if constexpr (P == kTileKeys) {
+        src = a.v_pool + static_cast<size_t>(uni_page) * (P * D) + d * P + logical * 8;
+      } else {
+        int slot;
+        const int page = page_of(k0 + logical * 8 - sg.first_token, &slot);
+        src = a.v_pool + static_cast<size_t>(page) * (P * D) + d * P + slot;
+      }
+      lds_dma16(src, st + L::K_CHUNKS * 16 + (j * NW + wave) * 1024);
     }
   };
 
   const int key_a0 = st_row_key(col);  // K row this lane feeds to block 0 (block 1: +32)
+  const int vrow_swz = L::v_swz(col);  // V^T rows db*32 + col share it
 
-  if (it.tile_begin < it.tile_end) load_tile(it.tile_begin);
-  for (int tile = it.tile_begin; tile < it.tile_end; ++tile) {
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int chunk = tid + i * kPrefillThreads;
-      *reinterpret_cast<u32x4 *>(sK + (chunk / (D / 8)) * KS + (chunk % (D / 8)) * 8) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int chunk = tid + i * kPrefillThreads;
-      *reinterpret_cast<u32x4 *>(sV + (chunk / (kTileKeys / 8)) * VS + (chunk % (kTileKeys / 8)) * 8) = vreg[i];
-    }
-    __syncthreads();
-    if (tile + 1 < it.tile_end) load_tile(tile + 1);
-
-    const int k0 = tile * kTileKeys;
-    const bool empty = k0 > p_wmax || (W > 0 && k0 + kTileKeys - 1 < p_wmin - W + 1);
-    if (empty) continue;
-    const bool full = k0 + kTileKeys - 1 <= p_wmin && (W == 0 || k0 >= p_wmax - W + 1);
-
+  // One 64-key tile: S^T = K Q^T, (mask), lazy online softmax, O^T += V^T P^T.
+  auto process = [&](const char *st, int k0, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      const bf16x8 ka0 = as_bf16x8(*reinterpret_cast<const u32x4 *>(sK + key_a0 * KS + kk * 16 + half * 8));
-      const bf16x8 ka1 = as_bf16x8(*reinterpret_cast<const u32x4 *>(sK + (key_a0 + 32) * KS + kk * 16 + half * 8));
+      const int c = (2 * kk + half) ^ L::k_swz(key_a0);
+      const bf16x8 ka0 = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + (key_a0 * L::KCPR + c) * 16));
+      const bf16x8 ka1 = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + ((key_a0 + 32) * L::KCPR + c) * 16));
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0, qv[kk], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qv[kk], s1, 0, 0, 0);
     }
-    if (!full) {
+    if constexpr (MASK) {
+      // key = k0 + 16 (v/8) + 8 half + v%8 (+32 for block 1); visible iff
+      // vis_lo <= key <= p, tested as one unsigned range compare.
+      const unsigned lo_rel = static_cast<unsigned>(vis_lo - k0 - 8 * half);
+      const unsigned span = static_cast<unsigned>(p - vis_lo);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int key = k0 + ((v >> 3) << 4) + (half << 3) + (v & 7);
-        if (key < vis_lo || key > p) s0[v] = kNegInf;
-        if (key + 32 < vis_lo || key + 32 > p) s1[v] = kNegInf;
+        const int off = ((v >> 3) << 4) + (v & 7);
+        if (static_cast<unsigned>(off) - lo_rel > span) s0[v] = kNegInf;
+        if (static_cast<unsigned>(off + 32) - lo_rel > span) s1[v] = kNegInf;
       }
     }
-    float mx = kNegInf;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, fmaxf(s0[v], s1[v]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = exp2f((m - m_use) * a.scale_log2);
-    const float msc = m_use * a.scale_log2;
-    float lsum = 0.f;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      s0[v] = exp2f(fmaf(s0[v], a.scale_log2, -msc));
-      s1[v] = exp2f(fmaf(s1[v], a.scale_log2, -msc));
-      lsum += s0[v] + s1[v];
+    float mx = max32(s0, s1);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
-    l = fmaf(l, alpha, lsum);
+    // Lazy running max (the lane pair of a column takes the same decision).
+    const bool bump = mx * a.scale_log2 > m * a.scale_log2 + kRescaleLog2;
+    const float m_new = bump ? mx : m;
+    const float msc = m_new == kNegInf ? 0.f : m_new * a.scale_log2;
+    // Rare after the first tiles: a scalar branch on the wave's ballot.
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(bump) != 0, 0)) {
+      const float alpha = bump ? fast_exp2(m * a.scale_log2 - msc) : 1.f;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    }
     m = m_new;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-
+    for (int v = 0; v < 16; ++v) {
+      s0[v] = fast_exp2(fmaf(s0[v], a.scale_log2, -msc));
+      s1[v] = fast_exp2(fmaf(s1[v], a.scale_log2, -msc));
+    }
+    l += sum32(s0, s1);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -267,14 +350,48 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
         const f32x16 &sv = kb ? s1 : s0;
         const bf16x8 pb = pack8_bf16(sv[8 * s + 0], sv[8 * s + 1], sv[8 * s + 2], sv[8 * s + 3], sv[8 * s + 4],
                                      sv[8 * s + 5], sv[8 * s + 6], sv[8 * s + 7]);
+        const int c = (kb * 4 + s * 2 + half) ^ vrow_swz;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const bf16x8 va = as_bf16x8(
-              *reinterpret_cast<const u32x4 *>(sV + (db * 32 + col) * VS + kb * 32 + s * 16 + half * 8));
+          const bf16x8 va =
+              as_bf16x8(*reinterpret_cast<const u32x4 *>(st + ((L::K_CHUNKS + (db * 32 + col) * 8) + c) * 16));
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[db], 0, 0, 0);
         }
       }
     }
+  };
+
+  // Three-stage ring: tile i + 2 is in flight while tile i is computed; the
+  // wait before each barrier lets only the newest tile's loads stay pending.
+  constexpr int LOADS_PER_TILE = K_INSTR + V_INSTR;
+  const int tb = it.tile_begin, te = it.tile_end;
+  if (tb < te) issue_tile(tb, 0);
+  if (tb + 1 < te) {
+    issue_tile(tb + 1, 1);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS_PER_TILE) : "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  __syncthreads();
+  for (int tile = tb; tile < te; ++tile) {
+    const int i = tile - tb;
+    const bool ahead2 = tile + 2 < te;
+    if (ahead2) issue_tile(tile + 2, (i + 2) % NSTAGE);
+    const char *st = smem + (i % NSTAGE) * L::STAGE_BYTES;
+    const int k0 = tile * kTileKeys;
+    const bool empty = k0 > p_wmax || (W > 0 && k0 + kTileKeys - 1 < p_wmin - W + 1);
+    const bool full = k0 + kTileKeys - 1 <= p_wmin && (W == 0 || k0 >= p_wmax - W + 1);
+    if (!empty) {
+      if (full)
+        process(st, k0, std::integral_constant<bool, false>{});
+      else
+        process(st, k0, std::integral_constant<bool, true>{});
+    }
+    if (ahead2)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS_PER_TILE) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
   }
 
   const float l_tot = l + __shfl_xor(l, 32);
@@ -311,14 +428,20 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
 }
 
 // ===========================================================================
-// Decode: one workgroup streams pages [page_begin, page_end) of one segment
-// for the (up to 16) query heads of its KV group.  Operands are loaded from
-// HBM straight into registers in the v_mfma_f32_16x16x32_bf16 layout (lane l
-// holds operand row l % 16 and k-elements 8*(l/16) .. +7; result lane l holds
-// column l % 16 and rows 4*(l/16) .. +3).  Each 64-key chunk is four 16-key
-// S^T blocks; block kb = 2s + hb, row 4u + j holds key 32 s + 8 u + 4 hb + j,
-// so lane group u feeds keys 32 s + 8 u .. +7 to PV step s.  The four waves
-// take chunks round-robin and are merged through LDS at the end.
+// Decode (stream-K): the visible pages of every (sequence, KV head) segment
+// of the batch form one list, cut into equal contiguous shares, one per
+// workgroup.  A share may cover the end of one segment and the start of the
+// next; each covered piece yields either the final output (a segment held by
+// one piece) or a normalised fp32 partial merged later by combine_kernel.
+//
+// Per piece, the (up to 16) query heads of the KV group are the columns of
+// v_mfma_f32_16x16x32_bf16 (lane l holds operand row l % 16 and k-elements
+// 8*(l/16) .. +7; result lane l holds column l % 16 and rows 4*(l/16) ..
+// +3).  K rows and V^T channel rows go from HBM straight into operand
+// registers.  Each 64-key chunk is four 16-key S^T blocks; block kb = 2s +
+// hb, row 4u + j holds key 32 s + 8 u + 4 hb + j, so lane group u feeds keys
+// 32 s + 8 u .. +7 to PV step s.  The four waves take chunks round-robin and
+// are merged through LDS.
 // ===========================================================================
 
 template <int D, int P>
@@ -326,156 +449,177 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
   constexpr int NKK = D / 32;  // k-steps of QK (32 channels each)
   constexpr int NDB = D / 16;  // 16-channel blocks of O^T
   constexpr int NW = kDecodeThreads / 64;
+  constexpr int TPC = D / 4;   // merge threads per column
   __shared__ float s_m[NW][kDecodeCols];
   __shared__ float s_l[NW][kDecodeCols];
   __shared__ __attribute__((aligned(16))) float s_o[NW][kDecodeCols][D];
 
-  const DecodeItem it = a.items[blockIdx.x];
-  const SeqDesc sd = a.seqs[it.seq];
-  const SegDesc sg = a.segs[it.seq * a.num_kv_heads + it.kv_head];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, u = lane >> 4;
   const int G = a.group;
+  const int piece_end = a.wg_piece_off[blockIdx.x + 1];
 
-  const int p = sd.kv_len - 1;
-  const int W = sg.window;
-  const int key_begin = sg.first_token + it.page_begin * P;
-  const int key_end = sg.first_token + it.page_end * P;  // exclusive
-  const int lo = max(key_begin, W > 0 ? p - W + 1 : 0);
-  const int hi = min(key_end - 1, p);
+  for (int pc = a.wg_piece_off[blockIdx.x]; pc < piece_end; ++pc) {
+    const DecodeItem it = a.items[pc];
+    const SeqDesc sd = a.seqs[it.seq];
+    const SegDesc sg = a.segs[it.seq * a.num_kv_heads + it.kv_head];
+    const int p = sd.kv_len - 1;
+    const int W = sg.window;
+    const int key_begin = sg.first_token + it.page_begin * P;
+    const int key_end = sg.first_token + it.page_end * P;  // exclusive
+    const int lo = max(key_begin, W > 0 ? p - W + 1 : 0);
+    const int hi = min(key_end - 1, p);
 
-  bf16x8 qv[NKK];
-  {
-    const uint16_t *qrow = a.q + (static_cast<size_t>(sd.q_start) * a.num_q_heads + it.kv_head * G + c16) * D;
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (c16 < G) x = ld16(qrow + kk * 32 + u * 8);
-      qv[kk] = as_bf16x8(x);
-    }
-  }
-
-  f32x4 oacc[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) oacc[db] = f32x4{};
-  float m = kNegInf, l = 0.f;
-
-  const int n_chunks = (key_end - key_begin + 63) / 64;
-  for (int ch = wave; ch < n_chunks; ch += NW) {
-    const int k0 = key_begin + ch * 64;
-    // K operand rows of the four S^T blocks.
-    u32x4 ka[4][NKK];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int key = k0 + 32 * (kb >> 1) + 8 * (c16 >> 2) + 4 * (kb & 1) + (c16 & 3);
-      const int rel = key - sg.first_token;
-      const bool ok = key < key_end && rel / P < sg.n_pages;
-      const int page = ok ? a.page_ids[sg.page_off + rel / P] : 0;
-      const uint16_t *krow = a.k_pool + (static_cast<size_t>(page) * P + rel % P) * D;
+    bf16x8 qv[NKK];
+    {
+      const uint16_t *qrow = a.q + (static_cast<size_t>(sd.q_start) * a.num_q_heads + it.kv_head * G + c16) * D;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         u32x4 x = {0u, 0u, 0u, 0u};
-        if (ok) x = ld16(krow + kk * 32 + u * 8);
-        ka[kb][kk] = x;
+        if (c16 < G) x = ld16(qrow + kk * 32 + u * 8);
+        qv[kk] = as_bf16x8(x);
       }
     }
-    // V^T operand: channel rows, 8 keys per lane group and PV step.
-    u32x4 va[2][NDB];
+
+    f32x4 oacc[NDB];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int key = k0 + 32 * s + 8 * u;
+    for (int db = 0; db < NDB; ++db) oacc[db] = f32x4{};
+    float m = kNegInf, l = 0.f;
+
+    // This wave's keys, 32 at a time ("halves" of its 64-key chunks, chunk
+    // wave + NW*i).  Loads of the next half are in flight while the current
+    // half is computed (two register buffers, so the loop is unrolled by 2).
+    const int n_chunks = (key_end - key_begin + 63) / 64;
+    const int my_chunks = n_chunks > wave ? (n_chunks - wave + NW - 1) / NW : 0;
+    const int n_halves = 2 * my_chunks;
+    auto half_base = [&](int j) { return key_begin + (wave + NW * (j >> 1)) * 64 + 32 * (j & 1); };
+    auto load_half = [&](int j, u32x4 (&kb_)[2][NKK], u32x4 (&vb_)[NDB]) {
+      const int kbase = half_base(j);
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const int key = kbase + 8 * (c16 >> 2) + 4 * hb + (c16 & 3);
+        const int rel = key - sg.first_token;
+        const bool ok = key < key_end;
+        const int page = ok ? a.page_ids[sg.page_off + rel / P] : 0;
+        const uint16_t *krow = a.k_pool + (static_cast<size_t>(page) * P + rel % P) * D;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          u32x4 x = {0u, 0u, 0u, 0u};
+          if (ok) x = ld16(krow + kk * 32 + u * 8);
+          kb_[hb][kk] = x;
+        }
+      }
+      const int key = kbase + 8 * u;
       const int rel = key - sg.first_token;
-      const bool ok = key < key_end && rel / P < sg.n_pages;
+      const bool ok = key < key_end;
       const int page = ok ? a.page_ids[sg.page_off + rel / P] : 0;
       const uint16_t *vbase = a.v_pool + static_cast<size_t>(page) * P * D + rel % P;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         u32x4 x = {0u, 0u, 0u, 0u};
         if (ok) x = ld16(vbase + static_cast<size_t>(db * 16 + c16) * P);
-        va[s][db] = x;
+        vb_[db] = x;
       }
-    }
-    f32x4 sc[4];
+    };
+    auto compute_half = [&](int j, const u32x4 (&kb_)[2][NKK], const u32x4 (&vb_)[NDB]) {
+      const int kbase = half_base(j);
+      f32x4 sc[2];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      f32x4 acc = f32x4{};
+      for (int hb = 0; hb < 2; ++hb) {
+        f32x4 acc = f32x4{};
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[kb][kk]), qv[kk], acc, 0, 0, 0);
-      sc[kb] = acc;
-    }
-    float mx = kNegInf;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = k0 + 32 * (kb >> 1) + 8 * u + 4 * (kb & 1) + j;
-        if (key < lo || key > hi) sc[kb][j] = kNegInf;
-        mx = fmaxf(mx, sc[kb][j]);
+        for (int kk = 0; kk < NKK; ++kk)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb_[hb][kk]), qv[kk], acc, 0, 0, 0);
+        sc[hb] = acc;
       }
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = exp2f((m - m_use) * a.scale_log2);
-    const float msc = m_use * a.scale_log2;
-    float lsum = 0.f;
+      float mx = kNegInf;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+      for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sc[kb][j] = exp2f(fmaf(sc[kb][j], a.scale_log2, -msc));
-        lsum += sc[kb][j];
+        for (int jj = 0; jj < 4; ++jj) {
+          const int key = kbase + 8 * u + 4 * hb + jj;
+          if (key < lo || key > hi) sc[hb][jj] = kNegInf;
+          mx = fmaxf(mx, sc[hb][jj]);
+        }
       }
-    }
-    l = fmaf(l, alpha, lsum);
-    m = m_new;
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool bump = mx * a.scale_log2 > m * a.scale_log2 + kRescaleLog2;
+      const float m_new = bump ? mx : m;
+      const float msc = m_new == kNegInf ? 0.f : m_new * a.scale_log2;
+      if (__any(bump)) {
+        const float alpha = bump ? fast_exp2(m * a.scale_log2 - msc) : 1.f;
+        l *= alpha;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+        for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      }
+      m = m_new;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const bf16x8 pb = pack8_bf16(sc[2 * s][0], sc[2 * s][1], sc[2 * s][2], sc[2 * s][3], sc[2 * s + 1][0],
-                                   sc[2 * s + 1][1], sc[2 * s + 1][2], sc[2 * s + 1][3]);
+      for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          sc[hb][jj] = fast_exp2(fmaf(sc[hb][jj], a.scale_log2, -msc));
+          l += sc[hb][jj];
+        }
+      }
+      const bf16x8 pb = pack8_bf16(sc[0][0], sc[0][1], sc[0][2], sc[0][3], sc[1][0], sc[1][1], sc[1][2], sc[1][3]);
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va[s][db]), pb, oacc[db], 0, 0, 0);
+        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vb_[db]), pb, oacc[db], 0, 0, 0);
+    };
+    u32x4 kb0[2][NKK], vb0[NDB], kb1[2][NKK], vb1[NDB];
+    if (n_halves > 0) load_half(0, kb0, vb0);
+    for (int j = 0; j < n_halves; j += 2) {
+      load_half(j + 1, kb1, vb1);  // n_halves is even: half j + 1 exists
+      compute_half(j, kb0, vb0);
+      if (j + 2 < n_halves) load_half(j + 2, kb0, vb0);
+      compute_half(j + 1, kb1, vb1);
     }
-  }
 
-  // Per-wave column statistics, then merge the waves through LDS.
-  float lt = l + __shfl_xor(l, 16);
-  lt += __shfl_xor(lt, 32);
-  if (u == 0) {
-    s_m[wave][c16] = m;
-    s_l[wave][c16] = lt;
-  }
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-    *reinterpret_cast<f32x4 *>(&s_o[wave][c16][db * 16 + u * 4]) = oacc[db];
-  __syncthreads();
-
-  // Thread -> (column, 4 channels); D/4 threads per column.
-  constexpr int TPC = D / 4;
-  for (int e = tid; e < G * TPC; e += kDecodeThreads) {
-    const int cc = e / TPC, d0 = (e - cc * TPC) * 4;
-    float mm = kNegInf;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) mm = fmaxf(mm, s_m[w][cc]);
-    const float m_use = mm == kNegInf ? 0.f : mm;
-    float lw = 0.f;
-    f32x4 acc = f32x4{};
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float f = exp2f((s_m[w][cc] - m_use) * a.scale_log2);
-      lw = fmaf(s_l[w][cc], f, lw);
-      acc += *reinterpret_cast<const f32x4 *>(&s_o[w][cc][d0]) * f;
+    // Per-wave column statistics, then merge the waves through LDS.
+    float lt = l + __shfl_xor(l, 16);
+    lt += __shfl_xor(lt, 32);
+    __syncthreads();  // the previous piece's merge has finished reading LDS
+    if (u == 0) {
+      s_m[wave][c16] = m;
+      s_l[wave][c16] = lt;
     }
-    const float inv = lw > 0.f ? 1.f / lw : 0.f;
-    *reinterpret_cast<f32x4 *>(a.part_o + (static_cast<size_t>(it.part) * kDecodeCols + cc) * D + d0) = acc * inv;
-    if (d0 == 0)
-      a.part_lse[static_cast<size_t>(it.part) * kDecodeCols + cc] = lw > 0.f ? mm * a.scale + logf(lw) : kNegInf;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      *reinterpret_cast<f32x4 *>(&s_o[wave][c16][db * 16 + u * 4]) = oacc[db];
+    __syncthreads();
+
+    // Thread -> (column, 4 channels).  A segment held by one piece writes
+    // the output; otherwise the piece writes its normalised partial.
+    const bool single = it.n_parts == 1;
+    const size_t out_row0 = static_cast<size_t>(sd.q_start) * a.num_q_heads + it.kv_head * G;
+    for (int e = tid; e < G * TPC; e += kDecodeThreads) {
+      const int cc = e / TPC, d0 = (e - cc * TPC) * 4;
+      float mm = kNegInf;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) mm = fmaxf(mm, s_m[w][cc]);
+      const float m_use = mm == kNegInf ? 0.f : mm;
+      float lw = 0.f;
+      f32x4 acc = f32x4{};
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float f = fast_exp2((s_m[w][cc] - m_use) * a.scale_log2);
+        lw = fmaf(s_l[w][cc], f, lw);
+        acc += *reinterpret_cast<const f32x4 *>(&s_o[w][cc][d0]) * f;
+      }
+      const float inv = lw > 0.f ? 1.f / lw : 0.f;
+      const float lse_v = lw > 0.f ? mm * a.scale + logf(lw) : kNegInf;
+      if (single) {
+        *reinterpret_cast<u32x2 *>(a.o + (out_row0 + cc) * D + d0) =
+            pack4_bf16(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+        if (d0 == 0 && a.lse) a.lse[out_row0 + cc] = lse_v;
+      } else {
+        *reinterpret_cast<f32x4 *>(a.part_o + (static_cast<size_t>(it.part) * kDecodeCols + cc) * D + d0) =
+            acc * inv;
+        if (d0 == 0) a.part_lse[static_cast<size_t>(it.part) * kDecodeCols + cc] = lse_v;
+      }
+    }
   }
 }
 
@@ -488,21 +632,38 @@ template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   constexpr int TPE = D / 4;        // threads per entry
   constexpr int EPP = 256 / TPE;    // entries per pass
+  constexpr int B = 4;              // parts loaded per batch
   const CombineItem it = a.items[blockIdx.x];
   const int entries = it.rows * it.heads;
   const int d0 = (threadIdx.x % TPE) * 4;
-  for (int e = threadIdx.x / TPE; e < entries; e += EPP) {
-    float mm = kNegInf;
-    for (int s = 0; s < it.n_parts; ++s)
-      mm = fmaxf(mm, a.part_lse[static_cast<size_t>(it.part_begin + s) * a.slot_rows + e]);
-    const float m_use = mm == kNegInf ? 0.f : mm;
-    float wsum = 0.f;
+  // grid.y: groups of EPP entries, so that a long item spreads over workgroups
+  for (int e = blockIdx.y * EPP + threadIdx.x / TPE; e < entries; e += EPP * gridDim.y) {
+    float mm = kNegInf, wsum = 0.f;
     f32x4 acc = f32x4{};
-    for (int s = 0; s < it.n_parts; ++s) {
-      const size_t slot = static_cast<size_t>(it.part_begin + s) * a.slot_rows + e;
-      const float w = __expf(a.part_lse[slot] - m_use);
-      wsum += w;
-      acc += *reinterpret_cast<const f32x4 *>(a.part_o + slot * D + d0) * w;
+    for (int s0 = 0; s0 < it.n_parts; s0 += B) {
+      float ls[B];
+      f32x4 os[B];
+#pragma unroll
+      for (int k = 0; k < B; ++k) {
+        const int s = min(s0 + k, it.n_parts - 1);
+        const size_t slot = static_cast<size_t>(it.part_begin + s) * a.slot_rows + e;
+        ls[k] = s0 + k < it.n_parts ? a.part_lse[slot] : kNegInf;
+        os[k] = *reinterpret_cast<const f32x4 *>(a.part_o + slot * D + d0);
+      }
+      float bm = mm;
+#pragma unroll
+      for (int k = 0; k < B; ++k) bm = fmaxf(bm, ls[k]);
+      if (bm == kNegInf) continue;
+      const float r = __expf(mm - bm);  // mm = -inf gives 0
+      wsum *= r;
+      acc *= r;
+#pragma unroll
+      for (int k = 0; k < B; ++k) {
+        const float w = __expf(ls[k] - bm);
+        wsum += w;
+        acc += os[k] * w;
+      }
+      mm = bm;
     }
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
     const int row = it.out_row + e / it.heads;
@@ -538,16 +699,18 @@ hipError_t launch_prefill(const PrefillArgs &a, int n_items, int head_dim, int p
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeArgs &a, int n_items, int head_dim, int page_size, hipStream_t s) {
-  if (n_items <= 0) return hipSuccess;
-  SEGKV_DISPATCH_DP(decode_kernel, head_dim, page_size, dim3(n_items), dim3(kDecodeThreads), s, a);
+hipError_t launch_decode(const DecodeArgs &a, int n_wgs, int head_dim, int page_size, hipStream_t s) {
+  if (n_wgs <= 0) return hipSuccess;
+  SEGKV_DISPATCH_DP(decode_kernel, head_dim, page_size, dim3(n_wgs), dim3(kDecodeThreads), s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const CombineArgs &a, int n_items, int head_dim, hipStream_t s) {
+hipError_t launch_combine(const CombineArgs &a, int n_items, int max_entries, int head_dim, hipStream_t s) {
   if (n_items <= 0) return hipSuccess;
-  if (head_dim == 64) hipLaunchKernelGGL(combine_kernel<64>, dim3(n_items), dim3(256), 0, s, a);
-  else if (head_dim == 128) hipLaunchKernelGGL(combine_kernel<128>, dim3(n_items), dim3(256), 0, s, a);
+  const int epp = 256 / (head_dim / 4);
+  const dim3 grid(n_items, (max_entries + epp - 1) / epp);
+  if (head_dim == 64) hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(256), 0, s, a);
+  else if (head_dim == 128) hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(256), 0, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

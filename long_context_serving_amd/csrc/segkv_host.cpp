@@ -31,8 +31,9 @@ namespace {
 thread_local std::string g_create_error;
 
 constexpr int kStages = 4;
-constexpr int kDefaultDecodePagesPerSplit = 16;
-constexpr int kDefaultPrefillSplitTiles = 0;
+constexpr int kDefaultDecodeMinPages = 8;
+constexpr int kDefaultPrefillSplitTiles = 0;  // automatic
+constexpr int64_t kMinSplitTiles = 16;
 
 struct Segment {
   int32_t first_token = 0;
@@ -95,10 +96,12 @@ struct segkv_ctx {
   int stage_next = 0;
   float *d_part = nullptr;
   size_t d_part_cap = 0;  // bytes
+  int32_t num_cus = 0;
 
   // tuning
-  int32_t decode_pps = kDefaultDecodePagesPerSplit;
-  int64_t prefill_split_tiles = kDefaultPrefillSplitTiles;
+  int32_t decode_pps = kDefaultDecodeMinPages;  // minimum pages per decode workgroup
+  int64_t prefill_split_tiles = kDefaultPrefillSplitTiles;  // 0 = automatic
+  int32_t prefill_order = 0;  // 0 = longest-first, 1 = XCD-aware
 
   // timing
   bool timing = false;
@@ -365,6 +368,14 @@ int segkv_create(const segkv_config *cfg, segkv_ctx **out) {
     }
   }
   if (!c->planning) {
+    int dev = 0;
+    hipError_t e0 = hipGetDevice(&dev);
+    if (e0 == hipSuccess) e0 = hipDeviceGetAttribute(&c->num_cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e0 != hipSuccess) {
+      g_create_error = std::string("hipDeviceGetAttribute: ") + hipGetErrorString(e0);
+      segkv_destroy(c);
+      return SEGKV_E_DEVICE;
+    }
     for (int i = 0; i < kStages; ++i) {
       hipError_t e = hipEventCreateWithFlags(&c->stage_ev[i], hipEventDisableTiming);
       if (e != hipSuccess) {
@@ -604,50 +615,95 @@ int segkv_prefill(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *se
   std::vector<CombineItem> &citems = c->scratch_citems;
   items.clear();
   citems.clear();
-  int32_t n_parts = 0;
-  int64_t max_cost = 0;
+  int64_t total_cost = 0;
   for (int32_t b = 0; b < n_seqs; ++b) {
     const int32_t ql = cu_q[b + 1] - cu_q[b];
     const SeqLayer &s = c->sl(layer, seq_ids[b]);
     for (int32_t g = 0; g < c->Hkv; ++g) {
       const int32_t w = c->win(layer, g);
-      for (int32_t qt = 0; qt * rows < ql; ++qt) {
+      // Last q tile first: for a global head the longest rows come first.
+      for (int32_t qt = (ql + rows - 1) / rows - 1; qt >= 0; --qt) {
         const int32_t p_min = s.kv_len - ql + qt * rows;
         const int32_t p_max = s.kv_len - ql + std::min((qt + 1) * rows, ql) - 1;
         const int32_t lo = w > 0 ? std::max(0, p_min - w + 1) : 0;
         const int32_t tb = lo / kTileKeys;
         const int32_t te = p_max / kTileKeys + 1;
-        const int64_t cost = te - tb;
-        if (c->prefill_split_tiles > 0 && cost > c->prefill_split_tiles) {
-          const int32_t ns = static_cast<int32_t>(ceil_div(cost, c->prefill_split_tiles));
-          const int32_t per = static_cast<int32_t>(ceil_div(cost, ns));
-          const int32_t part0 = n_parts;
-          int32_t k = 0;
-          for (int32_t t0 = tb; t0 < te; t0 += per, ++k)
-            items.push_back(PrefillItem{b, g, qt, t0, std::min(te, t0 + per), n_parts++, 0, 0});
-          citems.push_back(CombineItem{part0, k, cu_q[b] + qt * rows, std::min(rows, ql - qt * rows), g * G, G, 0, 0});
-          max_cost = std::max<int64_t>(max_cost, per);
-        } else {
-          items.push_back(PrefillItem{b, g, qt, tb, te, -1, 0, 0});
-          max_cost = std::max(max_cost, cost);
-        }
+        items.push_back(PrefillItem{b, g, qt, tb, te, -1, 0, 0});
+        total_cost += te - tb;
       }
     }
   }
-  // Longest first (counting sort on tile count, stable).
+  // Split rows that would outlast the average share of one workgroup slot;
+  // their parts are merged by the combine kernel.
+  int64_t split = c->prefill_split_tiles;
+  if (split <= 0) {
+    const int64_t slots = std::max<int64_t>(1, static_cast<int64_t>(c->num_cus) * kPrefillWgPerCu);
+    split = std::max<int64_t>(kMinSplitTiles, ceil_div(total_cost, slots));
+  }
+  int32_t n_parts = 0;
+  int64_t max_cost = 0;
   {
+    std::vector<PrefillItem> expanded;
+    expanded.reserve(items.size() + items.size() / 4);
+    for (const PrefillItem &x : items) {
+      const int64_t cost = x.tile_end - x.tile_begin;
+      if (cost > split) {
+        const int32_t ns = static_cast<int32_t>(ceil_div(cost, split));
+        const int32_t per = static_cast<int32_t>(ceil_div(cost, ns));
+        const int32_t part0 = n_parts;
+        int32_t k = 0;
+        for (int32_t t0 = x.tile_begin; t0 < x.tile_end; t0 += per, ++k)
+          expanded.push_back(PrefillItem{x.seq, x.kv_head, x.qtile, t0, std::min(x.tile_end, t0 + per), n_parts++, 0, 0});
+        const int32_t ql = cu_q[x.seq + 1] - cu_q[x.seq];
+        citems.push_back(CombineItem{part0, k, cu_q[x.seq] + x.qtile * rows, std::min(rows, ql - x.qtile * rows),
+                                     x.kv_head * G, G, 0, 0});
+        max_cost = std::max<int64_t>(max_cost, per);
+      } else {
+        expanded.push_back(x);
+        max_cost = std::max(max_cost, cost);
+      }
+    }
+    items.swap(expanded);
+  }
+  // Order: longest first.  XCD-aware order additionally gives each XCD (its
+  // own L2) a contiguous, cost-balanced run of the list, so the workgroups
+  // sharing an L2 read the same few heads' K/V; queue x holds the items at
+  // positions x, x + 8, x + 16, ... (empty slots padded with qtile = -1).
+  auto lpt_sort = [&](std::vector<PrefillItem> &v) {
     std::vector<int32_t> &cnt = c->scratch_i32;
     cnt.assign(static_cast<size_t>(max_cost) + 2, 0);
-    for (const PrefillItem &x : items) cnt[static_cast<size_t>(max_cost - (x.tile_end - x.tile_begin))]++;
+    for (const PrefillItem &x : v) cnt[static_cast<size_t>(max_cost - (x.tile_end - x.tile_begin))]++;
     int32_t acc = 0;
-    for (int32_t &v : cnt) {
-      int32_t t = v;
-      v = acc;
+    for (int32_t &cv : cnt) {
+      int32_t t = cv;
+      cv = acc;
       acc += t;
     }
-    std::vector<PrefillItem> sorted(items.size());
-    for (const PrefillItem &x : items) sorted[static_cast<size_t>(cnt[static_cast<size_t>(max_cost - (x.tile_end - x.tile_begin))]++)] = x;
-    items.swap(sorted);
+    std::vector<PrefillItem> sorted(v.size());
+    for (const PrefillItem &x : v) sorted[static_cast<size_t>(cnt[static_cast<size_t>(max_cost - (x.tile_end - x.tile_begin))]++)] = x;
+    v.swap(sorted);
+  };
+  if (c->prefill_order == 1 && items.size() > static_cast<size_t>(kXcds)) {
+    int64_t tot = 0;
+    for (const PrefillItem &x : items) tot += x.tile_end - x.tile_begin;
+    std::vector<PrefillItem> q[kXcds];
+    int64_t prefix = 0;
+    for (const PrefillItem &x : items) {
+      const int64_t cost = x.tile_end - x.tile_begin;
+      const int64_t xcd = std::min<int64_t>(kXcds - 1, (2 * prefix + cost) * kXcds / (2 * std::max<int64_t>(tot, 1)));
+      q[xcd].push_back(x);
+      prefix += cost;
+    }
+    size_t n_q = 0;
+    for (auto &v : q) {
+      lpt_sort(v);
+      n_q = std::max(n_q, v.size());
+    }
+    items.assign(n_q * kXcds, PrefillItem{0, 0, -1, 0, 0, -1, 0, 0});
+    for (int x = 0; x < kXcds; ++x)
+      for (size_t j = 0; j < q[x].size(); ++j) items[j * kXcds + x] = q[x][j];
+  } else {
+    lpt_sort(items);
   }
 
   int64_t total_pages = 0;
@@ -716,7 +772,7 @@ int segkv_prefill(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *se
     TimedLaunch t2{};
     rc = timed_begin(c, &t2, SEGKV_KERNEL_COMBINE);
     if (rc) return rc;
-    e = launch_combine(ca, static_cast<int>(citems.size()), c->D, c->stream);
+    e = launch_combine(ca, static_cast<int>(citems.size()), kPrefillRows, c->D, c->stream);
     if (e != hipSuccess) return c->device_fail(e, "combine launch");
     rc = timed_end(c, &t2);
     if (rc) return rc;
@@ -739,13 +795,14 @@ int segkv_decode(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq
     if (s.pending_from > s.kv_len - 1)
       return c->fail(SEGKV_E_INVAL, "seq %d: the last token was not appended as a query (n_query >= 1)", seq_ids[b]);
   }
+  int32_t n_parts_total = 0;
+  // Stream-K plan: the visible pages of all segments, in (sequence, KV head)
+  // order, are cut into equal contiguous shares, one per workgroup (at most
+  // the GPU's resident decode workgroups, at least min_pages pages each).
   const int32_t P = c->P;
-  const int32_t pps = c->decode_pps;
-  std::vector<DecodeItem> ditems;
-  std::vector<CombineItem> &citems = c->scratch_citems;
-  citems.clear();
-  ditems.reserve(static_cast<size_t>(n_seqs) * c->Hkv * 4);
-  int32_t n_parts = 0;
+  std::vector<int32_t> &seg_lo = c->scratch_i32;  // [n_seqs*Hkv][2]: first visible page, count
+  seg_lo.assign(static_cast<size_t>(n_seqs) * c->Hkv * 2, 0);
+  int64_t total = 0;
   for (int32_t b = 0; b < n_seqs; ++b) {
     const SeqLayer &s = c->sl(layer, seq_ids[b]);
     const int32_t p = s.kv_len - 1;
@@ -755,22 +812,75 @@ int segkv_decode(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq
       const int32_t lo = w > 0 ? std::max(0, p - w + 1) : 0;
       const int32_t pg_lo = (lo - sg.first_token) / P;
       const int32_t pg_hi = (p - sg.first_token) / P + 1;
-      const int32_t part0 = n_parts;
-      for (int32_t p0 = pg_lo; p0 < pg_hi; p0 += pps)
-        ditems.push_back(DecodeItem{b, g, p0, std::min(pg_hi, p0 + pps), n_parts++, 0, 0, 0});
-      citems.push_back(CombineItem{part0, n_parts - part0, b, 1, g * c->G, c->G, 0, 0});
+      seg_lo[(static_cast<size_t>(b) * c->Hkv + g) * 2] = pg_lo;
+      seg_lo[(static_cast<size_t>(b) * c->Hkv + g) * 2 + 1] = pg_hi - pg_lo;
+      total += pg_hi - pg_lo;
     }
   }
-  // Longer items (full splits) first.
-  std::stable_sort(ditems.begin(), ditems.end(), [](const DecodeItem &x, const DecodeItem &y) {
-    return (x.page_end - x.page_begin) > (y.page_end - y.page_begin);
-  });
+  const int64_t slots = std::max<int64_t>(1, static_cast<int64_t>(c->num_cus) * kDecodeWgPerCu);
+  const int64_t n_wg = std::max<int64_t>(1, std::min(slots, ceil_div(total, c->decode_pps)));
+  std::vector<DecodeItem> ditems;
+  std::vector<int32_t> wg_off;
+  ditems.reserve(static_cast<size_t>(n_wg + n_seqs * c->Hkv));
+  wg_off.reserve(static_cast<size_t>(n_wg + 1));
+  std::vector<CombineItem> &citems = c->scratch_citems;
+  citems.clear();
+  {
+    // first pass: pieces per segment (for part numbering)
+    const int64_t nseg = static_cast<int64_t>(n_seqs) * c->Hkv;
+    std::vector<int32_t> seg_parts(static_cast<size_t>(nseg), 0), seg_part0(static_cast<size_t>(nseg), 0);
+    auto share = [&](int64_t w) { return total * w / n_wg; };
+    for (int pass = 0; pass < 2; ++pass) {
+      int64_t si = 0, seg_start = 0;  // current segment and its first global page index
+      std::vector<int32_t> used(pass ? static_cast<size_t>(nseg) : 0, 0);
+      for (int64_t w = 0; w < n_wg; ++w) {
+        if (pass) wg_off.push_back(static_cast<int32_t>(ditems.size()));
+        int64_t pos = share(w);
+        const int64_t end = share(w + 1);
+        while (pos < end) {
+          while (seg_start + seg_lo[static_cast<size_t>(si) * 2 + 1] <= pos) {
+            seg_start += seg_lo[static_cast<size_t>(si) * 2 + 1];
+            ++si;
+          }
+          const int64_t seg_end = seg_start + seg_lo[static_cast<size_t>(si) * 2 + 1];
+          const int64_t stop = std::min(end, seg_end);
+          if (!pass) {
+            seg_parts[static_cast<size_t>(si)]++;
+          } else {
+            const int32_t b = static_cast<int32_t>(si / c->Hkv), g = static_cast<int32_t>(si % c->Hkv);
+            const int32_t pg0 = seg_lo[static_cast<size_t>(si) * 2] + static_cast<int32_t>(pos - seg_start);
+            const int32_t pg1 = seg_lo[static_cast<size_t>(si) * 2] + static_cast<int32_t>(stop - seg_start);
+            const int32_t part = seg_part0[static_cast<size_t>(si)] + used[static_cast<size_t>(si)]++;
+            ditems.push_back(DecodeItem{b, g, pg0, pg1, part, seg_part0[static_cast<size_t>(si)],
+                                        seg_parts[static_cast<size_t>(si)], 0});
+          }
+          pos = stop;
+        }
+      }
+      if (!pass) {
+        int32_t acc = 0;
+        for (int64_t i = 0; i < nseg; ++i) {
+          seg_part0[static_cast<size_t>(i)] = acc;
+          acc += seg_parts[static_cast<size_t>(i)];
+          if (seg_parts[static_cast<size_t>(i)] > 1) {
+            const int32_t b = static_cast<int32_t>(i / c->Hkv), g = static_cast<int32_t>(i % c->Hkv);
+            citems.push_back(CombineItem{seg_part0[static_cast<size_t>(i)], seg_parts[static_cast<size_t>(i)], b, 1,
+                                         g * c->G, c->G, 0, 0});
+          }
+        }
+        n_parts_total = acc;
+      }
+    }
+    wg_off.push_back(static_cast<int32_t>(ditems.size()));
+  }
+  const int32_t n_parts = n_parts_total;
 
   int64_t total_pages = 0;
   const size_t tbytes = seq_tables_bytes(c, layer, n_seqs, seq_ids, &total_pages);
   const size_t ibytes = align_up(sizeof(DecodeItem) * ditems.size(), 16);
+  const size_t obytes = align_up(sizeof(int32_t) * wg_off.size(), 16);
   const size_t cbytes = sizeof(CombineItem) * citems.size();
-  const size_t bytes = tbytes + ibytes + cbytes;
+  const size_t bytes = tbytes + ibytes + obytes + cbytes;
   char *stage = nullptr;
   int slot = 0;
   rc = acquire_stage(c, bytes, &stage, &slot);
@@ -783,7 +893,8 @@ int segkv_decode(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq
   if (rc) return rc;
   write_seq_tables(c, layer, n_seqs, seq_ids, nullptr, nullptr, total_pages, stage);
   std::memcpy(stage + tbytes, ditems.data(), sizeof(DecodeItem) * ditems.size());
-  std::memcpy(stage + tbytes + ibytes, citems.data(), cbytes);
+  std::memcpy(stage + tbytes + ibytes, wg_off.data(), sizeof(int32_t) * wg_off.size());
+  if (cbytes) std::memcpy(stage + tbytes + ibytes + obytes, citems.data(), cbytes);
   rc = upload(c, slot, bytes);
   if (rc) return rc;
 
@@ -796,8 +907,11 @@ int segkv_decode(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq
   a.page_ids = reinterpret_cast<const int32_t *>(reinterpret_cast<const char *>(a.segs) +
                                                  align_up(sizeof(SegDesc) * static_cast<size_t>(n_seqs) * c->Hkv, 16));
   a.items = reinterpret_cast<const DecodeItem *>(c->d_meta + tbytes);
+  a.wg_piece_off = reinterpret_cast<const int32_t *>(c->d_meta + tbytes + ibytes);
   a.part_o = c->d_part;
   a.part_lse = c->d_part + static_cast<size_t>(n_parts) * kDecodeCols * c->D;
+  a.o = static_cast<uint16_t *>(o);
+  a.lse = lse;
   a.num_q_heads = c->Hq;
   a.num_kv_heads = c->Hkv;
   a.group = c->G;
@@ -806,15 +920,14 @@ int segkv_decode(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq
   TimedLaunch t{};
   rc = timed_begin(c, &t, SEGKV_KERNEL_DECODE_SPLIT);
   if (rc) return rc;
-  hipError_t e = launch_decode(a, static_cast<int>(ditems.size()), c->D, c->P, c->stream);
+  hipError_t e = launch_decode(a, static_cast<int>(n_wg), c->D, c->P, c->stream);
   if (e != hipSuccess) return c->device_fail(e, "decode launch");
   rc = timed_end(c, &t);
-  if (rc) return rc;
-
+  if (rc || citems.empty()) return rc;
   CombineArgs ca;
   ca.part_o = a.part_o;
   ca.part_lse = a.part_lse;
-  ca.items = reinterpret_cast<const CombineItem *>(c->d_meta + tbytes + ibytes);
+  ca.items = reinterpret_cast<const CombineItem *>(c->d_meta + tbytes + ibytes + obytes);
   ca.o = static_cast<uint16_t *>(o);
   ca.lse = lse;
   ca.num_q_heads = c->Hq;
@@ -822,7 +935,7 @@ int segkv_decode(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq
   TimedLaunch t2{};
   rc = timed_begin(c, &t2, SEGKV_KERNEL_COMBINE);
   if (rc) return rc;
-  e = launch_combine(ca, static_cast<int>(citems.size()), c->D, c->stream);
+  e = launch_combine(ca, static_cast<int>(citems.size()), c->G, c->D, c->stream);
   if (e != hipSuccess) return c->device_fail(e, "combine launch");
   return timed_end(c, &t2);
 }
@@ -853,12 +966,16 @@ int segkv_read_timing(segkv_ctx *c, int32_t kernel, double *total_ms, int64_t *l
 int segkv_set_tuning(segkv_ctx *c, int32_t knob, int64_t value) {
   if (!c) return SEGKV_E_INVAL;
   switch (knob) {
-    case SEGKV_TUNE_DECODE_PAGES_PER_SPLIT:
+    case SEGKV_TUNE_DECODE_MIN_PAGES:
       if (value > (1 << 20)) return c->fail(SEGKV_E_INVAL, "pages per split too large");
-      c->decode_pps = value > 0 ? static_cast<int32_t>(value) : kDefaultDecodePagesPerSplit;
+      c->decode_pps = value > 0 ? static_cast<int32_t>(value) : kDefaultDecodeMinPages;
       return SEGKV_OK;
     case SEGKV_TUNE_PREFILL_SPLIT_TILES:
       c->prefill_split_tiles = value > 0 ? value : kDefaultPrefillSplitTiles;
+      return SEGKV_OK;
+    case SEGKV_TUNE_PREFILL_ORDER:
+      if (value > 1) return c->fail(SEGKV_E_INVAL, "prefill order must be 0 (longest first) or 1 (XCD-aware)");
+      c->prefill_order = value > 0 ? static_cast<int32_t>(value) : 0;
       return SEGKV_OK;
     default:
       return c->fail(SEGKV_E_INVAL, "unknown tuning knob %d", knob);

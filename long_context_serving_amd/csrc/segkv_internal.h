@@ -15,11 +15,14 @@
 namespace segkv {
 
 constexpr int kTileKeys = 64;      // keys per prefill KV tile (one LDS stage)
-constexpr int kPrefillRows = 128;  // (query position, query head) rows per prefill workgroup
-constexpr int kPrefillThreads = 256;
+constexpr int kPrefillRows = 256;  // (query position, query head) rows per prefill workgroup
+constexpr int kPrefillThreads = 512;  // 8 waves, 32 rows each, two per SIMD
 constexpr int kDecodeThreads = 256;
 constexpr int kDecodeCols = 16;    // query heads handled by one decode work item (GQA group, padded)
 constexpr int kScatterThreads = 256;
+constexpr int kPrefillWgPerCu = 1;  // resident prefill workgroups per CU (96 KiB of LDS each)
+constexpr int kDecodeWgPerCu = 2;   // resident decode workgroups per CU
+constexpr int kXcds = 8;           // MI355X: workgroup i of a launch runs on XCD i % 8
 
 struct SeqDesc {
   int32_t kv_len;   // tokens in the sequence (this layer)
@@ -51,6 +54,7 @@ struct ScatterItem {
 // One prefill workgroup: rows [qtile*rows_per_tile ...) of (sequence, KV head
 // group) over KV tiles [tile_begin, tile_end).  part >= 0 writes fp32
 // partial results to partial slot `part` instead of the final output.
+// qtile < 0 marks an empty slot of the XCD-ordered list (the workgroup exits).
 struct PrefillItem {
   int32_t seq;
   int32_t kv_head;
@@ -61,15 +65,19 @@ struct PrefillItem {
   int32_t pad0, pad1;
 };
 
-// One decode workgroup: pages [page_begin, page_end) of segment (seq, kv_head),
-// partial results to slot `part`.
+// One decode piece: pages [page_begin, page_end) of segment (seq, kv_head).
+// The segment is covered by n_parts pieces (partial slots [part_begin,
+// part_begin + n_parts)); with n_parts == 1 the piece writes the output,
+// otherwise its partial goes to slot `part`.
 struct DecodeItem {
   int32_t seq;
   int32_t kv_head;
   int32_t page_begin;
   int32_t page_end;
   int32_t part;
-  int32_t pad0, pad1, pad2;
+  int32_t part_begin;
+  int32_t n_parts;
+  int32_t pad0;
 };
 
 // One combine workgroup: merge partial slots [part_begin, part_begin+n_parts)
@@ -121,9 +129,12 @@ struct DecodeArgs {
   const SeqDesc *seqs;
   const SegDesc *segs;
   const int32_t *page_ids;
-  const DecodeItem *items;
+  const DecodeItem *items;     // pieces, grouped by workgroup
+  const int32_t *wg_piece_off; // [n_wgs + 1]: workgroup w runs pieces [off[w], off[w+1])
   float *part_o;    // [parts][kDecodeCols][head_dim]
   float *part_lse;  // [parts][kDecodeCols]
+  uint16_t *o;        // [n_seqs][num_q_heads][head_dim]
+  float *lse;         // [n_seqs][num_q_heads] or null
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t group;
@@ -147,7 +158,7 @@ struct CombineArgs {
 // Launchers (kernels.hip).  Return the launch status.
 hipError_t launch_scatter(const ScatterArgs &a, int n_items, int head_dim, int page_size, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs &a, int n_items, int head_dim, int page_size, hipStream_t s);
-hipError_t launch_decode(const DecodeArgs &a, int n_items, int head_dim, int page_size, hipStream_t s);
-hipError_t launch_combine(const CombineArgs &a, int n_items, int head_dim, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs &a, int n_wgs, int head_dim, int page_size, hipStream_t s);
+hipError_t launch_combine(const CombineArgs &a, int n_items, int max_entries, int head_dim, hipStream_t s);
 
 }  // namespace segkv

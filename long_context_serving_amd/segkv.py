@@ -28,8 +28,9 @@ KERNEL_PREFILL = 1
 KERNEL_DECODE_SPLIT = 2
 KERNEL_COMBINE = 3
 
-TUNE_DECODE_PAGES_PER_SPLIT = 0
+TUNE_DECODE_MIN_PAGES = 0
 TUNE_PREFILL_SPLIT_TILES = 1
+TUNE_PREFILL_ORDER = 2
 
 # Every entry point include/segkv.h declares.
 EXPORTED = (
@@ -67,11 +68,12 @@ _lib = None
 
 
 def load_library(path: Optional[str] = None):
-    """Load libsegkv.so (built in-tree by long_context_serving_amd.build)."""
+    """Load libsegkv.so (built in-tree by long_context_serving_amd.build; the
+    environment variable SEGKV_LIBRARY may name another build of it)."""
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or LIB_PATH
+    p = path or os.environ.get("SEGKV_LIBRARY") or LIB_PATH
     if not os.path.exists(p):
         raise ImportError(f"{p} is missing: build it with `python -m long_context_serving_amd.build` "
                           "(there is no fallback path)")

@@ -30,7 +30,7 @@ def gpu_run(w, x, mode="prefill", seed=None, windows=None, split_tiles=None, pps
         if split_tiles is not None:
             run.ctx.set_tuning(S.TUNE_PREFILL_SPLIT_TILES, split_tiles)
         if pps is not None:
-            run.ctx.set_tuning(S.TUNE_DECODE_PAGES_PER_SPLIT, pps)
+            run.ctx.set_tuning(S.TUNE_DECODE_MIN_PAGES, pps)
         run.load()
         outs = []
         for _ in range(repeat):

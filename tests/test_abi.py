@@ -99,7 +99,7 @@ def test_null_context_is_rejected(lib):
 
 def test_tuning_knobs(lib):
     kv = S.SegKV(planning=True, **_cfg())
-    kv.set_tuning(S.TUNE_DECODE_PAGES_PER_SPLIT, 8)
+    kv.set_tuning(S.TUNE_DECODE_MIN_PAGES, 8)
     kv.set_tuning(S.TUNE_PREFILL_SPLIT_TILES, 0)
     with pytest.raises(S.SegKVError):
         kv.set_tuning(7, 1)

@@ -166,3 +166,34 @@ def test_device_context_errors():
         run.ctx.prefill(0, [3], [1], dev.q[:1])
     assert e.value.code == S.SEGKV_E_RANGE
     run.close()
+
+
+def test_prefill_work_order_does_not_change_results():
+    w = small("order", (2000, 900, 64), (2000, 900, 64), 16, 4, 128, 64, (0, 300, 64, 1000), seed=41)
+    x = wl.make_inputs(w)
+    from long_context_serving_amd import runner as R
+    import torch
+    outs = []
+    for order, split in ((0, 0), (1, 0), (0, 1 << 30), (1, 1 << 30)):
+        run = R.WorkloadRun(w, R.to_device(w, x))
+        run.ctx.set_tuning(S.TUNE_PREFILL_ORDER, order)
+        run.ctx.set_tuning(S.TUNE_PREFILL_SPLIT_TILES, split)
+        run.load()
+        o, lse = run.prefill()
+        torch.cuda.synchronize()
+        outs.append((S.bf16_bits(o), lse.cpu().numpy().astype(np.float64)))
+        run.close()
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+    assert np.array_equal(outs[2][0], outs[3][0]) and np.array_equal(outs[2][1], outs[3][1])
+    for o, l in outs:
+        compare(w, x, o, l)
+
+
+def test_decode_repeated_calls_agree():
+    # many parts per segment: exercises the arrival counters across calls
+    w = decode_workload("dec_rep", 4, (5000, 300, 2500, 64), 32, 4, 128, 64, (0, 1000, 64, 0), seed=8)
+    x = wl.make_inputs(w)
+    (o1, l1), (o2, l2), (o3, l3) = gpu_run(w, x, mode="decode", pps=2, repeat=3)
+    assert np.array_equal(o1, o2) and np.array_equal(o1, o3)
+    assert np.array_equal(l1, l2) and np.array_equal(l1, l3)
+    compare(w, x, o1, l1)
