@@ -158,11 +158,13 @@ int64_t segkv_free_pages(const segkv_ctx *ctx);
 
 /*
  * Kernel timing with HIP events recorded on the context's stream around each
- * launch.  Enabling clears the counters.  segkv_read_timing synchronises the
- * recorded events and returns the summed duration (ms) and launch count of
- * one kernel (enum segkv_kernel).
+ * launch of the kernels selected by kernel_mask (bit k = enum segkv_kernel
+ * k; SEGKV_TIME_ALL selects all; 0 switches timing off).  Setting the mask
+ * clears the counters.  segkv_read_timing synchronises the recorded events
+ * and returns the summed duration (ms) and launch count of one kernel.
  */
-int segkv_set_timing(segkv_ctx *ctx, int32_t enable);
+#define SEGKV_TIME_ALL ((1 << SEGKV_KERNEL_COUNT) - 1)
+int segkv_set_timing(segkv_ctx *ctx, int32_t kernel_mask);
 int segkv_read_timing(segkv_ctx *ctx, int32_t kernel, double *total_ms, int64_t *launches);
 
 /*

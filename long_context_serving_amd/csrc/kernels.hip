@@ -455,7 +455,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
   __shared__ __attribute__((aligned(16))) float s_o[NW][kDecodeCols][D];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c16 = lane & 15, u = lane >> 4;
   const int G = a.group;
   const int piece_end = a.wg_piece_off[blockIdx.x + 1];
@@ -487,21 +487,21 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
     for (int db = 0; db < NDB; ++db) oacc[db] = f32x4{};
     float m = kNegInf, l = 0.f;
 
-    // This wave's keys, 32 at a time ("halves" of its 64-key chunks, chunk
-    // wave + NW*i).  Loads of the next half are in flight while the current
-    // half is computed (two register buffers, so the loop is unrolled by 2).
+    // This wave's keys in 64-key chunks (chunk wave + NW*i), each handled as
+    // two 32-key halves: all loads of a chunk are issued before its two
+    // halves are computed, so each wave keeps 32 KiB in flight.
     const int n_chunks = (key_end - key_begin + 63) / 64;
     const int my_chunks = n_chunks > wave ? (n_chunks - wave + NW - 1) / NW : 0;
     const int n_halves = 2 * my_chunks;
     auto half_base = [&](int j) { return key_begin + (wave + NW * (j >> 1)) * 64 + 32 * (j & 1); };
-    auto load_half = [&](int j, u32x4 (&kb_)[2][NKK], u32x4 (&vb_)[NDB]) {
+    auto load_half = [&](int j, u32x4 (&kb_)[2][NKK], u32x4 (&vb_)[NDB], int upage) {
       const int kbase = half_base(j);
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
         const int key = kbase + 8 * (c16 >> 2) + 4 * hb + (c16 & 3);
         const int rel = key - sg.first_token;
         const bool ok = key < key_end;
-        const int page = ok ? a.page_ids[sg.page_off + rel / P] : 0;
+        const int page = P == 64 ? upage : (ok ? a.page_ids[sg.page_off + rel / P] : 0);
         const uint16_t *krow = a.k_pool + (static_cast<size_t>(page) * P + rel % P) * D;
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
@@ -513,7 +513,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
       const int key = kbase + 8 * u;
       const int rel = key - sg.first_token;
       const bool ok = key < key_end;
-      const int page = ok ? a.page_ids[sg.page_off + rel / P] : 0;
+      const int page = P == 64 ? upage : (ok ? a.page_ids[sg.page_off + rel / P] : 0);
       const uint16_t *vbase = a.v_pool + static_cast<size_t>(page) * P * D + rel % P;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
@@ -569,12 +569,21 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
         oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vb_[db]), pb, oacc[db], 0, 0, 0);
     };
     u32x4 kb0[2][NKK], vb0[NDB], kb1[2][NKK], vb1[NDB];
-    if (n_halves > 0) load_half(0, kb0, vb0);
+    // P == 64: chunk j/2 of this wave is exactly one page; its id is a
+    // uniform (scalar) load, fetched one chunk ahead, so no vector load of
+    // the page table sits in front of the chunk's K/V loads.
+    auto chunk_page = [&](int j) {
+      const int pi = min((half_base(j) - sg.first_token) / P, sg.n_pages - 1);
+      return a.page_ids[sg.page_off + pi];
+    };
+    int upage = (P == 64 && n_halves > 0) ? chunk_page(0) : 0;
     for (int j = 0; j < n_halves; j += 2) {
-      load_half(j + 1, kb1, vb1);  // n_halves is even: half j + 1 exists
+      const int next = (P == 64 && j + 2 < n_halves) ? chunk_page(j + 2) : 0;
+      load_half(j, kb0, vb0, upage);
+      load_half(j + 1, kb1, vb1, upage);
       compute_half(j, kb0, vb0);
-      if (j + 2 < n_halves) load_half(j + 2, kb0, vb0);
       compute_half(j + 1, kb1, vb1);
+      upage = next;
     }
 
     // Per-wave column statistics, then merge the waves through LDS.
@@ -702,6 +711,20 @@ hipError_t launch_prefill(const PrefillArgs &a, int n_items, int head_dim, int p
 hipError_t launch_decode(const DecodeArgs &a, int n_wgs, int head_dim, int page_size, hipStream_t s) {
   if (n_wgs <= 0) return hipSuccess;
   SEGKV_DISPATCH_DP(decode_kernel, head_dim, page_size, dim3(n_wgs), dim3(kDecodeThreads), s, a);
+  return hipGetLastError();
+}
+
+// Copy of the per-call tables from pinned host memory to device memory.
+__global__ __launch_bounds__(256) void upload_kernel(uint4 *dst, const uint4 *src, size_t n16) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n16) dst[i] = src[i];
+}
+
+hipError_t launch_upload(void *dst, const void *src_pinned, size_t bytes, hipStream_t s) {
+  const size_t n16 = (bytes + 15) / 16;
+  if (n16 == 0) return hipSuccess;
+  hipLaunchKernelGGL(upload_kernel, dim3(static_cast<unsigned>((n16 + 255) / 256)), dim3(256), 0, s,
+                     static_cast<uint4 *>(dst), static_cast<const uint4 *>(src_pinned), n16);
   return hipGetLastError();
 }
 

@@ -90,6 +90,7 @@ struct segkv_ctx {
   char *d_meta = nullptr;
   size_t d_meta_cap = 0;
   char *h_stage[kStages] = {};
+  char *h_stage_dev[kStages] = {};  // the same pinned memory as seen by kernels
   size_t h_stage_cap[kStages] = {};
   hipEvent_t stage_ev[kStages] = {};
   bool stage_used[kStages] = {};
@@ -104,7 +105,7 @@ struct segkv_ctx {
   int32_t prefill_order = 0;  // 0 = longest-first, 1 = XCD-aware
 
   // timing
-  bool timing = false;
+  int32_t timing_mask = 0;  // bit k: record events around kernel k
   std::vector<TimedLaunch> pending;
   std::vector<hipEvent_t> event_pool;
   double tot_ms[SEGKV_KERNEL_COUNT] = {};
@@ -172,6 +173,8 @@ int acquire_stage(segkv_ctx *c, size_t bytes, char **out, int *slot_out) {
     size_t cap = std::max<size_t>(align_up(bytes, 1 << 16), 1 << 16);
     hipError_t e = hipHostMalloc(reinterpret_cast<void **>(&c->h_stage[slot]), cap, hipHostMallocDefault);
     if (e != hipSuccess) return c->device_fail(e, "hipHostMalloc(stage)");
+    e = hipHostGetDevicePointer(reinterpret_cast<void **>(&c->h_stage_dev[slot]), c->h_stage[slot], 0);
+    if (e != hipSuccess) return c->device_fail(e, "hipHostGetDevicePointer(stage)");
     c->h_stage_cap[slot] = cap;
   }
   *out = c->h_stage[slot];
@@ -197,10 +200,19 @@ int ensure_device_buffer(segkv_ctx *c, char **buf, size_t *cap, size_t bytes, co
   return SEGKV_OK;
 }
 
+int stage_done(segkv_ctx *c, int slot);
+
+// Tables go to device memory through a small copy kernel on the context's
+// stream (it reads the pinned staging buffer directly): a DMA-engine copy
+// between kernels costs a queue hand-off that is several times the copy.
 int upload(segkv_ctx *c, int slot, size_t bytes) {
-  hipError_t e = hipMemcpyAsync(c->d_meta, c->h_stage[slot], bytes, hipMemcpyHostToDevice, c->stream);
-  if (e != hipSuccess) return c->device_fail(e, "hipMemcpyAsync(tables)");
-  e = hipEventRecord(c->stage_ev[slot], c->stream);
+  hipError_t e = launch_upload(c->d_meta, c->h_stage_dev[slot], bytes, c->stream);
+  if (e != hipSuccess) return c->device_fail(e, "upload launch");
+  return stage_done(c, slot);
+}
+
+int stage_done(segkv_ctx *c, int slot) {
+  hipError_t e = hipEventRecord(c->stage_ev[slot], c->stream);
   if (e != hipSuccess) return c->device_fail(e, "hipEventRecord(stage)");
   c->stage_used[slot] = true;
   return SEGKV_OK;
@@ -209,7 +221,8 @@ int upload(segkv_ctx *c, int slot, size_t bytes) {
 // ---- timing --------------------------------------------------------------
 
 int timed_begin(segkv_ctx *c, TimedLaunch *t, int kernel) {
-  if (!c->timing) return SEGKV_OK;
+  t->kernel = -1;
+  if (!(c->timing_mask & (1 << kernel))) return SEGKV_OK;
   t->kernel = kernel;
   for (hipEvent_t *ev : {&t->start, &t->stop}) {
     if (!c->event_pool.empty()) {
@@ -226,7 +239,7 @@ int timed_begin(segkv_ctx *c, TimedLaunch *t, int kernel) {
 }
 
 int timed_end(segkv_ctx *c, TimedLaunch *t) {
-  if (!c->timing) return SEGKV_OK;
+  if (t->kernel < 0) return SEGKV_OK;
   hipError_t e = hipEventRecord(t->stop, c->stream);
   if (e != hipSuccess) return c->device_fail(e, "hipEventRecord");
   c->pending.push_back(*t);
@@ -523,8 +536,6 @@ int segkv_append_pages(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_
   if (!c->planning && n_items > 0) {
     rc = acquire_stage(c, bytes, &stage, &slot);
     if (rc) return rc;
-    rc = ensure_device_buffer(c, &c->d_meta, &c->d_meta_cap, bytes, "hipMalloc(tables)");
-    if (rc) return rc;
   }
 
   // Commit: trim, then allocate, then record scatter work.
@@ -568,21 +579,23 @@ int segkv_append_pages(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_
   }
   if (c->planning || n_items == 0) return SEGKV_OK;
 
-  rc = upload(c, slot, bytes);
-  if (rc) return rc;
   ScatterArgs a;
   a.k_new = static_cast<const uint16_t *>(k_new);
   a.v_new = static_cast<const uint16_t *>(v_new);
   a.k_pool = c->k_pool;
   a.v_pool = c->v_pool;
-  a.items = reinterpret_cast<const ScatterItem *>(c->d_meta);
+  // The scatter work list is read straight from the pinned staging buffer
+  // (one 32-byte item per workgroup), so the append needs no upload.
+  a.items = reinterpret_cast<const ScatterItem *>(c->h_stage_dev[slot]);
   a.num_kv_heads = c->Hkv;
   TimedLaunch t{};
   rc = timed_begin(c, &t, SEGKV_KERNEL_SCATTER);
   if (rc) return rc;
   hipError_t e = launch_scatter(a, static_cast<int>(n_items), c->D, c->P, c->stream);
   if (e != hipSuccess) return c->device_fail(e, "scatter launch");
-  return timed_end(c, &t);
+  rc = timed_end(c, &t);
+  if (rc) return rc;
+  return stage_done(c, slot);
 }
 
 int segkv_prefill(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_ids, const int32_t *cu_q,
@@ -940,16 +953,18 @@ int segkv_decode(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq
   return timed_end(c, &t2);
 }
 
-int segkv_set_timing(segkv_ctx *c, int32_t enable) {
+int segkv_set_timing(segkv_ctx *c, int32_t kernel_mask) {
   if (!c) return SEGKV_E_INVAL;
   if (c->planning) return c->fail(SEGKV_E_STATE, "timing needs a device context");
+  if (kernel_mask & ~((1 << SEGKV_KERNEL_COUNT) - 1))
+    return c->fail(SEGKV_E_INVAL, "timing mask 0x%x names unknown kernels", kernel_mask);
   int rc = drain_timing(c);
   if (rc) return rc;
   for (int k = 0; k < SEGKV_KERNEL_COUNT; ++k) {
     c->tot_ms[k] = 0.0;
     c->launches[k] = 0;
   }
-  c->timing = enable != 0;
+  c->timing_mask = kernel_mask;
   return SEGKV_OK;
 }
 

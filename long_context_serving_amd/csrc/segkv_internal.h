@@ -160,5 +160,7 @@ hipError_t launch_scatter(const ScatterArgs &a, int n_items, int head_dim, int p
 hipError_t launch_prefill(const PrefillArgs &a, int n_items, int head_dim, int page_size, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int n_wgs, int head_dim, int page_size, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, int n_items, int max_entries, int head_dim, hipStream_t s);
+// bytes are rounded up to 16; both buffers must hold the rounded size
+hipError_t launch_upload(void *dst, const void *src_pinned, size_t bytes, hipStream_t s);
 
 }  // namespace segkv

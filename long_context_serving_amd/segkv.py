@@ -295,8 +295,18 @@ class SegKV:
             raise SegKVError(int(v), self.last_error())
         return int(v)
 
-    def set_timing(self, enable: bool):
-        return self._check(self._lib.segkv_set_timing(self._h, 1 if enable else 0))
+    def set_timing(self, enable, kernels=None):
+        """Record HIP events around launches of ``kernels`` (ids KERNEL_*;
+        None = all) while ``enable`` is true."""
+        if not enable:
+            mask = 0
+        elif kernels is None:
+            mask = (1 << 4) - 1
+        else:
+            mask = 0
+            for k in kernels:
+                mask |= 1 << int(k)
+        return self._check(self._lib.segkv_set_timing(self._h, mask))
 
     def read_timing(self, kernel: int):
         """(total milliseconds, launches) of one kernel since timing was enabled."""

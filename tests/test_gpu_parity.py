@@ -197,3 +197,20 @@ def test_decode_repeated_calls_agree():
     assert np.array_equal(o1, o2) and np.array_equal(o1, o3)
     assert np.array_equal(l1, l2) and np.array_equal(l1, l3)
     compare(w, x, o1, l1)
+
+
+def test_kernel_timing_mask():
+    from long_context_serving_amd import runner as R
+    w = small("timing", (700,), (700,), 8, 2, 128, 64, (0, 100), seed=2)
+    x = wl.make_inputs(w)
+    run = R.WorkloadRun(w, R.to_device(w, x))
+    run.ctx.set_timing(True, [S.KERNEL_PREFILL])
+    run.load()
+    run.prefill()
+    ms, n = run.ctx.read_timing(S.KERNEL_PREFILL)
+    assert n == 1 and ms > 0
+    assert run.ctx.read_timing(S.KERNEL_SCATTER) == (0.0, 0)
+    run.ctx.set_timing(False)
+    with pytest.raises(S.SegKVError):
+        run.ctx._check(run.ctx._lib.segkv_set_timing(run.ctx._h, 1 << 9))
+    run.close()
