@@ -440,7 +440,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
 // +3).  K rows and V^T channel rows go from HBM straight into operand
 // registers.  Each 64-key chunk is four 16-key S^T blocks; block kb = 2s +
 // hb, row 4u + j holds key 32 s + 8 u + 4 hb + j, so lane group u feeds keys
-// 32 s + 8 u .. +7 to PV step s.  The four waves take chunks round-robin and
+// 32 s + 8 u .. +7 to PV step s.  The eight waves take chunks round-robin and
 // are merged through LDS.
 // ===========================================================================
 

@@ -17,11 +17,11 @@ namespace segkv {
 constexpr int kTileKeys = 64;      // keys per prefill KV tile (one LDS stage)
 constexpr int kPrefillRows = 256;  // (query position, query head) rows per prefill workgroup
 constexpr int kPrefillThreads = 512;  // 8 waves, 32 rows each, two per SIMD
-constexpr int kDecodeThreads = 256;
+constexpr int kDecodeThreads = 512;  // 8 waves, two per SIMD
 constexpr int kDecodeCols = 16;    // query heads handled by one decode work item (GQA group, padded)
 constexpr int kScatterThreads = 256;
 constexpr int kPrefillWgPerCu = 1;  // resident prefill workgroups per CU (96 KiB of LDS each)
-constexpr int kDecodeWgPerCu = 2;   // resident decode workgroups per CU
+constexpr int kDecodeWgPerCu = 1;   // resident decode workgroups per CU (the stream-K grid size)
 constexpr int kXcds = 8;           // MI355X: workgroup i of a launch runs on XCD i % 8
 
 struct SeqDesc {
