@@ -11,4 +11,5 @@ Modules:
   attention  masked softmax attention with per-head causal/window visibility
   segments   which tokens a head's segment must store
   ledger     closed-form visible-pair, FLOP and byte counts
+  rope       query-side rotary relocation by a per-head position offset
 """
