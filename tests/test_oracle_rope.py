@@ -1,75 +1,154 @@
 """Pins of the RoPE relocation oracle.
 
-* an independently written complex-number form of the rotation;
-* inverse and composition identities;
-* the relative-position property the relocation relies on;
-* end to end: keys encoded at canonical positions (document at 0) with
-  queries turned back by the document offset give the same attention as
-  keys and queries encoded at their true positions (full recomputation).
+* an independently written complex-number form of the rotation, for both
+  pairings and for a partial rotary block;
+* inverse and composition identities, and the relative-position property
+  that the relocation relies on;
+* round-to-nearest-even bfloat16 on hand-worked values and against the
+  input generator's float32 rounding;
+* end to end: keys encoded at canonical positions (document at 0), with
+  queries turned back by the document offset, give the attention of keys
+  and queries encoded at their true positions (full recomputation).
 """
 
 import numpy as np
 import pytest
 
+from long_context_serving_amd import workloads as wl
 from oracle import attention as A
 from oracle import rope as RP
 
 
-def test_rotation_matches_complex_multiplication():
-    rng = np.random.default_rng(0)
-    d, theta = 16, 10000.0
-    x = rng.standard_normal((5, d))
-    pos = np.array([0, 1, 7, 1000, 123457])
-    z = x[:, : d // 2] + 1j * x[:, d // 2:]
-    w = np.exp(1j * pos[:, None] * theta ** (-np.arange(d // 2) * 2.0 / d))
+def complex_rotation(x, pos, theta, style, rope_dims):
+    """Rotation written as complex multiplication: pair (a, b) -> (a + ib) *
+    exp(i pos w)."""
+    d = x.shape[-1]
+    r = rope_dims or d
+    blk = x[..., d - r:]
+    if style == 0:
+        z = blk[..., : r // 2] + 1j * blk[..., r // 2:]
+    else:
+        z = blk[..., 0::2] + 1j * blk[..., 1::2]
+    w = np.exp(1j * np.asarray(pos, dtype=np.float64)[..., None] * theta ** (-np.arange(r // 2) * 2.0 / r))
     zr = z * w
-    ref = np.concatenate([zr.real, zr.imag], axis=1)
-    np.testing.assert_allclose(RP.rope_rotate(x, pos, theta), ref, rtol=0, atol=1e-12)
+    out = np.array(x, dtype=np.float64, copy=True)
+    if style == 0:
+        out[..., d - r: d - r // 2] = zr.real
+        out[..., d - r // 2:] = zr.imag
+    else:
+        out[..., d - r::2] = zr.real
+        out[..., d - r + 1::2] = zr.imag
+    return out
 
 
-def test_inverse_and_composition():
+@pytest.mark.parametrize("style,d,rope_dims", [(0, 16, 0), (1, 16, 0), (0, 128, 64), (1, 64, 32), (0, 128, 0)])
+def test_rotation_matches_complex_multiplication(style, d, rope_dims):
+    rng = np.random.default_rng(d + rope_dims + style)
+    x = rng.standard_normal((5, d))
+    pos = np.array([0, 1, 7, -1000, 123457])
+    got = RP.rope_rotate(x, pos, 10000.0, style, rope_dims)
+    np.testing.assert_allclose(got, complex_rotation(x, pos, 10000.0, style, rope_dims), rtol=0, atol=1e-11)
+    if rope_dims:
+        np.testing.assert_array_equal(got[:, : d - rope_dims], x[:, : d - rope_dims])
+
+
+def test_interleaved_is_a_channel_permutation_of_rotate_half():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((3, 32))
+    perm = np.concatenate([np.arange(0, 32, 2), np.arange(1, 32, 2)])  # interleaved -> halves
+    a = RP.rope_rotate(x, 55, 10000.0, style=1)
+    b = RP.rope_rotate(x[:, perm], 55, 10000.0, style=0)
+    np.testing.assert_allclose(a[:, perm], b, atol=1e-13)
+
+
+@pytest.mark.parametrize("style", [0, 1])
+def test_inverse_and_composition(style):
     rng = np.random.default_rng(1)
     x = rng.standard_normal((4, 128))
     for th in (10000.0, 500000.0):
-        np.testing.assert_allclose(RP.rope_rotate(RP.rope_rotate(x, 977, th), -977, th), x, atol=1e-12)
-        np.testing.assert_allclose(RP.rope_rotate(RP.rope_rotate(x, 300, th), 45, th),
-                                   RP.rope_rotate(x, 345, th), atol=1e-11)
-        np.testing.assert_array_equal(RP.rope_rotate(x, 0, th), x)
+        np.testing.assert_allclose(RP.rope_rotate(RP.rope_rotate(x, 977, th, style), -977, th, style), x, atol=1e-12)
+        np.testing.assert_allclose(RP.rope_rotate(RP.rope_rotate(x, 300, th, style), 45, th, style),
+                                   RP.rope_rotate(x, 345, th, style), atol=1e-11)
+        np.testing.assert_array_equal(RP.rope_rotate(x, 0, th, style), x)
+        # a rotation preserves the norm of each row
+        np.testing.assert_allclose(np.linalg.norm(RP.rope_rotate(x, 12345, th, style), axis=-1),
+                                   np.linalg.norm(x, axis=-1), rtol=1e-13)
 
 
-def test_scores_depend_only_on_position_difference():
+@pytest.mark.parametrize("style,rope_dims", [(0, 0), (1, 0), (0, 64)])
+def test_scores_depend_only_on_position_difference(style, rope_dims):
     rng = np.random.default_rng(2)
-    q, k = rng.standard_normal(64), rng.standard_normal(64)
+    q, k = rng.standard_normal(128), rng.standard_normal(128)
     for p, j, delta in ((500, 17, 300), (9000, 8999, 8000), (5, 5, 5)):
-        s_true = RP.rope_rotate(q, p, 10000.0) @ RP.rope_rotate(k, j, 10000.0)
-        s_shift = RP.rope_rotate(q, p - delta, 10000.0) @ RP.rope_rotate(k, j - delta, 10000.0)
+        s_true = RP.rope_rotate(q, p, 10000.0, style, rope_dims) @ RP.rope_rotate(k, j, 10000.0, style, rope_dims)
+        s_shift = (RP.rope_rotate(q, p - delta, 10000.0, style, rope_dims)
+                   @ RP.rope_rotate(k, j - delta, 10000.0, style, rope_dims))
         assert abs(s_true - s_shift) < 1e-10
 
 
-@pytest.mark.parametrize("delta,window", [(0, 0), (37, 0), (1000, 16), (250, 0)])
-def test_canonical_keys_with_relocated_queries_equal_recomputation(delta, window):
+def test_round_to_bf16_hand_worked_values():
+    e = 2.0 ** -8
+    cases = {
+        1.0: 1.0,
+        1.0 + e: 1.0,                        # halfway, ties to the even significand
+        1.0 + 3 * e: 1.0 + 4 * e,            # halfway, the even neighbour is above
+        1.0 + e + 2.0 ** -30: 1.0 + 2 * e,   # just above halfway
+        -(1.0 + 3 * e): -(1.0 + 4 * e),
+        255.5: 256.0,                        # halfway between 255 and 256
+        0.0: 0.0,
+        3.0 * 2.0 ** -134: 2.0 ** -132,      # subnormal: 1.5 quanta of 2^-133 ties to 2 quanta
+    }
+    for x, want in cases.items():
+        assert RP.round_to_bf16(x) == want, (x, want)
+
+
+def test_round_to_bf16_agrees_with_float32_rounding_of_the_generator():
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(20000) * np.exp(rng.uniform(-20, 20, 20000))).astype(np.float32)
+    bits = wl.to_bf16_bits(x)
+    np.testing.assert_array_equal(RP.round_to_bf16(x.astype(np.float64)), A.bf16_bits_to_f64(bits))
+
+
+def test_relocated_queries_are_the_rounded_rotation():
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((9, 4, 64))
+    got = RP.relocate_queries(q, 777, 10000.0, 1, 32)
+    np.testing.assert_array_equal(got, RP.round_to_bf16(RP.rope_rotate(q, -777.0, 10000.0, 1, 32)))
+    np.testing.assert_array_equal(RP.relocate_queries(q, 0, 10000.0), q)
+
+
+@pytest.mark.parametrize("delta,window,style,rope_dims", [(0, 0, 0, 0), (37, 0, 0, 0), (1000, 16, 1, 0),
+                                                          (250, 0, 0, 16), (4096, 7, 1, 16)])
+def test_canonical_keys_with_relocated_queries_equal_recomputation(delta, window, style, rope_dims):
     """A document of n tokens sits at offset delta.  Its keys were encoded at
     canonical positions 0..n-1; queries arrive encoded at their absolute
-    positions delta + t.  Relocating the queries by -delta reproduces the
-    attention of keys encoded at their true positions."""
-    rng = np.random.default_rng(delta + window)
+    positions delta + t.  Turning the queries back by delta reproduces the
+    attention of keys encoded at their true positions: exactly before the
+    bfloat16 rounding, and within the rounding's effect after it."""
+    rng = np.random.default_rng(delta + window + style)
     n, hq, hkv, d, theta = 40, 4, 2, 32, 10000.0
     raw_q = rng.standard_normal((n, hq, d))
     raw_k = rng.standard_normal((n, hkv, d))
     v = rng.standard_normal((n, hkv, d))
     pos_true = delta + np.arange(n)
-    q_abs = RP.rope_rotate(raw_q, pos_true[:, None], theta)
-    k_true = RP.rope_rotate(raw_k, pos_true[:, None], theta)
-    k_canon = RP.rope_rotate(raw_k, np.arange(n)[:, None], theta)
+    enc = lambda x, pos: RP.rope_rotate(x, pos[:, None], theta, style, rope_dims)
+    q_abs, k_true, k_canon = enc(raw_q, pos_true), enc(raw_k, pos_true), enc(raw_k, np.arange(n))
     windows = (0, window)
     ref_o, ref_l = A.attend_sequence(q_abs, k_true, v, windows, 0.2)
-    got_o, got_l = RP.attend_sequence_relocated(q_abs, k_canon, v, windows, 0.2, (delta, delta), theta)
-    np.testing.assert_allclose(got_o, ref_o, atol=1e-10)
-    np.testing.assert_allclose(got_l, ref_l, atol=1e-10)
+    exact_o, exact_l = A.attend_sequence(RP.rope_rotate(q_abs, -float(delta), theta, style, rope_dims),
+                                         k_canon, v, windows, 0.2)
+    np.testing.assert_allclose(exact_o, ref_o, atol=1e-10)
+    np.testing.assert_allclose(exact_l, ref_l, atol=1e-10)
+    got_o, got_l = RP.attend_sequence_relocated(q_abs, k_canon, v, windows, 0.2, (delta, delta), theta,
+                                                style, rope_dims)
+    # bf16 rounding moves each query channel by at most 2^-9 of its value, so
+    # a score moves by at most scale * 2^-9 * |q| |k| (the rotation keeps |q|)
+    bound = 0.2 * 2.0 ** -9 * np.max(np.linalg.norm(q_abs, axis=-1)) * np.max(np.linalg.norm(k_canon, axis=-1))
+    assert np.max(np.abs(got_l - ref_l)) <= bound
+    assert np.max(np.abs(got_o - ref_o)) <= 2 * bound * np.max(np.abs(v))
     if delta:
-        # without the relocation the result is different
         bad_o, _ = A.attend_sequence(q_abs, k_canon, v, windows, 0.2)
-        assert np.max(np.abs(bad_o - ref_o)) > 1e-3
+        assert np.max(np.abs(bad_o - ref_o)) > 1e-2
 
 
 def test_zero_delta_heads_are_untouched():
@@ -81,3 +160,18 @@ def test_zero_delta_heads_are_untouched():
     o2, l2 = A.attend_sequence(q, k, v, (0, 3), 0.3)
     np.testing.assert_array_equal(o1, o2)
     np.testing.assert_array_equal(l1, l2)
+
+
+def test_each_kv_head_group_takes_its_own_delta():
+    rng = np.random.default_rng(8)
+    n, theta = 30, 10000.0
+    q = rng.standard_normal((n, 6, 16))
+    k = rng.standard_normal((n, 3, 16))
+    v = rng.standard_normal((n, 3, 16))
+    deltas = (0, 500, 90)
+    o, l = RP.attend_sequence_relocated(q, k, v, (0, 4, 0), 0.25, deltas, theta)
+    for g, dl in enumerate(deltas):
+        qg = RP.relocate_queries(q[:, 2 * g: 2 * g + 2], dl, theta)
+        og, lg = A.attend_sequence(qg, k[:, g: g + 1], v[:, g: g + 1], ((0, 4, 0)[g],), 0.25)
+        np.testing.assert_array_equal(o[:, 2 * g: 2 * g + 2], og)
+        np.testing.assert_array_equal(l[:, 2 * g: 2 * g + 2], lg)
