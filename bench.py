@@ -18,6 +18,10 @@ In the same JSON line:
                 dense bf16 MFMA peak (traffic: rocprofv3 counter bytes when
                 they were taken on the current kernel source, else null);
   all_global    the same steps with every head forced global;
+  relocation    query-side RoPE relocation: the same prefill and decode with
+                every local head's queries relocated by a document offset
+                (the global head at offset 0), and the cost over the plain
+                kernels;
   protocol      3 unmeasured + 10 measured (segmented, all-global) pairs,
                 p50 / p95 of the prefill kernel time;
   decode        visible-KV GB/s of split-KV decode + combine at 32K x 31
@@ -48,6 +52,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "visible-token attention TFLOP/s (prefill) & visible-KV GB/s (decode), 1 MI355X"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "long_context_serving_amd", "csrc", "kernels.hip")
+RELOCATION_OFFSET = 8192    # document offset of the relocation arm
 
 
 def log(*a):
@@ -89,11 +94,11 @@ def kernel_avg(ctx, kernel):
 
 # --------------------------------------------------------------- prefill
 
-def prefill_arm(w, dev, steps, warmup, windows=None, split_tiles=None):
+def prefill_arm(w, dev, steps, warmup, windows=None, split_tiles=None, deltas=None):
     import torch
     from long_context_serving_amd import runner as R
     from long_context_serving_amd import segkv as S
-    run = R.WorkloadRun(w, dev, windows=windows)
+    run = R.WorkloadRun(w, dev, windows=windows, deltas=deltas)
     if split_tiles:
         run.ctx.set_tuning(S.TUNE_PREFILL_SPLIT_TILES, split_tiles)
     o = torch.empty_like(dev.q)
@@ -149,11 +154,11 @@ def paired_protocol(run_a, run_b, warm=3, measured=10):
 
 # ---------------------------------------------------------------- decode
 
-def decode_arm(w, dev, steps, warmup, windows=None):
+def decode_arm(w, dev, steps, warmup, windows=None, deltas=None):
     import torch
     from long_context_serving_amd import runner as R
     from long_context_serving_amd import segkv as S
-    run = R.WorkloadRun(w, dev, windows=windows).load()
+    run = R.WorkloadRun(w, dev, windows=windows, deltas=deltas).load()
     o = torch.empty_like(dev.q)
     lse = torch.empty(dev.q.shape[:2], dtype=torch.float32, device=dev.q.device)
     for _ in range(warmup):
@@ -173,6 +178,12 @@ def decode_arm(w, dev, steps, warmup, windows=None):
 
 
 # ----------------------------------------------------------- cpu baseline
+
+def local_head_deltas(w, offset):
+    """Every local KV head of every sequence relocated by ``offset``; global
+    heads (recomputed online at their true positions) by 0."""
+    return [[offset if win > 0 else 0 for win in w.windows] for _ in range(w.n_seqs)]
+
 
 def cpu_baseline(w, x, budget_s=15.0):
     """The fp64 oracle, as it stands, on a seeded sample of query rows of the
@@ -217,8 +228,11 @@ def cpu_baseline(w, x, budget_s=15.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # The GPU reaches its steady clock after ~100 headline steps (~40 ms of
+    # work) and drops back within a second of idling, so every arm warms up
+    # with its own W untimed steps.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all",
                     help="profiling runs: only the segmented headline prefill, or only segmented decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -272,6 +286,10 @@ def main():
             log(f"  {glob}")
             proto = paired_protocol(run_seg, run_glob)
             run_glob.close()
+            log("prefill relocated")
+            run_rel, rel = prefill_arm(headline, dev2, K, Wm, deltas=local_head_deltas(headline, RELOCATION_OFFSET))
+            run_rel.close()
+            log(f"  {rel}")
         run_seg.close()
         achieved = flops / (seg["prefill_kernel_ms"] * 1e-3) / 1e12
         traffic = measured_traffic("prefill_" + headline.name)
@@ -298,6 +316,11 @@ def main():
                            "segmented_speedup_step": glob["ms_per_step"] / seg["ms_per_step"],
                            "segmented_speedup_kernel": glob["prefill_kernel_ms"] / seg["prefill_kernel_ms"]},
             "protocol": proto,
+            "relocation": {"offset": RELOCATION_OFFSET, "prefill": {
+                "kernel_tflops": flops / (rel["prefill_kernel_ms"] * 1e-3) / 1e12,
+                "step_tflops": flops / (rel["ms_per_step"] * 1e-3) / 1e12,
+                "prefill_kernel_ms": rel["prefill_kernel_ms"],
+                "kernel_time_over_plain": rel["prefill_kernel_ms"] / seg["prefill_kernel_ms"]}},
         })
         del dev2
 
@@ -312,11 +335,14 @@ def main():
         log("decode segmented")
         d = decode_arm(dw, dev4, K, Wm)
         log(f"  {d}")
-        dg = None
+        dg = dr = None
         if args.only == "all":
             log("decode all-global")
             dg = decode_arm(dw, dev4, K, Wm, windows=(0,) * dw.num_kv_heads)
             log(f"  {dg}")
+            log("decode relocated")
+            dr = decode_arm(dw, dev4, K, Wm, deltas=local_head_deltas(dw, RELOCATION_OFFSET))
+            log(f"  {dr}")
         kern = d["split_kernel_ms"] + d["combine_kernel_ms"]
         dec = {
             "metric": "visible-KV GB/s (decode)", "unit": "GB/s", "workload": dw.name,
@@ -335,6 +361,11 @@ def main():
             kern_g = dg["split_kernel_ms"] + dg["combine_kernel_ms"]
             dec["all_global"] = {"value": by_g["total"] / (kern_g * 1e-3) / 1e9, "visible_bytes": by_g,
                                  "detail": dg, "segmented_speedup_kernel": kern_g / kern}
+        if dr is not None:
+            kern_r = dr["split_kernel_ms"] + dr["combine_kernel_ms"]
+            out.setdefault("relocation", {"offset": RELOCATION_OFFSET})["decode"] = {
+                "value": by["total"] / (kern_r * 1e-3) / 1e9, "unit": "GB/s", "detail": dr,
+                "kernel_time_over_plain": kern_r / kern}
         out["decode"] = dec
         del dev4
 
@@ -346,8 +377,8 @@ def main():
             dev = R.to_device(w, x)
             del x
             f = M.prefill_flops(w)
-            steps = max(2, K // 4)
-            run, r = prefill_arm(w, dev, steps, 1, split_tiles=split)
+            steps = max(2, K // 8)
+            run, r = prefill_arm(w, dev, steps, max(1, Wm // 8), split_tiles=split)
             run.close()
             sec[w.name] = {"visible_flops": f, "steps": steps, "step_tflops": f / (r["ms_per_step"] * 1e-3) / 1e12,
                            "kernel_tflops": f / ((r["prefill_kernel_ms"] + r["combine_kernel_ms"]) * 1e-3) / 1e12,

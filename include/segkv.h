@@ -16,7 +16,9 @@
  * W, p - W < j.  Queries are the last tokens of their sequence: query t of a
  * sequence with kv_len cached tokens and q_len queries sits at
  * kv_len - q_len + t.  Query head h uses KV head h / (num_q_heads /
- * num_kv_heads).  Q and K are taken after any position encoding.
+ * num_kv_heads).  Q and K are taken after any position encoding; a segment
+ * whose keys were encoded at shifted positions takes a query rotation set
+ * by segkv_set_relocation.
  *
  * Outputs: o = softmax(scale * q k^T restricted to visible keys) v, rounded
  * once to bf16, and lse = ln(sum over visible keys of exp(scale * q.k)) in
@@ -79,6 +81,13 @@ typedef struct segkv_config {
                              (layer, sequence, KV head) */
   void *v_pool;           /* device bf16 [num_pages][head_dim][page_size]: each V page is stored transposed */
   void *stream;           /* hipStream_t for all device work; NULL = the default stream */
+  /* Rotary position code of the queries, used only by segkv_set_relocation
+     (zero-initialised fields give the defaults). */
+  float rope_theta;       /* base of the rotary frequencies; 0 => 10000 */
+  int32_t rope_style;     /* 0: rotate-half (channel i pairs with i + rope_dims/2);
+                             1: interleaved (channels 2i and 2i+1 pair) */
+  int32_t rope_dims;      /* rotary channels, the trailing ones of a head; 0 => head_dim; otherwise a
+                             multiple of 16 in [16, head_dim].  Leading channels carry no position code. */
 } segkv_config;
 
 /*
@@ -139,8 +148,28 @@ int segkv_prefill(segkv_ctx *ctx, int32_t layer, int32_t n_seqs, const int32_t *
 int segkv_decode(segkv_ctx *ctx, int32_t layer, int32_t n_seqs, const int32_t *seq_ids,
                  const void *q, void *o, float *lse);
 
-/* Return every page of a sequence (all layers, all heads) to the pool and
- * reset its length to 0. */
+/*
+ * Query-side RoPE relocation ("RedKnot-MLA: Multi-Head Offline-Online Reuse
+ * for DeepSeek-V4 Long-Context Serving" review, "Summary"; the paper page's
+ * abstract).  A reused document's KV is encoded at canonical positions
+ * (the document starting at 0); placed at offset delta in a live request,
+ * its keys keep that encoding and the queries are turned back by delta
+ * instead.  A rotary code makes q.k depend only on the position difference,
+ * so the scores equal those of keys re-encoded at their true positions.
+ *
+ * Sets the offset of every (layer, KV head) segment of one sequence:
+ *   deltas  host int32 [num_layers][num_kv_heads], or NULL for all zero.
+ * Later prefill and decode calls rotate each query of KV head g's group by
+ * -delta (pair i of the rotary block by angle -delta * rope_theta^(-2i /
+ * rope_dims)) in fp32 from an fp64 cos/sin table, and round the result once
+ * to bf16 before scoring.  delta = 0 leaves the queries untouched.  Offsets
+ * persist until changed or until segkv_release, which clears them.  Valid in
+ * a planning-only context (host state only).
+ */
+int segkv_set_relocation(segkv_ctx *ctx, int32_t seq_id, const int32_t *deltas);
+
+/* Return every page of a sequence (all layers, all heads) to the pool,
+ * reset its length to 0 and clear its relocation offsets. */
 int segkv_release(segkv_ctx *ctx, int32_t seq_id);
 
 /*

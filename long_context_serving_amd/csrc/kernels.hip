@@ -60,6 +60,38 @@ __device__ __forceinline__ bf16x8 pack8_bf16(float a0, float a1, float a2, float
   return v;
 }
 
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// Query-side RoPE relocation of channels ch0 .. ch0+7 of one query row
+// ("RedKnot-MLA: Multi-Head Offline-Online Reuse for DeepSeek-V4 Long-Context
+// Serving" review, "Summary"): channel c becomes cos[c] q[c] + ssin[c]
+// q[partner(c)] in fp32 (tab = cos[D] then signed sin[D] of the segment's
+// offset), rounded once to bf16.  ch0 is a multiple of 8.
+template <int D>
+__device__ __forceinline__ u32x4 relocate_chunk(const uint16_t *qrow, int ch0, const float *tab, const RopeArgs &r) {
+  const u32x4 x = ld16(qrow + ch0);
+  int pc = ch0;
+  if (r.style == 0 && ch0 >= r.lo) pc = ch0 - r.lo < r.half ? ch0 + r.half : ch0 - r.half;
+  const u32x4 y = ld16(qrow + pc);
+  const f32x4 c0 = *reinterpret_cast<const f32x4 *>(tab + ch0);
+  const f32x4 c1 = *reinterpret_cast<const f32x4 *>(tab + ch0 + 4);
+  const f32x4 s0 = *reinterpret_cast<const f32x4 *>(tab + D + ch0);
+  const f32x4 s1 = *reinterpret_cast<const f32x4 *>(tab + D + ch0 + 4);
+  const float cs[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+  const float sn[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+  float out[8];
+  const bool swap = r.style == 1;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float xl = bf16_lo(x[w]), xh = bf16_hi(x[w]);
+    const float yl = bf16_lo(y[w]), yh = bf16_hi(y[w]);
+    out[2 * w] = cs[2 * w] * xl + sn[2 * w] * (swap ? yh : yl);
+    out[2 * w + 1] = cs[2 * w + 1] * xh + sn[2 * w + 1] * (swap ? yl : yh);
+  }
+  return __builtin_bit_cast(u32x4, pack8_bf16(out[0], out[1], out[2], out[3], out[4], out[5], out[6], out[7]));
+}
+
 // ===========================================================================
 // Scatter: copy newly appended K/V rows into their pages.
 // ===========================================================================
@@ -228,11 +260,21 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
   bf16x8 qv[NKK];
   {
     const uint16_t *qrow = a.q + (static_cast<size_t>(sd.q_start + t) * a.num_q_heads + h) * D;
+    if (sg.rope_off < 0) {
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (valid) x = ld16(qrow + kk * 16 + half * 8);
-      qv[kk] = as_bf16x8(x);
+      for (int kk = 0; kk < NKK; ++kk) {
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (valid) x = ld16(qrow + kk * 16 + half * 8);
+        qv[kk] = as_bf16x8(x);
+      }
+    } else {
+      const float *tab = a.rope.tables + sg.rope_off;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (valid) x = relocate_chunk<D>(qrow, kk * 16 + half * 8, tab, a.rope);
+        qv[kk] = as_bf16x8(x);
+      }
     }
   }
 
@@ -474,11 +516,21 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
     bf16x8 qv[NKK];
     {
       const uint16_t *qrow = a.q + (static_cast<size_t>(sd.q_start) * a.num_q_heads + it.kv_head * G + c16) * D;
+      if (sg.rope_off < 0) {
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (c16 < G) x = ld16(qrow + kk * 32 + u * 8);
-        qv[kk] = as_bf16x8(x);
+        for (int kk = 0; kk < NKK; ++kk) {
+          u32x4 x = {0u, 0u, 0u, 0u};
+          if (c16 < G) x = ld16(qrow + kk * 32 + u * 8);
+          qv[kk] = as_bf16x8(x);
+        }
+      } else {
+        const float *tab = a.rope.tables + sg.rope_off;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          u32x4 x = {0u, 0u, 0u, 0u};
+          if (c16 < G) x = relocate_chunk<D>(qrow, kk * 32 + u * 8, tab, a.rope);
+          qv[kk] = as_bf16x8(x);
+        }
       }
     }
 

@@ -37,6 +37,7 @@ constexpr int64_t kMinSplitTiles = 16;
 
 struct Segment {
   int32_t first_token = 0;
+  int32_t delta = 0;           // query relocation offset (0 = none)
   std::vector<int32_t> pages;  // live pages are pages[head, size)
   size_t head = 0;
   int32_t n_live() const { return static_cast<int32_t>(pages.size() - head); }
@@ -76,6 +77,9 @@ struct segkv_ctx {
   int64_t num_pages = 0;
   float scale = 0.f;
   std::vector<int32_t> window;  // [L][Hkv]
+  double rope_theta = 10000.0;
+  int32_t rope_style = 0;  // 0 rotate-half, 1 interleaved
+  int32_t rope_dims = 0;   // trailing rotary channels
   uint16_t *k_pool = nullptr;
   uint16_t *v_pool = nullptr;
   hipStream_t stream = nullptr;
@@ -113,6 +117,7 @@ struct segkv_ctx {
 
   // scratch reused across calls
   std::vector<int32_t> scratch_i32;
+  std::vector<int32_t> scratch_deltas;  // distinct nonzero offsets of the current call
   std::vector<PrefillItem> scratch_pitems;
   std::vector<CombineItem> scratch_citems;
 
@@ -275,38 +280,91 @@ int check_layer_seqs(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t 
   return SEGKV_OK;
 }
 
-// Lays out SeqDesc / SegDesc / page ids for a batch into `dst` (when not
-// null) and returns the byte size of that block.
-size_t seq_tables_bytes(const segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_ids,
-                        int64_t *total_pages) {
+// Byte offsets of the per-call sequence tables: SeqDesc, SegDesc, page ids
+// and relocation tables, each 16-byte aligned.
+struct SeqTables {
+  size_t seg_off = 0, pid_off = 0, rope_off = 0, bytes = 0;
+};
+
+// Sizes the tables of a batch; collects the distinct nonzero relocation
+// offsets of its segments into c->scratch_deltas (sorted).
+SeqTables seq_tables_layout(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_ids) {
   int64_t pages = 0;
+  std::vector<int32_t> &deltas = c->scratch_deltas;
+  deltas.clear();
   for (int32_t b = 0; b < n_seqs; ++b)
-    for (int32_t g = 0; g < c->Hkv; ++g) pages += c->seg(layer, seq_ids[b], g).n_live();
-  *total_pages = pages;
-  size_t bytes = align_up(sizeof(SeqDesc) * n_seqs, 16);
-  bytes += align_up(sizeof(SegDesc) * static_cast<size_t>(n_seqs) * c->Hkv, 16);
-  bytes += align_up(sizeof(int32_t) * static_cast<size_t>(pages), 16);
-  return bytes;
+    for (int32_t g = 0; g < c->Hkv; ++g) {
+      const Segment &sg = c->seg(layer, seq_ids[b], g);
+      pages += sg.n_live();
+      if (sg.delta) deltas.push_back(sg.delta);
+    }
+  std::sort(deltas.begin(), deltas.end());
+  deltas.erase(std::unique(deltas.begin(), deltas.end()), deltas.end());
+  SeqTables t;
+  t.seg_off = align_up(sizeof(SeqDesc) * n_seqs, 16);
+  t.pid_off = t.seg_off + align_up(sizeof(SegDesc) * static_cast<size_t>(n_seqs) * c->Hkv, 16);
+  t.rope_off = t.pid_off + align_up(sizeof(int32_t) * static_cast<size_t>(pages), 16);
+  t.bytes = t.rope_off + sizeof(float) * 2 * static_cast<size_t>(c->D) * deltas.size();
+  return t;
+}
+
+// Relocation table of one offset: channel ch of a query becomes cos[ch] *
+// q[ch] + ssin[ch] * q[partner(ch)], the rotation of its pair by -delta
+// radians times the pair's frequency rope_theta^(-2i / rope_dims).  The
+// first element of a pair takes -sin, the second +sin.  Evaluated in fp64,
+// stored in fp32.
+void write_rope_table(const segkv_ctx *c, int32_t delta, float *cs) {
+  const int32_t D = c->D, R = c->rope_dims, lo = D - R;
+  for (int32_t ch = 0; ch < D; ++ch) {
+    if (ch < lo) {
+      cs[ch] = 1.f;
+      cs[D + ch] = 0.f;
+      continue;
+    }
+    const int32_t j = ch - lo;
+    const int32_t pair = c->rope_style == 0 ? j % (R / 2) : j / 2;
+    const bool first = c->rope_style == 0 ? j < R / 2 : (j % 2) == 0;
+    const double ang = -static_cast<double>(delta) * std::pow(c->rope_theta, -2.0 * pair / R);
+    cs[ch] = static_cast<float>(std::cos(ang));
+    cs[D + ch] = static_cast<float>(first ? -std::sin(ang) : std::sin(ang));
+  }
 }
 
 void write_seq_tables(const segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_ids,
-                      const int32_t *q_start, const int32_t *q_len, int64_t total_pages, char *dst) {
+                      const int32_t *q_start, const int32_t *q_len, const SeqTables &t, char *dst) {
   SeqDesc *sd = reinterpret_cast<SeqDesc *>(dst);
-  SegDesc *gd = reinterpret_cast<SegDesc *>(dst + align_up(sizeof(SeqDesc) * n_seqs, 16));
-  int32_t *pid = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(gd) +
-                                             align_up(sizeof(SegDesc) * static_cast<size_t>(n_seqs) * c->Hkv, 16));
+  SegDesc *gd = reinterpret_cast<SegDesc *>(dst + t.seg_off);
+  int32_t *pid = reinterpret_cast<int32_t *>(dst + t.pid_off);
+  float *rope = reinterpret_cast<float *>(dst + t.rope_off);
+  const std::vector<int32_t> &deltas = c->scratch_deltas;
+  for (size_t i = 0; i < deltas.size(); ++i) write_rope_table(c, deltas[i], rope + i * 2 * c->D);
   int32_t off = 0;
   for (int32_t b = 0; b < n_seqs; ++b) {
     const SeqLayer &s = c->sl(layer, seq_ids[b]);
     sd[b] = SeqDesc{s.kv_len, q_start ? q_start[b] : b, q_len ? q_len[b] : 1, 0};
     for (int32_t g = 0; g < c->Hkv; ++g) {
       const Segment &sg = c->seg(layer, seq_ids[b], g);
-      gd[static_cast<size_t>(b) * c->Hkv + g] = SegDesc{sg.first_token, off, sg.n_live(), c->win(layer, g)};
+      int32_t rope_off = -1;
+      if (sg.delta) {
+        const size_t i = static_cast<size_t>(std::lower_bound(deltas.begin(), deltas.end(), sg.delta) - deltas.begin());
+        rope_off = static_cast<int32_t>(i * 2 * c->D);
+      }
+      gd[static_cast<size_t>(b) * c->Hkv + g] =
+          SegDesc{sg.first_token, off, sg.n_live(), c->win(layer, g), rope_off, 0, 0, 0};
       std::memcpy(pid + off, sg.live(), sizeof(int32_t) * sg.n_live());
       off += sg.n_live();
     }
   }
-  (void)total_pages;
+}
+
+RopeArgs rope_args(const segkv_ctx *c, const SeqTables &t) {
+  RopeArgs r;
+  r.tables = reinterpret_cast<const float *>(c->d_meta + t.rope_off);
+  r.lo = c->D - c->rope_dims;
+  r.half = c->rope_dims / 2;
+  r.style = c->rope_style;
+  r.pad = 0;
+  return r;
 }
 
 }  // namespace
@@ -343,6 +401,12 @@ int segkv_create(const segkv_config *cfg, segkv_ctx **out) {
     return bad(SEGKV_E_INVAL, "k_pool and v_pool must both be set or both be NULL");
   if (!(cfg->softmax_scale >= 0.f) || std::isinf(cfg->softmax_scale))
     return bad(SEGKV_E_INVAL, "softmax_scale must be finite and >= 0");
+  if (!(cfg->rope_theta >= 0.f) || std::isinf(cfg->rope_theta) || (cfg->rope_theta > 0.f && cfg->rope_theta <= 1.f))
+    return bad(SEGKV_E_INVAL, "rope_theta must be 0 (default) or a finite value > 1");
+  if (cfg->rope_style != 0 && cfg->rope_style != 1)
+    return bad(SEGKV_E_INVAL, "rope_style must be 0 (rotate-half) or 1 (interleaved)");
+  if (cfg->rope_dims != 0 && (cfg->rope_dims < 16 || cfg->rope_dims > cfg->head_dim || cfg->rope_dims % 16))
+    return bad(SEGKV_E_INVAL, "rope_dims must be 0 or a multiple of 16 in [16, head_dim]");
   size_t nwin = static_cast<size_t>(cfg->num_layers) * cfg->num_kv_heads;
   for (size_t i = 0; i < nwin; ++i)
     if (cfg->head_window[i] < 0) return bad(SEGKV_E_INVAL, "head_window entries must be >= 0");
@@ -359,6 +423,9 @@ int segkv_create(const segkv_config *cfg, segkv_ctx **out) {
   c->num_pages = cfg->num_pages;
   c->scale = cfg->softmax_scale > 0.f ? cfg->softmax_scale : 1.0f / std::sqrt(static_cast<float>(cfg->head_dim));
   c->window.assign(cfg->head_window, cfg->head_window + nwin);
+  c->rope_theta = cfg->rope_theta > 0.f ? static_cast<double>(cfg->rope_theta) : 10000.0;
+  c->rope_style = cfg->rope_style;
+  c->rope_dims = cfg->rope_dims ? cfg->rope_dims : cfg->head_dim;
   c->k_pool = static_cast<uint16_t *>(cfg->k_pool);
   c->v_pool = static_cast<uint16_t *>(cfg->v_pool);
   c->stream = static_cast<hipStream_t>(cfg->stream);
@@ -444,6 +511,15 @@ int segkv_page_table(const segkv_ctx *cc, int32_t layer, int32_t seq_id, int32_t
   return SEGKV_OK;
 }
 
+int segkv_set_relocation(segkv_ctx *c, int32_t seq_id, const int32_t *deltas) {
+  if (!c) return SEGKV_E_INVAL;
+  if (seq_id < 0 || seq_id >= c->S) return c->fail(SEGKV_E_RANGE, "seq id %d out of range", seq_id);
+  for (int32_t layer = 0; layer < c->L; ++layer)
+    for (int32_t g = 0; g < c->Hkv; ++g)
+      c->seg(layer, seq_id, g).delta = deltas ? deltas[static_cast<size_t>(layer) * c->Hkv + g] : 0;
+  return SEGKV_OK;
+}
+
 int segkv_release(segkv_ctx *c, int32_t seq_id) {
   if (!c) return SEGKV_E_INVAL;
   if (seq_id < 0 || seq_id >= c->S) return c->fail(SEGKV_E_RANGE, "seq id %d out of range", seq_id);
@@ -454,6 +530,7 @@ int segkv_release(segkv_ctx *c, int32_t seq_id) {
       s.pages.clear();
       s.head = 0;
       s.first_token = 0;
+      s.delta = 0;
     }
     c->sl(layer, seq_id) = SeqLayer{};
   }
@@ -719,8 +796,8 @@ int segkv_prefill(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *se
     lpt_sort(items);
   }
 
-  int64_t total_pages = 0;
-  const size_t tbytes = seq_tables_bytes(c, layer, n_seqs, seq_ids, &total_pages);
+  const SeqTables tl = seq_tables_layout(c, layer, n_seqs, seq_ids);
+  const size_t tbytes = align_up(tl.bytes, 16);
   const size_t ibytes = align_up(sizeof(PrefillItem) * items.size(), 16);
   const size_t cbytes = sizeof(CombineItem) * citems.size();
   const size_t bytes = tbytes + ibytes + cbytes;
@@ -741,7 +818,7 @@ int segkv_prefill(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *se
     qs[b] = cu_q[b];
     ql[b] = cu_q[b + 1] - cu_q[b];
   }
-  write_seq_tables(c, layer, n_seqs, seq_ids, qs.data(), ql.data(), total_pages, stage);
+  write_seq_tables(c, layer, n_seqs, seq_ids, qs.data(), ql.data(), tl, stage);
   std::memcpy(stage + tbytes, items.data(), sizeof(PrefillItem) * items.size());
   if (cbytes) std::memcpy(stage + tbytes + ibytes, citems.data(), cbytes);
   rc = upload(c, slot, bytes);
@@ -754,9 +831,9 @@ int segkv_prefill(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *se
   a.k_pool = c->k_pool;
   a.v_pool = c->v_pool;
   a.seqs = reinterpret_cast<const SeqDesc *>(c->d_meta);
-  a.segs = reinterpret_cast<const SegDesc *>(c->d_meta + align_up(sizeof(SeqDesc) * n_seqs, 16));
-  a.page_ids = reinterpret_cast<const int32_t *>(reinterpret_cast<const char *>(a.segs) +
-                                                 align_up(sizeof(SegDesc) * static_cast<size_t>(n_seqs) * c->Hkv, 16));
+  a.segs = reinterpret_cast<const SegDesc *>(c->d_meta + tl.seg_off);
+  a.page_ids = reinterpret_cast<const int32_t *>(c->d_meta + tl.pid_off);
+  a.rope = rope_args(c, tl);
   a.items = reinterpret_cast<const PrefillItem *>(c->d_meta + tbytes);
   a.part_o = c->d_part;
   a.part_lse = c->d_part ? c->d_part + static_cast<size_t>(n_parts) * kPrefillRows * c->D : nullptr;
@@ -888,8 +965,8 @@ int segkv_decode(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq
   }
   const int32_t n_parts = n_parts_total;
 
-  int64_t total_pages = 0;
-  const size_t tbytes = seq_tables_bytes(c, layer, n_seqs, seq_ids, &total_pages);
+  const SeqTables tl = seq_tables_layout(c, layer, n_seqs, seq_ids);
+  const size_t tbytes = align_up(tl.bytes, 16);
   const size_t ibytes = align_up(sizeof(DecodeItem) * ditems.size(), 16);
   const size_t obytes = align_up(sizeof(int32_t) * wg_off.size(), 16);
   const size_t cbytes = sizeof(CombineItem) * citems.size();
@@ -904,7 +981,7 @@ int segkv_decode(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq
   rc = ensure_device_buffer(c, reinterpret_cast<char **>(&c->d_part), &c->d_part_cap, part_bytes,
                             "hipMalloc(partials)");
   if (rc) return rc;
-  write_seq_tables(c, layer, n_seqs, seq_ids, nullptr, nullptr, total_pages, stage);
+  write_seq_tables(c, layer, n_seqs, seq_ids, nullptr, nullptr, tl, stage);
   std::memcpy(stage + tbytes, ditems.data(), sizeof(DecodeItem) * ditems.size());
   std::memcpy(stage + tbytes + ibytes, wg_off.data(), sizeof(int32_t) * wg_off.size());
   if (cbytes) std::memcpy(stage + tbytes + ibytes + obytes, citems.data(), cbytes);
@@ -916,9 +993,9 @@ int segkv_decode(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq
   a.k_pool = c->k_pool;
   a.v_pool = c->v_pool;
   a.seqs = reinterpret_cast<const SeqDesc *>(c->d_meta);
-  a.segs = reinterpret_cast<const SegDesc *>(c->d_meta + align_up(sizeof(SeqDesc) * n_seqs, 16));
-  a.page_ids = reinterpret_cast<const int32_t *>(reinterpret_cast<const char *>(a.segs) +
-                                                 align_up(sizeof(SegDesc) * static_cast<size_t>(n_seqs) * c->Hkv, 16));
+  a.segs = reinterpret_cast<const SegDesc *>(c->d_meta + tl.seg_off);
+  a.page_ids = reinterpret_cast<const int32_t *>(c->d_meta + tl.pid_off);
+  a.rope = rope_args(c, tl);
   a.items = reinterpret_cast<const DecodeItem *>(c->d_meta + tbytes);
   a.wg_piece_off = reinterpret_cast<const int32_t *>(c->d_meta + tbytes + ibytes);
   a.part_o = c->d_part;

@@ -5,6 +5,8 @@
 //   SeqDesc  [n_seqs]
 //   SegDesc  [n_seqs * num_kv_heads]
 //   int32    page ids of every listed segment (SegDesc::page_off indexes here)
+//   float    relocation tables, 2 * head_dim floats per distinct nonzero
+//            offset of the listed segments (SegDesc::rope_off indexes here)
 //   work items of the call (ScatterItem, PrefillItem or DecodeItem)
 //   combine items (CombineItem), when the call has split work
 #pragma once
@@ -36,6 +38,22 @@ struct SegDesc {
   int32_t page_off;     // index of page 0 in the page id table
   int32_t n_pages;
   int32_t window;       // 0 = global, W >= 1 = local
+  int32_t rope_off;     // -1: queries used as given; else the segment's relocation table
+                        // (cos[head_dim], then signed sin[head_dim]) starts at float rope_off
+  int32_t pad0, pad1, pad2;
+};
+
+// Query relocation: channel c of a relocated query becomes
+// cos[c] * q[c] + ssin[c] * q[partner(c)], where channels below `lo` have
+// cos 1 and ssin 0 and, above it, partner(c) = c +- half (style 0) or c ^ 1
+// (style 1).  lo and half are multiples of 8, so a 16-byte chunk of
+// channels has its partners in one chunk.
+struct RopeArgs {
+  const float *tables;
+  int32_t lo;     // first rotary channel
+  int32_t half;   // rotary channels / 2
+  int32_t style;  // 0 rotate-half, 1 interleaved
+  int32_t pad;
 };
 
 // One page touched by an append: K rows [slot_begin, slot_end) come from
@@ -120,6 +138,7 @@ struct PrefillArgs {
   int32_t rows_per_tile;  // query positions per workgroup = kPrefillRows / group
   float scale_log2;       // softmax scale * log2(e)
   float scale;
+  RopeArgs rope;
 };
 
 struct DecodeArgs {
@@ -140,6 +159,7 @@ struct DecodeArgs {
   int32_t group;
   float scale_log2;
   float scale;
+  RopeArgs rope;
 };
 
 // Partial slot layout for combine: slot s holds `slot_rows` rows of

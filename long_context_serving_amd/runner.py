@@ -53,13 +53,18 @@ class WorkloadRun:
     """A libsegkv context holding one workload's sequences in layer 0."""
 
     def __init__(self, w: Workload, dev: DeviceInputs, page_order_seed: Optional[int] = None,
-                 windows=None, num_pages: Optional[int] = None):
+                 windows=None, num_pages: Optional[int] = None, deltas=None, rope_theta: float = 0.0,
+                 rope_style: int = 0, rope_dims: int = 0):
+        """``deltas[b][g]``: query relocation offset of sequence b, KV head g
+        (None = no relocation)."""
         self.w = w
         self.dev = dev
         self.windows = tuple(w.windows if windows is None else windows)
+        self.deltas = None if deltas is None else np.asarray(deltas, dtype=np.int64).reshape(w.n_seqs, w.num_kv_heads)
         self.ctx = S.SegKV(1, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size, max(w.n_seqs, 1),
                            num_pages or pages_for(w), self.windows, softmax_scale=w.scale,
-                           page_order_seed=w.page_order_seed if page_order_seed is None else page_order_seed)
+                           page_order_seed=w.page_order_seed if page_order_seed is None else page_order_seed,
+                           rope_theta=rope_theta, rope_style=rope_style, rope_dims=rope_dims)
         self.seq_ids = list(range(w.n_seqs))
 
     def append_fill(self):
@@ -73,6 +78,9 @@ class WorkloadRun:
     def load(self):
         self.append_fill()
         self.append_queries()
+        if self.deltas is not None:
+            for b, s in enumerate(self.seq_ids):
+                self.ctx.set_relocation(s, self.deltas[b])
         return self
 
     def reset(self):

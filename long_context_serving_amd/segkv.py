@@ -36,8 +36,11 @@ TUNE_PREFILL_ORDER = 2
 EXPORTED = (
     "segkv_create", "segkv_destroy", "segkv_append_pages", "segkv_prefill", "segkv_decode",
     "segkv_release", "segkv_page_table", "segkv_free_pages", "segkv_set_timing",
-    "segkv_read_timing", "segkv_set_tuning", "segkv_last_error",
+    "segkv_read_timing", "segkv_set_tuning", "segkv_last_error", "segkv_set_relocation",
 )
+
+ROPE_ROTATE_HALF = 0
+ROPE_INTERLEAVED = 1
 
 
 class SegKVError(RuntimeError):
@@ -61,6 +64,9 @@ class _Config(ctypes.Structure):
         ("k_pool", ctypes.c_void_p),
         ("v_pool", ctypes.c_void_p),
         ("stream", ctypes.c_void_p),
+        ("rope_theta", ctypes.c_float),
+        ("rope_style", ctypes.c_int32),
+        ("rope_dims", ctypes.c_int32),
     ]
 
 
@@ -102,6 +108,8 @@ def load_library(path: Optional[str] = None):
     lib.segkv_read_timing.restype = ctypes.c_int
     lib.segkv_set_tuning.argtypes = [vp, i32, i64]
     lib.segkv_set_tuning.restype = ctypes.c_int
+    lib.segkv_set_relocation.argtypes = [vp, i32, pi32]
+    lib.segkv_set_relocation.restype = ctypes.c_int
     lib.segkv_last_error.argtypes = [vp]
     lib.segkv_last_error.restype = ctypes.c_char_p
     if path is None:
@@ -151,7 +159,8 @@ class SegKV:
     def __init__(self, num_layers: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                  page_size: int, max_seqs: int, num_pages: int, head_window: Sequence[int],
                  softmax_scale: float = 0.0, page_order_seed: int = 0, planning: bool = False,
-                 k_pool=None, v_pool=None, stream=None):
+                 k_pool=None, v_pool=None, stream=None, rope_theta: float = 0.0, rope_style: int = 0,
+                 rope_dims: int = 0):
         self._lib = load_library()
         self.num_layers, self.num_q_heads, self.num_kv_heads = num_layers, num_q_heads, num_kv_heads
         self.head_dim, self.page_size, self.max_seqs, self.num_pages = head_dim, page_size, max_seqs, num_pages
@@ -164,6 +173,7 @@ class SegKV:
         cfg.head_window = win_p
         cfg.softmax_scale = softmax_scale
         cfg.page_order_seed = page_order_seed
+        cfg.rope_theta, cfg.rope_style, cfg.rope_dims = rope_theta, rope_style, rope_dims
         if not planning:
             import torch
             if k_pool is None:
@@ -278,6 +288,19 @@ class SegKV:
 
     def release(self, seq_id: int):
         return self._check(self._lib.segkv_release(self._h, seq_id))
+
+    def set_relocation(self, seq_id: int, deltas=None):
+        """Query-side RoPE relocation offsets of one sequence: int32
+        [num_layers][num_kv_heads] (None = all zero)."""
+        if deltas is None:
+            return self._check(self._lib.segkv_set_relocation(self._h, seq_id, None))
+        d = np.asarray(deltas, dtype=np.int64).reshape(-1)
+        if d.size != self.num_layers * self.num_kv_heads:
+            raise ValueError(f"deltas must hold num_layers * num_kv_heads = {self.num_layers * self.num_kv_heads}")
+        if np.any(np.abs(d) >= 2 ** 31):
+            raise ValueError("deltas must fit int32")
+        arr, p = _i32(d)
+        return self._check(self._lib.segkv_set_relocation(self._h, seq_id, p))
 
     def page_table(self, layer: int, seq_id: int, kv_head: int):
         """(first_token, kv_len, page ids as int32 numpy array)."""

@@ -11,6 +11,7 @@ from long_context_serving_amd import runner as R
 from long_context_serving_amd import segkv as S
 from long_context_serving_amd import workloads as wl
 from oracle import attention as A
+from oracle import rope as RP
 
 O_TOL = 2e-2    # max-abs on bf16 outputs against the unrounded fp64 oracle
 LSE_TOL = 1e-3  # max-abs on fp32 log-sum-exp
@@ -20,12 +21,17 @@ def say(*msg):
     print("[gpu]", *msg, file=sys.stderr, flush=True)
 
 
-def gpu_run(w, x, mode="prefill", seed=None, windows=None, split_tiles=None, pps=None, repeat=1):
+def gpu_run(w, x, mode="prefill", seed=None, windows=None, split_tiles=None, pps=None, repeat=1, rope=None):
+    """``rope``: dict(deltas=[n_seqs][Hkv], theta=, style=, dims=) for query
+    relocation, or None."""
     import torch
     say(f"{mode} {w.name} kv={w.kv_lens[:4]} q={w.q_lens[:4]} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
-        f"D={w.head_dim} P={w.page_size} W={windows or w.windows} seed={seed} split={split_tiles} pps={pps}")
+        f"D={w.head_dim} P={w.page_size} W={windows or w.windows} seed={seed} split={split_tiles} pps={pps}"
+        + ("" if rope is None else f" rope={rope}"))
     dev = R.to_device(w, x)
-    run = R.WorkloadRun(w, dev, page_order_seed=seed, windows=windows)
+    rkw = {} if rope is None else dict(deltas=rope["deltas"], rope_theta=rope.get("theta", 0.0),
+                                       rope_style=rope.get("style", 0), rope_dims=rope.get("dims", 0))
+    run = R.WorkloadRun(w, dev, page_order_seed=seed, windows=windows, **rkw)
     try:
         if split_tiles is not None:
             run.ctx.set_tuning(S.TUNE_PREFILL_SPLIT_TILES, split_tiles)
@@ -42,9 +48,14 @@ def gpu_run(w, x, mode="prefill", seed=None, windows=None, split_tiles=None, pps
         run.close()
 
 
-def compare(w, x, o_bits, lse, rows_per_seq=None, windows=None, o_tol=O_TOL, lse_tol=LSE_TOL):
+def compare(w, x, o_bits, lse, rows_per_seq=None, windows=None, o_tol=O_TOL, lse_tol=LSE_TOL, rope=None):
     """Oracle rows vs GPU rows; returns (max |do|, max |dlse|)."""
-    ref = A.attend_batch(x.q, x.k, x.v, x.cu_q, x.cu_kv, windows or w.windows, w.scale, rows_per_seq)
+    if rope is None:
+        ref = A.attend_batch(x.q, x.k, x.v, x.cu_q, x.cu_kv, windows or w.windows, w.scale, rows_per_seq)
+    else:
+        ref = RP.attend_batch_relocated(x.q, x.k, x.v, x.cu_q, x.cu_kv, windows or w.windows, w.scale,
+                                        rope["deltas"], rope.get("theta") or 10000.0, rope.get("style", 0),
+                                        rope.get("dims", 0), rows_per_seq)
     worst_o = worst_l = 0.0
     for b, (ro, rl) in enumerate(ref):
         rows = np.arange(w.q_lens[b]) if rows_per_seq is None else np.asarray(rows_per_seq[b])

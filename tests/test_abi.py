@@ -57,6 +57,12 @@ def _cfg(**kw):
     (dict(head_window=[0, -1]), "head_window"),
     (dict(num_layers=0), "num_layers"),
     (dict(softmax_scale=-1.0), "softmax_scale"),
+    (dict(rope_theta=-1.0), "rope_theta"),
+    (dict(rope_theta=1.0), "rope_theta"),
+    (dict(rope_style=2), "rope_style"),
+    (dict(rope_dims=8), "rope_dims"),
+    (dict(rope_dims=136), "rope_dims"),
+    (dict(head_dim=64, rope_dims=80), "rope_dims"),
 ])
 def test_create_rejects_bad_config(lib, kw, msg):
     with pytest.raises(S.SegKVError) as e:
@@ -103,3 +109,18 @@ def test_tuning_knobs(lib):
     kv.set_tuning(S.TUNE_PREFILL_SPLIT_TILES, 0)
     with pytest.raises(S.SegKVError):
         kv.set_tuning(7, 1)
+
+
+def test_relocation_offsets_on_a_planning_context(lib):
+    kv = S.SegKV(planning=True, **_cfg(num_layers=2, rope_style=1, rope_dims=64))
+    kv.set_relocation(1, [[5, 0], [0, -9]])
+    kv.set_relocation(1, None)
+    kv.set_relocation(3, np.zeros((2, 2)))
+    with pytest.raises(S.SegKVError) as e:
+        kv.set_relocation(4, None)
+    assert e.value.code == S.SEGKV_E_RANGE
+    with pytest.raises(ValueError):
+        kv.set_relocation(0, [1, 2, 3])
+    with pytest.raises(ValueError):
+        kv.set_relocation(0, [[2 ** 31, 0], [0, 0]])
+    assert kv.release(1) == S.SEGKV_OK
