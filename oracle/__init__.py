@@ -12,4 +12,5 @@ Modules:
   segments   which tokens a head's segment must store
   ledger     closed-form visible-pair, FLOP and byte counts
   rope       query-side rotary relocation by a per-head position offset
+  merge      head-decomposition merge: per-(row, head) select or log-sum-exp merge
 """
