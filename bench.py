@@ -26,6 +26,10 @@ In the same JSON line:
                 p50 / p95 of the prefill kernel time;
   decode        visible-KV GB/s of split-KV decode + combine at 32K x 31
                 sequences against 8 TB/s, and its all-global arm;
+  merge         the head-decomposition merge of a reused 128K-token document
+                (offline Local-head partials, online Global heads and
+                protected rows, LSE merge on the window's boundary rows):
+                algorithmic GB/s against 8 TB/s;
   workloads     the varlen Llama-3.3-70B-shaped and the 128K chunked prefill;
   cpu_baseline  the fp64 oracle on a bounded sample of the headline workload.
 
@@ -179,6 +183,40 @@ def decode_arm(w, dev, steps, warmup, windows=None, deltas=None):
 
 # ----------------------------------------------------------- cpu baseline
 
+def merge_arm(mw, steps, warmup):
+    import torch
+    from long_context_serving_amd import metrics as M
+    from long_context_serving_amd import segkv as S
+    from long_context_serving_amd import workloads as wl
+    mi = wl.make_merge_inputs(mw)
+    by = M.merge_bytes(mi.mode, mw.head_dim)
+    ctx = S.SegKV(1, mw.num_q_heads, mw.num_kv_heads, mw.head_dim, 64, 1, 4, [0] * mw.num_kv_heads)
+    args = (S.bf16_tensor(mi.o_a), torch.from_numpy(mi.lse_a).cuda(), S.bf16_tensor(mi.o_b),
+            torch.from_numpy(mi.lse_b).cuda(), torch.from_numpy(mi.mode).cuda())
+    del mi
+    o = torch.empty_like(args[0])
+    lse = torch.empty_like(args[1])
+    for _ in range(warmup):
+        ctx.merge(*args, o=o, lse=lse)
+    sync()
+    ctx.set_timing(True, [S.KERNEL_MERGE])
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        ctx.merge(*args, o=o, lse=lse)
+    sync()
+    dt = (time.perf_counter() - t0) / steps
+    k_ms, k_n = kernel_avg(ctx, S.KERNEL_MERGE)
+    ctx.set_timing(False)
+    ctx.close()
+    gbs = by["total"] / (k_ms * 1e-3) / 1e9
+    return {"workload": mw.name, "rows": mw.rows, "num_q_heads": mw.num_q_heads, "head_dim": mw.head_dim,
+            "value": gbs, "unit": "GB/s", "bytes": by, "ms_per_call": dt * 1e3, "kernel_ms": k_ms,
+            "launches": k_n,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS, "traffic": measured_traffic("merge_" + mw.name),
+                         "kernel": "merge_kernel<128>", "avg_launch_ms": k_ms}}
+
+
 def local_head_deltas(w, offset):
     """Every local KV head of every sequence relocated by ``offset``; global
     heads (recomputed online at their true positions) by 0."""
@@ -233,7 +271,7 @@ def main():
     # with its own W untimed steps.
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all",
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "merge"], default="all",
                     help="profiling runs: only the segmented headline prefill, or only segmented decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the varlen and 128K prefill workloads")
@@ -369,6 +407,11 @@ def main():
         out["decode"] = dec
         del dev4
 
+    if args.only in ("all", "merge"):
+        log(f"merge {wl.MERGE_128K.name}")
+        out["merge"] = merge_arm(wl.MERGE_128K, K, Wm)
+        log(f"  {out['merge']['value']:.1f} GB/s, kernel {out['merge']['kernel_ms']:.4f} ms")
+
     if args.only == "all" and not args.no_secondary:
         sec = {}
         for w, split in ((wl.LLAMA70B_VARLEN_PREFILL, None), (wl.CHUNKED_PREFILL_128K, None)):
@@ -394,6 +437,12 @@ def main():
     elif "value" in out:
         out["cpu_baseline"] = None
 
+    if "value" not in out and args.only == "merge":  # profiling runs still print one line
+        m = out["merge"]
+        out = {"metric": METRIC, "value": m["value"], "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": Wm,
+               "ms_per_step": m["ms_per_call"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+               "dtype": "bf16", "data": "synthetic", "config": {"workload": m["workload"]},
+               "roofline": m["roofline"], "cpu_baseline": None, "merge": m}
     if "value" not in out:  # decode-only runs still print one line
         dec = out.get("decode", {})
         out = {"metric": METRIC, "value": dec.get("value"), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": Wm,

@@ -60,7 +60,8 @@ enum segkv_kernel {
   SEGKV_KERNEL_PREFILL = 1,       /* varlen prefill attention                */
   SEGKV_KERNEL_DECODE_SPLIT = 2,  /* split-KV decode, partial (o, lse)      */
   SEGKV_KERNEL_COMBINE = 3,       /* log-sum-exp combine of split partials   */
-  SEGKV_KERNEL_COUNT = 4
+  SEGKV_KERNEL_MERGE = 4,         /* head-decomposition merge (segkv_merge)  */
+  SEGKV_KERNEL_COUNT = 5
 };
 
 typedef struct segkv_ctx segkv_ctx;
@@ -167,6 +168,41 @@ int segkv_decode(segkv_ctx *ctx, int32_t layer, int32_t n_seqs, const int32_t *s
  * a planning-only context (host state only).
  */
 int segkv_set_relocation(segkv_ctx *ctx, int32_t seq_id, const int32_t *deltas);
+
+/*
+ * Head-decomposition merge ("RedKnot: Head-Aware KV Reuse and
+ * SegPagedAttention" page, "The Three Core Mechanisms in Detail", first
+ * mechanism; "RedKnot-MLA: Multi-Head Offline-Online Reuse for DeepSeek-V4
+ * Long-Context Serving" review, "Key claims under review" and
+ * "Strengths").  Local-head results prepared offline (partial A) are
+ * combined with results computed online (partial B): Global heads,
+ * protected rows, and the keys a reused document's rows see outside the
+ * document.  Each (row, query head) pair takes, by its mode byte:
+ *   SEGKV_MERGE_TAKE_A  o = o_a, lse = lse_a (bit for bit)
+ *   SEGKV_MERGE_TAKE_B  o = o_b, lse = lse_b (bit for bit)
+ *   SEGKV_MERGE_LSE     the softmax over the union of the two parts' key
+ *                       sets (they must be disjoint): lse = ln(e^lse_a +
+ *                       e^lse_b), o = e^(lse_a - lse) o_a + e^(lse_b - lse)
+ *                       o_b, evaluated in fp32 and rounded once to bf16.  A
+ *                       part with lse = -inf weighs 0; if both are -inf then
+ *                       o = 0, lse = -inf.  Any mode value >= 2 merges.
+ * Only the parts a pair's mode needs are read.
+ *   o_a, o_b      device bf16 [n_rows][num_q_heads][head_dim], 16-byte aligned
+ *   lse_a, lse_b  device fp32 [n_rows][num_q_heads] (natural log)
+ *   mode          device uint8 [n_rows][num_q_heads]
+ *   o             device bf16 [n_rows][num_q_heads][head_dim], 16-byte aligned;
+ *                 may be o_a or o_b (in place)
+ *   lse           device fp32 [n_rows][num_q_heads] or NULL; may be lse_a or lse_b
+ * Other overlaps between inputs and outputs are not allowed.  Device
+ * contexts only (SEGKV_E_STATE in a planning context).
+ */
+enum segkv_merge_mode {
+  SEGKV_MERGE_TAKE_A = 0,
+  SEGKV_MERGE_TAKE_B = 1,
+  SEGKV_MERGE_LSE = 2
+};
+int segkv_merge(segkv_ctx *ctx, int64_t n_rows, const void *o_a, const float *lse_a, const void *o_b,
+                const float *lse_b, const uint8_t *mode, void *o, float *lse);
 
 /* Return every page of a sequence (all layers, all heads) to the pool,
  * reset its length to 0 and clear its relocation offsets. */

@@ -1030,6 +1030,40 @@ int segkv_decode(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq
   return timed_end(c, &t2);
 }
 
+int segkv_merge(segkv_ctx *c, int64_t n_rows, const void *o_a, const float *lse_a, const void *o_b,
+                const float *lse_b, const uint8_t *mode, void *o, float *lse) {
+  if (!c) return SEGKV_E_INVAL;
+  if (c->planning) return c->fail(SEGKV_E_STATE, "merge needs a device context (planning-only context)");
+  if (n_rows < 0) return c->fail(SEGKV_E_INVAL, "n_rows < 0");
+  if (n_rows == 0) return SEGKV_OK;
+  if (n_rows > std::numeric_limits<int64_t>::max() / (static_cast<int64_t>(c->Hq) * c->D * 2))
+    return c->fail(SEGKV_E_INVAL, "n_rows too large");
+  if (!o_a || !lse_a || !o_b || !lse_b || !mode || !o)
+    return c->fail(SEGKV_E_INVAL, "o_a, lse_a, o_b, lse_b, mode and o must be set");
+  auto misaligned = [](const void *p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a != 0; };
+  if (misaligned(o_a, 16) || misaligned(o_b, 16) || misaligned(o, 16))
+    return c->fail(SEGKV_E_INVAL, "o_a, o_b and o must be 16-byte aligned");
+  if (misaligned(lse_a, 4) || misaligned(lse_b, 4) || (lse && misaligned(lse, 4)))
+    return c->fail(SEGKV_E_INVAL, "lse arrays must be 4-byte aligned");
+  MergeArgs a;
+  a.o_a = static_cast<const uint16_t *>(o_a);
+  a.lse_a = lse_a;
+  a.o_b = static_cast<const uint16_t *>(o_b);
+  a.lse_b = lse_b;
+  a.mode = mode;
+  a.o = static_cast<uint16_t *>(o);
+  a.lse = lse;
+  a.n_pairs = n_rows * c->Hq;
+  const int64_t per_wg = static_cast<int64_t>(kMergeThreads / (c->D / 8)) * kMergeUnroll;
+  const int64_t n_wgs = std::min<int64_t>(ceil_div(a.n_pairs, per_wg), static_cast<int64_t>(c->num_cus) * 8);
+  TimedLaunch t{};
+  int rc = timed_begin(c, &t, SEGKV_KERNEL_MERGE);
+  if (rc) return rc;
+  hipError_t e = launch_merge(a, static_cast<int>(n_wgs), c->D, c->stream);
+  if (e != hipSuccess) return c->device_fail(e, "merge launch");
+  return timed_end(c, &t);
+}
+
 int segkv_set_timing(segkv_ctx *c, int32_t kernel_mask) {
   if (!c) return SEGKV_E_INVAL;
   if (c->planning) return c->fail(SEGKV_E_STATE, "timing needs a device context");

@@ -22,6 +22,8 @@ constexpr int kPrefillThreads = 512;  // 8 waves, 32 rows each, two per SIMD
 constexpr int kDecodeThreads = 512;  // 8 waves, two per SIMD
 constexpr int kDecodeCols = 16;    // query heads handled by one decode work item (GQA group, padded)
 constexpr int kScatterThreads = 256;
+constexpr int kMergeThreads = 256;
+constexpr int kMergeUnroll = 4;    // (row, head) pairs in flight per lane of the merge kernel
 constexpr int kPrefillWgPerCu = 1;  // resident prefill workgroups per CU (96 KiB of LDS each)
 constexpr int kDecodeWgPerCu = 1;   // resident decode workgroups per CU (the stream-K grid size)
 constexpr int kXcds = 8;           // MI355X: workgroup i of a launch runs on XCD i % 8
@@ -175,11 +177,23 @@ struct CombineArgs {
   int32_t slot_rows;
 };
 
+struct MergeArgs {
+  const uint16_t *o_a;
+  const float *lse_a;
+  const uint16_t *o_b;
+  const float *lse_b;
+  const uint8_t *mode;
+  uint16_t *o;
+  float *lse;  // or null
+  int64_t n_pairs;  // rows * query heads
+};
+
 // Launchers (kernels.hip).  Return the launch status.
 hipError_t launch_scatter(const ScatterArgs &a, int n_items, int head_dim, int page_size, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs &a, int n_items, int head_dim, int page_size, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int n_wgs, int head_dim, int page_size, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, int n_items, int max_entries, int head_dim, hipStream_t s);
+hipError_t launch_merge(const MergeArgs &a, int n_wgs, int head_dim, hipStream_t s);
 // bytes are rounded up to 16; both buffers must hold the rounded size
 hipError_t launch_upload(void *dst, const void *src_pinned, size_t bytes, hipStream_t s);
 

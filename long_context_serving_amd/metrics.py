@@ -47,3 +47,18 @@ def decode_bytes(w: Workload, windows=None, elem_bytes: int = 2) -> dict:
             kv += 2 * int(visible_keys(np.array([n - 1]), int(win))[0]) * w.head_dim * elem_bytes
     q_o = 2 * w.n_seqs * w.num_q_heads * w.head_dim * elem_bytes
     return {"kv": kv, "q_o": q_o, "total": kv + q_o}
+
+
+def merge_bytes(mode: np.ndarray, head_dim: int, elem_bytes: int = 2) -> dict:
+    """Algorithmic HBM bytes of the head-decomposition merge: each (row,
+    head) reads its mode byte and the partials its mode needs (o row and
+    lse of A, of B, or of both) and writes one o row and one lse."""
+    mode = np.asarray(mode)
+    part = head_dim * elem_bytes + 4
+    n_a = int(np.count_nonzero(mode == 0))
+    n_b = int(np.count_nonzero(mode == 1))
+    n_m = int(mode.size - n_a - n_b)
+    read = mode.size + (n_a + n_b) * part + 2 * n_m * part
+    write = mode.size * part
+    return {"pairs": int(mode.size), "take_a": n_a, "take_b": n_b, "merge": n_m,
+            "read": read, "write": write, "total": read + write}

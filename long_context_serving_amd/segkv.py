@@ -27,6 +27,7 @@ KERNEL_SCATTER = 0
 KERNEL_PREFILL = 1
 KERNEL_DECODE_SPLIT = 2
 KERNEL_COMBINE = 3
+KERNEL_MERGE = 4
 
 TUNE_DECODE_MIN_PAGES = 0
 TUNE_PREFILL_SPLIT_TILES = 1
@@ -36,8 +37,12 @@ TUNE_PREFILL_ORDER = 2
 EXPORTED = (
     "segkv_create", "segkv_destroy", "segkv_append_pages", "segkv_prefill", "segkv_decode",
     "segkv_release", "segkv_page_table", "segkv_free_pages", "segkv_set_timing",
-    "segkv_read_timing", "segkv_set_tuning", "segkv_last_error", "segkv_set_relocation",
+    "segkv_read_timing", "segkv_set_tuning", "segkv_last_error", "segkv_set_relocation", "segkv_merge",
 )
+
+MERGE_TAKE_A = 0
+MERGE_TAKE_B = 1
+MERGE_LSE = 2
 
 ROPE_ROTATE_HALF = 0
 ROPE_INTERLEAVED = 1
@@ -108,6 +113,8 @@ def load_library(path: Optional[str] = None):
     lib.segkv_read_timing.restype = ctypes.c_int
     lib.segkv_set_tuning.argtypes = [vp, i32, i64]
     lib.segkv_set_tuning.restype = ctypes.c_int
+    lib.segkv_merge.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp]
+    lib.segkv_merge.restype = ctypes.c_int
     lib.segkv_set_relocation.argtypes = [vp, i32, pi32]
     lib.segkv_set_relocation.restype = ctypes.c_int
     lib.segkv_last_error.argtypes = [vp]
@@ -165,6 +172,8 @@ class SegKV:
         self.num_layers, self.num_q_heads, self.num_kv_heads = num_layers, num_q_heads, num_kv_heads
         self.head_dim, self.page_size, self.max_seqs, self.num_pages = head_dim, page_size, max_seqs, num_pages
         self._win, win_p = _i32(np.asarray(head_window, dtype=np.int32).reshape(-1))
+        if num_layers > 0 and num_kv_heads > 0 and self._win.size != num_layers * num_kv_heads:
+            raise ValueError(f"head_window must hold num_layers * num_kv_heads = {num_layers * num_kv_heads} entries")
         self.k_pool = self.v_pool = None
         self.stream = None
         cfg = _Config()
@@ -284,6 +293,36 @@ class SegKV:
             _check_dev(lse, "lse", torch.float32)
         self._check(self._lib.segkv_decode(self._h, layer, len(ids), ids_p, q.data_ptr(), o.data_ptr(),
                                            lse.data_ptr() if lse is not None else None))
+        return o, lse
+
+    def merge(self, o_a, lse_a, o_b, lse_b, mode, o=None, lse=None, want_lse: bool = True):
+        """Head-decomposition merge: per (row, head) take A, take B or
+        log-sum-exp merge (mode uint8 [rows][Hq] of MERGE_*).  o_*: bf16
+        [rows][Hq][D], lse_*: fp32 [rows][Hq].  Returns (o, lse)."""
+        import torch
+        _check_dev(o_a, "o_a", torch.bfloat16)
+        rows = o_a.shape[0] if o_a.dim() == 3 else -1
+        want = (rows, self.num_q_heads, self.head_dim)
+        for t, name, dt, shape in ((o_a, "o_a", torch.bfloat16, want), (o_b, "o_b", torch.bfloat16, want),
+                                   (lse_a, "lse_a", torch.float32, want[:2]), (lse_b, "lse_b", torch.float32, want[:2]),
+                                   (mode, "mode", torch.uint8, want[:2])):
+            _check_dev(t, name, dt)
+            if tuple(t.shape) != shape:
+                raise ValueError(f"{name} must be {list(shape)}")
+        if o is None:
+            o = torch.empty_like(o_a)
+        _check_dev(o, "o", torch.bfloat16)
+        if tuple(o.shape) != want:
+            raise ValueError(f"o must be {list(want)}")
+        if lse is None and want_lse:
+            lse = torch.empty(want[:2], dtype=torch.float32, device=o_a.device)
+        if lse is not None:
+            _check_dev(lse, "lse", torch.float32)
+            if tuple(lse.shape) != want[:2]:
+                raise ValueError(f"lse must be {list(want[:2])}")
+        self._check(self._lib.segkv_merge(self._h, rows, o_a.data_ptr(), lse_a.data_ptr(), o_b.data_ptr(),
+                                          lse_b.data_ptr(), mode.data_ptr(), o.data_ptr(),
+                                          lse.data_ptr() if lse is not None else None))
         return o, lse
 
     def release(self, seq_id: int):

@@ -180,3 +180,94 @@ def small_workload(name: str, kv_lens, q_lens, hq: int, hkv: int, d: int, p: int
     """A free-form workload for parity sweeps (same recipe, any shape)."""
     return Workload(name, tuple(int(x) for x in kv_lens), tuple(int(x) for x in q_lens),
                     hq, hkv, d, p, tuple(int(x) for x in windows), seed)
+
+
+# ------------------------------------------------------------ head merge
+
+TAKE_A, TAKE_B, MERGE = 0, 1, 2  # mode bytes of the head-decomposition merge
+
+
+@dataclass(frozen=True)
+class MergeWorkload:
+    """Inputs of the head-decomposition merge for one reused document.
+
+    ``rows`` document rows x ``num_q_heads`` heads.  Query heads of the
+    KV groups in ``global_kv_heads`` are recomputed online (take B).
+    Local heads take the offline partial A except on:
+
+    * protected rows, recomputed online (take B): every row at a
+      ``boundary_every``-token boundary, the last ``tail`` rows, the last
+      ``query_rows`` rows (query and new tokens) and a seeded
+      ``dirty_frac`` fraction (dirty rows and the indexer's top rows).
+      This is the protected-row set RedKnot-MLA lists ("RedKnot-MLA:
+      Multi-Head Offline-Online Reuse for DeepSeek-V4 Long-Context Serving"
+      review, "Strengths");
+    * the first ``window - 1`` rows, which in the live request also see
+      keys before the document.  Their offline partial is merged (MERGE)
+      with an online partial over those keys.
+
+    Partials: o ~ N(0, 0.5^2) rounded to bf16; lse ~ N(ln(keys), 2^2), with
+    a seeded ``empty_frac`` of each side set to -inf (a part without keys).
+    """
+
+    name: str
+    rows: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    window: int
+    tail: int
+    query_rows: int
+    boundary_every: int
+    dirty_frac: float
+    seed: int
+    global_kv_heads: Tuple[int, ...] = (0,)
+    empty_frac: float = 0.0
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+
+@dataclass
+class MergeInputs:
+    o_a: np.ndarray    # uint16 bf16 bits [rows][Hq][D]
+    lse_a: np.ndarray  # float32 [rows][Hq]
+    o_b: np.ndarray
+    lse_b: np.ndarray
+    mode: np.ndarray   # uint8 [rows][Hq]
+
+
+def merge_modes(mw: MergeWorkload) -> np.ndarray:
+    """Mode byte of every (row, head) following the class docstring."""
+    rng = np.random.default_rng(mw.seed + 1)
+    protected = np.zeros(mw.rows, bool)
+    protected[:: mw.boundary_every] = True
+    protected[max(0, mw.rows - mw.tail):] = True
+    protected[max(0, mw.rows - mw.query_rows):] = True
+    protected |= rng.random(mw.rows) < mw.dirty_frac
+    local = np.array([(h // mw.group) not in mw.global_kv_heads for h in range(mw.num_q_heads)])
+    mode = np.full((mw.rows, mw.num_q_heads), TAKE_A, np.uint8)
+    mode[: max(0, mw.window - 1), :] = MERGE
+    mode[protected, :] = TAKE_B
+    mode[:, ~local] = TAKE_B
+    return mode
+
+
+def make_merge_inputs(mw: MergeWorkload) -> MergeInputs:
+    rng = np.random.default_rng(mw.seed)
+    shape = (mw.rows, mw.num_q_heads)
+    keys = np.log(np.minimum(np.arange(1, mw.rows + 1), mw.window or mw.rows))[:, None]
+    o_a = to_bf16_bits(rng.standard_normal(shape + (mw.head_dim,), dtype=np.float32) * np.float32(0.5))
+    o_b = to_bf16_bits(rng.standard_normal(shape + (mw.head_dim,), dtype=np.float32) * np.float32(0.5))
+    lse_a = (keys + 2.0 * rng.standard_normal(shape)).astype(np.float32)
+    lse_b = (keys + 2.0 * rng.standard_normal(shape)).astype(np.float32)
+    if mw.empty_frac > 0:
+        lse_a[rng.random(shape) < mw.empty_frac] = -np.inf
+        lse_b[rng.random(shape) < mw.empty_frac] = -np.inf
+    return MergeInputs(o_a, lse_a, o_b, lse_b, merge_modes(mw))
+
+
+MERGE_128K = MergeWorkload(
+    "merge_128k_doc", rows=131072, num_q_heads=32, num_kv_heads=8, head_dim=128, window=4096,
+    tail=32768, query_rows=512, boundary_every=128, dirty_frac=0.02, seed=6)

@@ -42,8 +42,11 @@ def test_library_exports_every_declared_symbol(lib):
 
 def _cfg(**kw):
     base = dict(num_layers=1, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=64, max_seqs=4,
-                num_pages=100, head_window=[0, 64])
+                num_pages=100)
     base.update(kw)
+    if "head_window" not in base:  # one global head, the rest local, in every layer
+        n = max(base["num_layers"], 1) * max(base["num_kv_heads"], 1)
+        base["head_window"] = [0 if i % base["num_kv_heads"] == 0 else 64 for i in range(n)]
     return base
 
 
@@ -97,6 +100,11 @@ def test_planning_context_refuses_device_calls(lib):
     assert kv.page_table(0, 0, 0)[1] == 0
 
 
+def test_binding_checks_the_window_table_size(lib):
+    with pytest.raises(ValueError):
+        S.SegKV(planning=True, **_cfg(num_layers=2, head_window=[0, 64]))
+
+
 def test_null_context_is_rejected(lib):
     assert lib.segkv_release(None, 0) == S.SEGKV_E_INVAL
     assert lib.segkv_free_pages(None) == S.SEGKV_E_INVAL
@@ -112,7 +120,7 @@ def test_tuning_knobs(lib):
 
 
 def test_relocation_offsets_on_a_planning_context(lib):
-    kv = S.SegKV(planning=True, **_cfg(num_layers=2, rope_style=1, rope_dims=64))
+    kv = S.SegKV(planning=True, **_cfg(num_layers=2, head_window=[0, 64, 0, 64], rope_style=1, rope_dims=64))
     kv.set_relocation(1, [[5, 0], [0, -9]])
     kv.set_relocation(1, None)
     kv.set_relocation(3, np.zeros((2, 2)))
@@ -124,3 +132,9 @@ def test_relocation_offsets_on_a_planning_context(lib):
     with pytest.raises(ValueError):
         kv.set_relocation(0, [[2 ** 31, 0], [0, 0]])
     assert kv.release(1) == S.SEGKV_OK
+
+
+def test_merge_refused_in_planning_context(lib):
+    kv = S.SegKV(planning=True, **_cfg())
+    assert lib.segkv_merge(kv._h, 4, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, None) == S.SEGKV_E_STATE
+    assert lib.segkv_merge(None, 4, None, None, None, None, None, None, None) == S.SEGKV_E_INVAL

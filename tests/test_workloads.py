@@ -2,6 +2,7 @@
 
 import numpy as np
 
+from long_context_serving_amd import metrics as M
 from long_context_serving_amd import workloads as wl
 
 
@@ -56,3 +57,33 @@ def test_product_ledger_matches_oracle_closed_forms():
     rows = np.arange(0, 8192, 97)
     assert M.prefill_flops_rows(w, 0, rows) == 4 * 128 * 4 * sum(
         min(p + 1, x) if x else p + 1 for p in rows for x in w.windows)
+
+
+def test_merge_modes_follow_the_recipe():
+    mw = wl.MergeWorkload("m", 2000, 16, 4, 64, window=300, tail=256, query_rows=40, boundary_every=128,
+                          dirty_frac=0.03, seed=3)
+    mode = wl.merge_modes(mw)
+    assert mode.shape == (2000, 16) and mode.dtype == np.uint8
+    assert np.all(mode[:, :4] == wl.TAKE_B)            # KV head 0's query heads are global
+    local = mode[:, 4:]
+    assert np.all(local[::128] == wl.TAKE_B)
+    assert np.all(local[-256:] == wl.TAKE_B)
+    unprotected = np.all(local != wl.TAKE_B, axis=1)
+    assert np.all(local[:299][unprotected[:299]] == wl.MERGE)
+    assert np.all(local[299:][unprotected[299:]] == wl.TAKE_A)
+    dirty = np.flatnonzero(~unprotected[:-256])
+    dirty = dirty[dirty % 128 != 0]
+    assert 0.01 < len(dirty) / 2000 < 0.05
+
+
+def test_merge_bytes_against_per_pair_count():
+    rng = np.random.default_rng(0)
+    mode = rng.integers(0, 3, size=(50, 6)).astype(np.uint8)
+    d = 64
+    read = write = 0
+    for m in mode.ravel():
+        read += 1 + (d * 2 + 4) * (2 if m == 2 else 1)
+        write += d * 2 + 4
+    b = M.merge_bytes(mode, d)
+    assert (b["read"], b["write"], b["total"]) == (read, write, read + write)
+    assert b["take_a"] + b["take_b"] + b["merge"] == b["pairs"] == 300
