@@ -13,4 +13,5 @@ Modules:
   ledger     closed-form visible-pair, FLOP and byte counts
   rope       query-side rotary relocation by a per-head position offset
   merge      head-decomposition merge: per-(row, head) select or log-sum-exp merge
+  fork       token-level model of copy-on-write forks of per-head segments
 """
