@@ -118,7 +118,9 @@ void segkv_destroy(segkv_ctx *ctx);
  * kv_len - n_query is the earliest pending query.  Pages wholly below that
  * start return to the pool and new tokens below it are never stored.  The
  * segment start never moves back.  Fails with SEGKV_E_NOMEM (no change) if
- * the pool cannot hold the whole batch.
+ * the pool cannot hold the whole batch.  When new tokens land in a
+ * partially filled page that a fork also holds (segkv_fork), the sequence
+ * first gets a private copy of that page (copy-on-write, one extra page).
  */
 int segkv_append_pages(segkv_ctx *ctx, int32_t layer, int32_t n_seqs, const int32_t *seq_ids,
                        const int32_t *cu_new, const int32_t *n_query, const void *k_new,
@@ -204,8 +206,25 @@ enum segkv_merge_mode {
 int segkv_merge(segkv_ctx *ctx, int64_t n_rows, const void *o_a, const float *lse_a, const void *o_b,
                 const float *lse_b, const uint8_t *mode, void *o, float *lse);
 
-/* Return every page of a sequence (all layers, all heads) to the pool,
- * reset its length to 0 and clear its relocation offsets. */
+/*
+ * Fork ("RedKnot: Head-Aware KV Reuse and SegPagedAttention" page, sections
+ * "Getting Started: Repository Layout and Entry Points" and "Experimental
+ * Features and Current Limitations": request forks with copy-on-write
+ * append).  dst_seq, which must hold no tokens in any layer, becomes a
+ * copy of src_seq: same lengths, pending queries and relocation offsets,
+ * and the same physical pages in every (layer, KV head) segment, shared by
+ * reference count.  No page is allocated and no device work is enqueued.
+ * Full shared pages are never written again; an append that writes into a
+ * shared partially filled tail page copies it first (segkv_append_pages).
+ * A page returns to the pool when its last holder releases or trims it.
+ * Errors: SEGKV_E_RANGE for ids out of range, SEGKV_E_INVAL if src == dst,
+ * SEGKV_E_STATE if dst is not empty.  Valid in a planning-only context.
+ */
+int segkv_fork(segkv_ctx *ctx, int32_t src_seq, int32_t dst_seq);
+
+/* Drop every page reference of a sequence (all layers, all heads): pages no
+ * other sequence holds return to the pool.  Resets its length to 0 and
+ * clears its relocation offsets. */
 int segkv_release(segkv_ctx *ctx, int32_t seq_id);
 
 /*

@@ -106,6 +106,19 @@ __global__ __launch_bounds__(kScatterThreads) void scatter_kernel(ScatterArgs a)
   uint16_t *kpage = a.k_pool + static_cast<size_t>(it.page_id) * P * D;
   uint16_t *vpage = a.v_pool + static_cast<size_t>(it.page_id) * P * D;
 
+  // Copy-on-write: slots [0, slot_begin) of the shared page this one
+  // replaces.  They are disjoint from every slot written below.
+  if (it.copy_from >= 0) {
+    const uint16_t *ksrc = a.k_pool + static_cast<size_t>(it.copy_from) * P * D;
+    const uint16_t *vsrc = a.v_pool + static_cast<size_t>(it.copy_from) * P * D;
+    for (int c = tid; c < it.slot_begin * CPR; c += kScatterThreads)
+      *reinterpret_cast<u32x4 *>(kpage + c * 8) = ld16(ksrc + c * 8);
+    for (int c = tid; c < D * it.slot_begin; c += kScatterThreads) {
+      const int d = c / it.slot_begin, sl = c - d * it.slot_begin;
+      vpage[d * P + sl] = vsrc[d * P + sl];
+    }
+  }
+
   // K rows, and V rows staged in LDS for the transpose.
   for (int c = tid; c < n_rows * CPR; c += kScatterThreads) {
     const int row = c / CPR, dc = c - row * CPR;

@@ -87,6 +87,7 @@ struct segkv_ctx {
 
   // allocator state
   std::vector<int32_t> free_list;  // stack; back() is handed out first
+  std::vector<int32_t> refcnt;     // [num_pages]: segments holding each page (0 = free)
   std::vector<Segment> segs;       // [L][S][Hkv]
   std::vector<SeqLayer> seq_layer; // [L][S]
 
@@ -118,6 +119,7 @@ struct segkv_ctx {
   // scratch reused across calls
   std::vector<int32_t> scratch_i32;
   std::vector<int32_t> scratch_deltas;  // distinct nonzero offsets of the current call
+  std::vector<int32_t> scratch_release;  // pages whose reference an append drops after it allocated
   std::vector<PrefillItem> scratch_pitems;
   std::vector<CombineItem> scratch_citems;
 
@@ -134,6 +136,18 @@ struct segkv_ctx {
     return seq_layer[static_cast<size_t>(layer) * S + s];
   }
   int32_t win(int32_t layer, int32_t g) const { return window[static_cast<size_t>(layer) * Hkv + g]; }
+
+  // Pages are shared between forked sequences; a page returns to the free
+  // list when its last holder drops it.
+  int32_t take_page() {
+    const int32_t id = free_list.back();
+    free_list.pop_back();
+    refcnt[static_cast<size_t>(id)] = 1;
+    return id;
+  }
+  void drop_page(int32_t id) {
+    if (--refcnt[static_cast<size_t>(id)] == 0) free_list.push_back(id);
+  }
 
   int fail(int code, const char *fmt, ...) {
     char buf[512];
@@ -434,6 +448,7 @@ int segkv_create(const segkv_config *cfg, segkv_ctx **out) {
     c->segs.resize(static_cast<size_t>(c->L) * c->S * c->Hkv);
     c->seq_layer.resize(static_cast<size_t>(c->L) * c->S);
     c->free_list.resize(static_cast<size_t>(c->num_pages));
+    c->refcnt.assign(static_cast<size_t>(c->num_pages), 0);
   } catch (...) {
     delete c;
     return bad(SEGKV_E_NOMEM, "out of host memory for allocator state");
@@ -520,13 +535,38 @@ int segkv_set_relocation(segkv_ctx *c, int32_t seq_id, const int32_t *deltas) {
   return SEGKV_OK;
 }
 
+int segkv_fork(segkv_ctx *c, int32_t src_seq, int32_t dst_seq) {
+  if (!c) return SEGKV_E_INVAL;
+  if (src_seq < 0 || src_seq >= c->S || dst_seq < 0 || dst_seq >= c->S)
+    return c->fail(SEGKV_E_RANGE, "seq id out of range (src %d, dst %d)", src_seq, dst_seq);
+  if (src_seq == dst_seq) return c->fail(SEGKV_E_INVAL, "fork needs two different sequences");
+  for (int32_t layer = 0; layer < c->L; ++layer) {
+    if (c->sl(layer, dst_seq).kv_len != 0) return c->fail(SEGKV_E_STATE, "fork target %d is not empty", dst_seq);
+    for (int32_t g = 0; g < c->Hkv; ++g)
+      if (c->seg(layer, dst_seq, g).n_live() != 0) return c->fail(SEGKV_E_STATE, "fork target %d holds pages", dst_seq);
+  }
+  for (int32_t layer = 0; layer < c->L; ++layer) {
+    c->sl(layer, dst_seq) = c->sl(layer, src_seq);
+    for (int32_t g = 0; g < c->Hkv; ++g) {
+      const Segment &from = c->seg(layer, src_seq, g);
+      Segment &to = c->seg(layer, dst_seq, g);
+      to.first_token = from.first_token;
+      to.delta = from.delta;
+      to.head = 0;
+      to.pages.assign(from.live(), from.live() + from.n_live());
+      for (int32_t id : to.pages) c->refcnt[static_cast<size_t>(id)]++;
+    }
+  }
+  return SEGKV_OK;
+}
+
 int segkv_release(segkv_ctx *c, int32_t seq_id) {
   if (!c) return SEGKV_E_INVAL;
   if (seq_id < 0 || seq_id >= c->S) return c->fail(SEGKV_E_RANGE, "seq id %d out of range", seq_id);
   for (int32_t layer = 0; layer < c->L; ++layer) {
     for (int32_t g = 0; g < c->Hkv; ++g) {
       Segment &s = c->seg(layer, seq_id, g);
-      for (int32_t i = 0; i < s.n_live(); ++i) c->free_list.push_back(s.live()[i]);
+      for (int32_t i = 0; i < s.n_live(); ++i) c->drop_page(s.live()[i]);
       s.pages.clear();
       s.head = 0;
       s.first_token = 0;
@@ -562,11 +602,15 @@ int segkv_append_pages(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_
     return c->fail(SEGKV_E_INVAL, "k_new / v_new is NULL");
   }
 
-  // Plan: per (b, g) the new segment start, pages freed and pages needed.
+  // Plan: per (b, g) the new segment start, pages dropped, kept and added,
+  // and whether the kept tail page is shared with a fork and must be copied
+  // before the new tokens are written into it.
   const int32_t P = c->P;
-  std::vector<int32_t> &plan = c->scratch_i32;  // [n_seqs*Hkv][4]: new_first, n_free, n_keep, n_add
-  plan.assign(static_cast<size_t>(n_seqs) * c->Hkv * 4, 0);
+  constexpr int kPlan = 5;
+  std::vector<int32_t> &plan = c->scratch_i32;  // [n_seqs*Hkv][5]: new_first, n_drop, n_keep, n_add, cow
+  plan.assign(static_cast<size_t>(n_seqs) * c->Hkv * kPlan, 0);
   int64_t need = 0, freed = 0;
+  std::vector<std::pair<int32_t, int32_t>> shared_drops;  // dropped pages that other segments also hold
   for (int32_t b = 0; b < n_seqs; ++b) {
     const SeqLayer &s = c->sl(layer, seq_ids[b]);
     const int32_t new_kv = s.kv_len + (cu_new[b + 1] - cu_new[b]);
@@ -575,17 +619,38 @@ int segkv_append_pages(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_
       const int32_t w = c->win(layer, g);
       int32_t new_first = sg.first_token;
       if (w > 0) new_first = std::max(new_first, local_segment_start(new_kv, n_query[b], w, P));
-      int32_t n_free = std::min<int32_t>(sg.n_live(), (new_first - sg.first_token) / P);
-      int32_t n_keep = sg.n_live() - n_free;
+      int32_t n_drop = std::min<int32_t>(sg.n_live(), (new_first - sg.first_token) / P);
+      int32_t n_keep = sg.n_live() - n_drop;
       int32_t n_total = new_kv > new_first ? static_cast<int32_t>(ceil_div(new_kv - new_first, P)) : 0;
       int32_t n_add = std::max(0, n_total - n_keep);
-      int32_t *pl = &plan[(static_cast<size_t>(b) * c->Hkv + g) * 4];
+      // The first new token lands in kept page (tok_lo - new_first) / P; when
+      // that is the kept tail and a fork also holds it, copy it first.
+      const int32_t tok_lo = std::max(s.kv_len, new_first);
+      int32_t cow = 0;
+      if (n_keep > 0 && tok_lo < new_kv && (tok_lo - new_first) / P == n_keep - 1 &&
+          c->refcnt[static_cast<size_t>(sg.live()[n_drop + n_keep - 1])] > 1)
+        cow = 1;
+      int32_t *pl = &plan[(static_cast<size_t>(b) * c->Hkv + g) * kPlan];
       pl[0] = new_first;
-      pl[1] = n_free;
+      pl[1] = n_drop;
       pl[2] = n_keep;
       pl[3] = n_add;
-      need += n_add;
-      freed += n_free;
+      pl[4] = cow;
+      need += n_add + cow;
+      for (int32_t i = 0; i < n_drop; ++i) {
+        const int32_t id = sg.live()[i];
+        if (c->refcnt[static_cast<size_t>(id)] == 1) ++freed;
+        else shared_drops.emplace_back(id, 1);
+      }
+    }
+  }
+  if (!shared_drops.empty()) {  // shared pages dropped by every holder in this call are freed too
+    std::sort(shared_drops.begin(), shared_drops.end());
+    for (size_t i = 0; i < shared_drops.size();) {
+      size_t j = i;
+      while (j < shared_drops.size() && shared_drops[j].first == shared_drops[i].first) ++j;
+      if (static_cast<int64_t>(j - i) == c->refcnt[static_cast<size_t>(shared_drops[i].first)]) ++freed;
+      i = j;
     }
   }
   if (need > static_cast<int64_t>(c->free_list.size()) + freed)
@@ -600,7 +665,7 @@ int segkv_append_pages(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_
       const SeqLayer &s = c->sl(layer, seq_ids[b]);
       const int32_t new_kv = s.kv_len + (cu_new[b + 1] - cu_new[b]);
       for (int32_t g = 0; g < c->Hkv; ++g) {
-        const int32_t *pl = &plan[(static_cast<size_t>(b) * c->Hkv + g) * 4];
+        const int32_t *pl = &plan[(static_cast<size_t>(b) * c->Hkv + g) * kPlan];
         int32_t tok_lo = std::max(s.kv_len, pl[0]);
         if (tok_lo >= new_kv) continue;
         n_items += (new_kv - 1 - pl[0]) / P - (tok_lo - pl[0]) / P + 1;
@@ -615,23 +680,32 @@ int segkv_append_pages(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_
     if (rc) return rc;
   }
 
-  // Commit: trim, then allocate, then record scatter work.
+  // Commit: trim, then copy shared tails and allocate, then record scatter
+  // work.  A copied page's reference is dropped only after every allocation
+  // of the call, so a page that this launch reads as a copy source is never
+  // handed out (and written) by the same launch.
   ScatterItem *items = reinterpret_cast<ScatterItem *>(stage);
   int64_t it = 0;
+  std::vector<int32_t> &cow_src = c->scratch_release;
+  cow_src.clear();
   for (int32_t b = 0; b < n_seqs; ++b) {
     SeqLayer &s = c->sl(layer, seq_ids[b]);
     const int32_t old_kv = s.kv_len;
     const int32_t new_kv = old_kv + (cu_new[b + 1] - cu_new[b]);
     for (int32_t g = 0; g < c->Hkv; ++g) {
       Segment &sg = c->seg(layer, seq_ids[b], g);
-      const int32_t *pl = &plan[(static_cast<size_t>(b) * c->Hkv + g) * 4];
-      for (int32_t i = 0; i < pl[1]; ++i) c->free_list.push_back(sg.live()[i]);
+      const int32_t *pl = &plan[(static_cast<size_t>(b) * c->Hkv + g) * kPlan];
+      for (int32_t i = 0; i < pl[1]; ++i) c->drop_page(sg.live()[i]);
       sg.drop_front(pl[1]);
       sg.first_token = pl[0];
-      for (int32_t i = 0; i < pl[3]; ++i) {
-        sg.pages.push_back(c->free_list.back());
-        c->free_list.pop_back();
+      int32_t cow_from = -1;
+      if (pl[4]) {
+        int32_t &tail = sg.pages[sg.head + static_cast<size_t>(pl[2] - 1)];
+        cow_from = tail;
+        cow_src.push_back(tail);
+        tail = c->take_page();
       }
+      for (int32_t i = 0; i < pl[3]; ++i) sg.pages.push_back(c->take_page());
       if (c->planning) continue;
       const int32_t tok_lo = std::max(old_kv, pl[0]);
       if (tok_lo >= new_kv) continue;
@@ -647,13 +721,16 @@ int segkv_append_pages(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_
         si.slot_begin = t0 - ps;
         si.slot_end = t1 - ps;
         si.src_row = cu_new[b] + (t0 - old_kv);
-        si.zero_tail = pi >= pl[2] ? 1 : 0;
-        si.pad0 = si.pad1 = 0;
+        const bool copied = pl[4] && pi == pl[2] - 1;
+        si.zero_tail = pi >= pl[2] || copied ? 1 : 0;
+        si.copy_from = copied ? cow_from : -1;
+        si.pad1 = 0;
       }
     }
     s.kv_len = new_kv;
     s.pending_from = new_kv - n_query[b];
   }
+  for (int32_t id : cow_src) c->drop_page(id);
   if (c->planning || n_items == 0) return SEGKV_OK;
 
   ScatterArgs a;

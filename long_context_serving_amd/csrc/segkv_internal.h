@@ -61,6 +61,8 @@ struct RopeArgs {
 // One page touched by an append: K rows [slot_begin, slot_end) come from
 // new-token rows src_row ..; when zero_tail is set the page is new and slots
 // [slot_end, page_size) are cleared so that no live page holds stale bits.
+// copy_from >= 0: the page replaces a page shared with a fork, whose slots
+// [0, slot_begin) are copied first (copy-on-write).
 struct ScatterItem {
   int32_t page_id;
   int32_t kv_head;
@@ -68,7 +70,8 @@ struct ScatterItem {
   int32_t slot_end;
   int32_t src_row;
   int32_t zero_tail;
-  int32_t pad0, pad1;
+  int32_t copy_from;
+  int32_t pad1;
 };
 
 // One prefill workgroup: rows [qtile*rows_per_tile ...) of (sequence, KV head

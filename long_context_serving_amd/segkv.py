@@ -38,6 +38,7 @@ EXPORTED = (
     "segkv_create", "segkv_destroy", "segkv_append_pages", "segkv_prefill", "segkv_decode",
     "segkv_release", "segkv_page_table", "segkv_free_pages", "segkv_set_timing",
     "segkv_read_timing", "segkv_set_tuning", "segkv_last_error", "segkv_set_relocation", "segkv_merge",
+    "segkv_fork",
 )
 
 MERGE_TAKE_A = 0
@@ -113,6 +114,8 @@ def load_library(path: Optional[str] = None):
     lib.segkv_read_timing.restype = ctypes.c_int
     lib.segkv_set_tuning.argtypes = [vp, i32, i64]
     lib.segkv_set_tuning.restype = ctypes.c_int
+    lib.segkv_fork.argtypes = [vp, i32, i32]
+    lib.segkv_fork.restype = ctypes.c_int
     lib.segkv_merge.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp]
     lib.segkv_merge.restype = ctypes.c_int
     lib.segkv_set_relocation.argtypes = [vp, i32, pi32]
@@ -327,6 +330,10 @@ class SegKV:
 
     def release(self, seq_id: int):
         return self._check(self._lib.segkv_release(self._h, seq_id))
+
+    def fork(self, src_seq: int, dst_seq: int):
+        """dst_seq (empty) shares src_seq's tokens and pages (copy-on-write)."""
+        return self._check(self._lib.segkv_fork(self._h, src_seq, dst_seq))
 
     def set_relocation(self, seq_id: int, deltas=None):
         """Query-side RoPE relocation offsets of one sequence: int32
