@@ -30,6 +30,10 @@ In the same JSON line:
                 (offline Local-head partials, online Global heads and
                 protected rows, LSE merge on the window's boundary rows):
                 algorithmic GB/s against 8 TB/s;
+  fork          copy-on-write forks: the 32K x 31 decode with the 31 sequences
+                forked from one 32767-token parent (each appends its own query
+                token): pages in use against 31 unshared copies, forks that fit
+                in the unshared pool, and the decode kernel over the forks;
   workloads     the varlen Llama-3.3-70B-shaped and the 128K chunked prefill;
   cpu_baseline  the fp64 oracle on a bounded sample of the headline workload.
 
@@ -177,8 +181,10 @@ def decode_arm(w, dev, steps, warmup, windows=None, deltas=None):
     d_ms, d_n = kernel_avg(run.ctx, S.KERNEL_DECODE_SPLIT)
     c_ms, _ = kernel_avg(run.ctx, S.KERNEL_COMBINE)
     run.ctx.set_timing(False)
+    pages = run.ctx.num_pages - run.ctx.free_pages()
     run.close()
-    return {"ms_per_step": dt * 1e3, "split_kernel_ms": d_ms, "combine_kernel_ms": c_ms, "launches": d_n}
+    return {"ms_per_step": dt * 1e3, "split_kernel_ms": d_ms, "combine_kernel_ms": c_ms, "launches": d_n,
+            "pages_in_use": pages}
 
 
 # ----------------------------------------------------------- cpu baseline
@@ -215,6 +221,54 @@ def merge_arm(mw, steps, warmup):
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": gbs / PEAK_HBM_GBS, "traffic": measured_traffic("merge_" + mw.name),
                          "kernel": "merge_kernel<128>", "avg_launch_ms": k_ms}}
+
+
+def fork_arm(dw, steps, warmup, pages_unshared):
+    """31 forks of one parent of kv_len - 1 tokens, each appending one query."""
+    import torch
+    from long_context_serving_amd import metrics as M
+    from long_context_serving_amd import segkv as S
+    from long_context_serving_amd import workloads as wl
+    n, L = dw.n_seqs, dw.kv_lens[0]
+    fw = wl.Workload("fork_parent", (L - 1 + n,), (n,), dw.num_q_heads, dw.num_kv_heads, dw.head_dim,
+                     dw.page_size, dw.windows, seed=dw.seed + 50)
+    x = wl.make_inputs(fw)
+    k, v, q = S.bf16_tensor(x.k), S.bf16_tensor(x.v), S.bf16_tensor(x.q)
+    del x
+    ctx = S.SegKV(1, dw.num_q_heads, dw.num_kv_heads, dw.head_dim, dw.page_size, n + 1, pages_unshared,
+                  list(dw.windows), softmax_scale=dw.scale, page_order_seed=dw.page_order_seed)
+    parent = n
+    ctx.append_pages(0, [parent], [L - 1], [0], k[: L - 1].contiguous(), v[: L - 1].contiguous())
+    parent_pages = ctx.num_pages - ctx.free_pages()
+    t0 = time.perf_counter()
+    for i in range(n):
+        ctx.fork(parent, i)
+    fork_us = (time.perf_counter() - t0) / n * 1e6
+    ctx.append_pages(0, list(range(n)), [1] * n, [1] * n, k[L - 1:].contiguous(), v[L - 1:].contiguous())
+    used = ctx.num_pages - ctx.free_pages()
+    per_fork = (used - parent_pages) / n
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    ids = list(range(n))
+    for _ in range(warmup):
+        ctx.decode(0, ids, q, o, lse)
+    sync()
+    ctx.set_timing(True, [S.KERNEL_DECODE_SPLIT, S.KERNEL_COMBINE])
+    for _ in range(steps):
+        ctx.decode(0, ids, q, o, lse)
+    sync()
+    d_ms, _ = kernel_avg(ctx, S.KERNEL_DECODE_SPLIT)
+    c_ms, _ = kernel_avg(ctx, S.KERNEL_COMBINE)
+    ctx.set_timing(False)
+    ctx.close()
+    by = M.decode_bytes(dw)
+    return {"workload": "decode_32k_x31 as 31 forks of one parent", "pages_in_use": used,
+            "pages_parent": parent_pages, "pages_per_fork": per_fork, "pages_unshared": pages_unshared,
+            "page_ratio": pages_unshared / used, "forks_fitting_in_unshared_pool":
+                int((pages_unshared - parent_pages) // per_fork) if per_fork else None,
+            "fork_call_us": fork_us, "split_kernel_ms": d_ms, "combine_kernel_ms": c_ms,
+            "visible_kv_gbs": by["total"] / ((d_ms + c_ms) * 1e-3) / 1e9,
+            "note": "forks read the shared pages, so part of the visible bytes come from cache"}
 
 
 def local_head_deltas(w, offset):
@@ -406,6 +460,10 @@ def main():
                 "kernel_time_over_plain": kern_r / kern}
         out["decode"] = dec
         del dev4
+        if args.only == "all":
+            log("decode over forks")
+            out["fork"] = fork_arm(dw, K, Wm, d["pages_in_use"])
+            log(f"  {out['fork']}")
 
     if args.only in ("all", "merge"):
         log(f"merge {wl.MERGE_128K.name}")

@@ -495,8 +495,13 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
 // +3).  K rows and V^T channel rows go from HBM straight into operand
 // registers.  Each 64-key chunk is four 16-key S^T blocks; block kb = 2s +
 // hb, row 4u + j holds key 32 s + 8 u + 4 hb + j, so lane group u feeds keys
-// 32 s + 8 u .. +7 to PV step s.  The eight waves take chunks round-robin and
-// are merged through LDS.
+// 32 s + 8 u .. +7 to PV step s.
+//
+// The workgroup's pieces (at most 9 at a time) are laid end to end and their
+// 64-key chunks cut into eight contiguous runs, one per wave.  A wave that
+// reaches the end of a piece leaves its partial (max, sum, o) in its own LDS
+// slot and goes on with the next piece, so no wave waits for another until
+// the batch is done; then each piece is merged over the waves that touched it.
 // ===========================================================================
 
 template <int D, int P>
@@ -505,195 +510,234 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
   constexpr int NDB = D / 16;  // 16-channel blocks of O^T
   constexpr int NW = kDecodeThreads / 64;
   constexpr int TPC = D / 4;   // merge threads per column
-  __shared__ float s_m[NW][kDecodeCols];
-  __shared__ float s_l[NW][kDecodeCols];
-  __shared__ __attribute__((aligned(16))) float s_o[NW][kDecodeCols][D];
+  constexpr int NSLOT = kDecodeSlots;
+  constexpr int MAXP = NSLOT - NW + 1;  // pieces per batch: (piece, wave) pairs fit the slots
+  static_assert(MAXP >= 1, "too few partial slots");
+  __shared__ float s_m[NSLOT][kDecodeCols];
+  __shared__ float s_l[NSLOT][kDecodeCols];
+  __shared__ __attribute__((aligned(16))) float s_o[NSLOT][kDecodeCols][D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c16 = lane & 15, u = lane >> 4;
   const int G = a.group;
-  const int piece_end = a.wg_piece_off[blockIdx.x + 1];
-
-  for (int pc = a.wg_piece_off[blockIdx.x]; pc < piece_end; ++pc) {
+  const int wg_end = a.wg_piece_off[blockIdx.x + 1];
+  auto piece_chunks = [&](int pc) {
     const DecodeItem it = a.items[pc];
-    const SeqDesc sd = a.seqs[it.seq];
-    const SegDesc sg = a.segs[it.seq * a.num_kv_heads + it.kv_head];
-    const int p = sd.kv_len - 1;
-    const int W = sg.window;
-    const int key_begin = sg.first_token + it.page_begin * P;
-    const int key_end = sg.first_token + it.page_end * P;  // exclusive
-    const int lo = max(key_begin, W > 0 ? p - W + 1 : 0);
-    const int hi = min(key_end - 1, p);
+    return ((it.page_end - it.page_begin) * P + 63) / 64;
+  };
 
-    bf16x8 qv[NKK];
-    {
-      const uint16_t *qrow = a.q + (static_cast<size_t>(sd.q_start) * a.num_q_heads + it.kv_head * G + c16) * D;
-      if (sg.rope_off < 0) {
+  for (int b0 = a.wg_piece_off[blockIdx.x]; b0 < wg_end; b0 += MAXP) {
+    const int b1 = min(wg_end, b0 + MAXP);
+    int total = 0;
+    for (int pc = b0; pc < b1; ++pc) total += piece_chunks(pc);
+    // This wave's contiguous run of the batch's 64-key chunks, across pieces.
+    const int c_end = total * (wave + 1) / NW;
+    int c = total * wave / NW;
+    int pc = b0, cum = 0;  // cum: first batch chunk of piece pc
+    while (c < c_end) {
+      int nch = piece_chunks(pc);
+      while (cum + nch <= c) {
+        cum += nch;
+        nch = piece_chunks(++pc);
+      }
+      const int k0 = c - cum;                      // first chunk of the run inside piece pc
+      const int k1 = min(c_end - cum, nch);        // end chunk inside piece pc
+      const DecodeItem it = a.items[pc];
+      const SeqDesc sd = a.seqs[it.seq];
+      const SegDesc sg = a.segs[it.seq * a.num_kv_heads + it.kv_head];
+      const int p = sd.kv_len - 1;
+      const int W = sg.window;
+      const int key_begin = sg.first_token + it.page_begin * P;
+      const int key_end = sg.first_token + it.page_end * P;  // exclusive
+      const int lo = max(key_begin, W > 0 ? p - W + 1 : 0);
+      const int hi = min(key_end - 1, p);
+
+      bf16x8 qv[NKK];
+      {
+        const uint16_t *qrow = a.q + (static_cast<size_t>(sd.q_start) * a.num_q_heads + it.kv_head * G + c16) * D;
+        if (sg.rope_off < 0) {
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          u32x4 x = {0u, 0u, 0u, 0u};
-          if (c16 < G) x = ld16(qrow + kk * 32 + u * 8);
-          qv[kk] = as_bf16x8(x);
-        }
-      } else {
-        const float *tab = a.rope.tables + sg.rope_off;
+          for (int kk = 0; kk < NKK; ++kk) {
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (c16 < G) x = ld16(qrow + kk * 32 + u * 8);
+            qv[kk] = as_bf16x8(x);
+          }
+        } else {
+          const float *tab = a.rope.tables + sg.rope_off;
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          u32x4 x = {0u, 0u, 0u, 0u};
-          if (c16 < G) x = relocate_chunk<D>(qrow, kk * 32 + u * 8, tab, a.rope);
-          qv[kk] = as_bf16x8(x);
+          for (int kk = 0; kk < NKK; ++kk) {
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (c16 < G) x = relocate_chunk<D>(qrow, kk * 32 + u * 8, tab, a.rope);
+            qv[kk] = as_bf16x8(x);
+          }
         }
       }
-    }
 
-    f32x4 oacc[NDB];
+      f32x4 oacc[NDB];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[db] = f32x4{};
-    float m = kNegInf, l = 0.f;
+      for (int db = 0; db < NDB; ++db) oacc[db] = f32x4{};
+      float m = kNegInf, l = 0.f;
 
-    // This wave's keys in 64-key chunks (chunk wave + NW*i), each handled as
-    // two 32-key halves: all loads of a chunk are issued before its two
-    // halves are computed, so each wave keeps 32 KiB in flight.
-    const int n_chunks = (key_end - key_begin + 63) / 64;
-    const int my_chunks = n_chunks > wave ? (n_chunks - wave + NW - 1) / NW : 0;
-    const int n_halves = 2 * my_chunks;
-    auto half_base = [&](int j) { return key_begin + (wave + NW * (j >> 1)) * 64 + 32 * (j & 1); };
-    auto load_half = [&](int j, u32x4 (&kb_)[2][NKK], u32x4 (&vb_)[NDB], int upage) {
-      const int kbase = half_base(j);
+      // Chunks k0 .. k1-1 of the piece, each handled as two 32-key halves:
+      // all loads of a chunk are issued before its two halves are computed,
+      // so each wave keeps 32 KiB in flight.
+      const int n_halves = 2 * (k1 - k0);
+      auto half_base = [&](int j) { return key_begin + (k0 + (j >> 1)) * 64 + 32 * (j & 1); };
+      auto load_half = [&](int j, u32x4 (&kb_)[2][NKK], u32x4 (&vb_)[NDB], int upage) {
+        const int kbase = half_base(j);
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        const int key = kbase + 8 * (c16 >> 2) + 4 * hb + (c16 & 3);
+        for (int hb = 0; hb < 2; ++hb) {
+          const int key = kbase + 8 * (c16 >> 2) + 4 * hb + (c16 & 3);
+          const int rel = key - sg.first_token;
+          const bool ok = key < key_end;
+          const int page = P == 64 ? upage : (ok ? a.page_ids[sg.page_off + rel / P] : 0);
+          const uint16_t *krow = a.k_pool + (static_cast<size_t>(page) * P + rel % P) * D;
+#pragma unroll
+          for (int kk = 0; kk < NKK; ++kk) {
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (ok) x = ld16(krow + kk * 32 + u * 8);
+            kb_[hb][kk] = x;
+          }
+        }
+        const int key = kbase + 8 * u;
         const int rel = key - sg.first_token;
         const bool ok = key < key_end;
         const int page = P == 64 ? upage : (ok ? a.page_ids[sg.page_off + rel / P] : 0);
-        const uint16_t *krow = a.k_pool + (static_cast<size_t>(page) * P + rel % P) * D;
+        const uint16_t *vbase = a.v_pool + static_cast<size_t>(page) * P * D + rel % P;
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
+        for (int db = 0; db < NDB; ++db) {
           u32x4 x = {0u, 0u, 0u, 0u};
-          if (ok) x = ld16(krow + kk * 32 + u * 8);
-          kb_[hb][kk] = x;
+          if (ok) x = ld16(vbase + static_cast<size_t>(db * 16 + c16) * P);
+          vb_[db] = x;
         }
-      }
-      const int key = kbase + 8 * u;
-      const int rel = key - sg.first_token;
-      const bool ok = key < key_end;
-      const int page = P == 64 ? upage : (ok ? a.page_ids[sg.page_off + rel / P] : 0);
-      const uint16_t *vbase = a.v_pool + static_cast<size_t>(page) * P * D + rel % P;
+      };
+      auto compute_half = [&](int j, const u32x4 (&kb_)[2][NKK], const u32x4 (&vb_)[NDB]) {
+        const int kbase = half_base(j);
+        f32x4 sc[2];
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (ok) x = ld16(vbase + static_cast<size_t>(db * 16 + c16) * P);
-        vb_[db] = x;
-      }
-    };
-    auto compute_half = [&](int j, const u32x4 (&kb_)[2][NKK], const u32x4 (&vb_)[NDB]) {
-      const int kbase = half_base(j);
-      f32x4 sc[2];
+        for (int hb = 0; hb < 2; ++hb) {
+          f32x4 acc = f32x4{};
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        f32x4 acc = f32x4{};
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb_[hb][kk]), qv[kk], acc, 0, 0, 0);
-        sc[hb] = acc;
-      }
-      float mx = kNegInf;
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int key = kbase + 8 * u + 4 * hb + jj;
-          if (key < lo || key > hi) sc[hb][jj] = kNegInf;
-          mx = fmaxf(mx, sc[hb][jj]);
+          for (int kk = 0; kk < NKK; ++kk)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb_[hb][kk]), qv[kk], acc, 0, 0, 0);
+          sc[hb] = acc;
         }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const bool bump = mx * a.scale_log2 > m * a.scale_log2 + kRescaleLog2;
-      const float m_new = bump ? mx : m;
-      const float msc = m_new == kNegInf ? 0.f : m_new * a.scale_log2;
-      if (__any(bump)) {
-        const float alpha = bump ? fast_exp2(m * a.scale_log2 - msc) : 1.f;
-        l *= alpha;
+        float mx = kNegInf;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-      }
-      m = m_new;
+        for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          sc[hb][jj] = fast_exp2(fmaf(sc[hb][jj], a.scale_log2, -msc));
-          l += sc[hb][jj];
+          for (int jj = 0; jj < 4; ++jj) {
+            const int key = kbase + 8 * u + 4 * hb + jj;
+            if (key < lo || key > hi) sc[hb][jj] = kNegInf;
+            mx = fmaxf(mx, sc[hb][jj]);
+          }
         }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const bool bump = mx * a.scale_log2 > m * a.scale_log2 + kRescaleLog2;
+        const float m_new = bump ? mx : m;
+        const float msc = m_new == kNegInf ? 0.f : m_new * a.scale_log2;
+        if (__any(bump)) {
+          const float alpha = bump ? fast_exp2(m * a.scale_log2 - msc) : 1.f;
+          l *= alpha;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+        }
+        m = m_new;
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            sc[hb][jj] = fast_exp2(fmaf(sc[hb][jj], a.scale_log2, -msc));
+            l += sc[hb][jj];
+          }
+        }
+        const bf16x8 pb = pack8_bf16(sc[0][0], sc[0][1], sc[0][2], sc[0][3], sc[1][0], sc[1][1], sc[1][2], sc[1][3]);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vb_[db]), pb, oacc[db], 0, 0, 0);
+      };
+      u32x4 kb0[2][NKK], vb0[NDB], kb1[2][NKK], vb1[NDB];
+      // P == 64: a chunk is exactly one page; its id is a uniform (scalar)
+      // load, fetched one chunk ahead, so no vector load of the page table
+      // sits in front of the chunk's K/V loads.
+      auto chunk_page = [&](int j) {
+        const int pi = min((half_base(j) - sg.first_token) / P, sg.n_pages - 1);
+        return a.page_ids[sg.page_off + pi];
+      };
+      int upage = (P == 64 && n_halves > 0) ? chunk_page(0) : 0;
+      for (int j = 0; j < n_halves; j += 2) {
+        const int next = (P == 64 && j + 2 < n_halves) ? chunk_page(j + 2) : 0;
+        load_half(j, kb0, vb0, upage);
+        load_half(j + 1, kb1, vb1, upage);
+        compute_half(j, kb0, vb0);
+        compute_half(j + 1, kb1, vb1);
+        upage = next;
       }
-      const bf16x8 pb = pack8_bf16(sc[0][0], sc[0][1], sc[0][2], sc[0][3], sc[1][0], sc[1][1], sc[1][2], sc[1][3]);
+
+      // This wave's partial of piece pc goes to its own slot: slot
+      // (pc - b0) + wave is distinct for every (piece, wave) pair of a batch
+      // because each wave's pieces follow the previous wave's.
+      float lt = l + __shfl_xor(l, 16);
+      lt += __shfl_xor(lt, 32);
+      const int slot = pc - b0 + wave;
+      if (u == 0) {
+        s_m[slot][c16] = m;
+        s_l[slot][c16] = lt;
+      }
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vb_[db]), pb, oacc[db], 0, 0, 0);
-    };
-    u32x4 kb0[2][NKK], vb0[NDB], kb1[2][NKK], vb1[NDB];
-    // P == 64: chunk j/2 of this wave is exactly one page; its id is a
-    // uniform (scalar) load, fetched one chunk ahead, so no vector load of
-    // the page table sits in front of the chunk's K/V loads.
-    auto chunk_page = [&](int j) {
-      const int pi = min((half_base(j) - sg.first_token) / P, sg.n_pages - 1);
-      return a.page_ids[sg.page_off + pi];
-    };
-    int upage = (P == 64 && n_halves > 0) ? chunk_page(0) : 0;
-    for (int j = 0; j < n_halves; j += 2) {
-      const int next = (P == 64 && j + 2 < n_halves) ? chunk_page(j + 2) : 0;
-      load_half(j, kb0, vb0, upage);
-      load_half(j + 1, kb1, vb1, upage);
-      compute_half(j, kb0, vb0);
-      compute_half(j + 1, kb1, vb1);
-      upage = next;
+        *reinterpret_cast<f32x4 *>(&s_o[slot][c16][db * 16 + u * 4]) = oacc[db];
+      c = cum + k1;
     }
-
-    // Per-wave column statistics, then merge the waves through LDS.
-    float lt = l + __shfl_xor(l, 16);
-    lt += __shfl_xor(lt, 32);
-    __syncthreads();  // the previous piece's merge has finished reading LDS
-    if (u == 0) {
-      s_m[wave][c16] = m;
-      s_l[wave][c16] = lt;
-    }
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-      *reinterpret_cast<f32x4 *>(&s_o[wave][c16][db * 16 + u * 4]) = oacc[db];
     __syncthreads();
 
+    // Merge each piece of the batch over the waves whose runs touched it.
     // Thread -> (column, 4 channels).  A segment held by one piece writes
     // the output; otherwise the piece writes its normalised partial.
-    const bool single = it.n_parts == 1;
-    const size_t out_row0 = static_cast<size_t>(sd.q_start) * a.num_q_heads + it.kv_head * G;
-    for (int e = tid; e < G * TPC; e += kDecodeThreads) {
-      const int cc = e / TPC, d0 = (e - cc * TPC) * 4;
-      float mm = kNegInf;
+    int pstart = 0;
+    for (int pc2 = b0; pc2 < b1; ++pc2) {
+      const int pend = pstart + piece_chunks(pc2);
+      const DecodeItem it = a.items[pc2];
+      const SeqDesc sd = a.seqs[it.seq];
+      const bool single = it.n_parts == 1;
+      const size_t out_row0 = static_cast<size_t>(sd.q_start) * a.num_q_heads + it.kv_head * G;
+      for (int e = tid; e < G * TPC; e += kDecodeThreads) {
+        const int cc = e / TPC, d0 = (e - cc * TPC) * 4;
+        float mm = kNegInf;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) mm = fmaxf(mm, s_m[w][cc]);
-      const float m_use = mm == kNegInf ? 0.f : mm;
-      float lw = 0.f;
-      f32x4 acc = f32x4{};
+        for (int w = 0; w < NW; ++w) {
+          const bool touched = max(pstart, total * w / NW) < min(pend, total * (w + 1) / NW);
+          if (touched) mm = fmaxf(mm, s_m[pc2 - b0 + w][cc]);
+        }
+        const float m_use = mm == kNegInf ? 0.f : mm;
+        float lw = 0.f;
+        f32x4 acc = f32x4{};
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float f = fast_exp2((s_m[w][cc] - m_use) * a.scale_log2);
-        lw = fmaf(s_l[w][cc], f, lw);
-        acc += *reinterpret_cast<const f32x4 *>(&s_o[w][cc][d0]) * f;
+        for (int w = 0; w < NW; ++w) {
+          const bool touched = max(pstart, total * w / NW) < min(pend, total * (w + 1) / NW);
+          if (!touched) continue;
+          const int sl = pc2 - b0 + w;
+          const float f = fast_exp2((s_m[sl][cc] - m_use) * a.scale_log2);
+          lw = fmaf(s_l[sl][cc], f, lw);
+          acc += *reinterpret_cast<const f32x4 *>(&s_o[sl][cc][d0]) * f;
+        }
+        const float inv = lw > 0.f ? 1.f / lw : 0.f;
+        const float lse_v = lw > 0.f ? mm * a.scale + logf(lw) : kNegInf;
+        if (single) {
+          *reinterpret_cast<u32x2 *>(a.o + (out_row0 + cc) * D + d0) =
+              pack4_bf16(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+          if (d0 == 0 && a.lse) a.lse[out_row0 + cc] = lse_v;
+        } else {
+          *reinterpret_cast<f32x4 *>(a.part_o + (static_cast<size_t>(it.part) * kDecodeCols + cc) * D + d0) =
+              acc * inv;
+          if (d0 == 0) a.part_lse[static_cast<size_t>(it.part) * kDecodeCols + cc] = lse_v;
+        }
       }
-      const float inv = lw > 0.f ? 1.f / lw : 0.f;
-      const float lse_v = lw > 0.f ? mm * a.scale + logf(lw) : kNegInf;
-      if (single) {
-        *reinterpret_cast<u32x2 *>(a.o + (out_row0 + cc) * D + d0) =
-            pack4_bf16(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
-        if (d0 == 0 && a.lse) a.lse[out_row0 + cc] = lse_v;
-      } else {
-        *reinterpret_cast<f32x4 *>(a.part_o + (static_cast<size_t>(it.part) * kDecodeCols + cc) * D + d0) =
-            acc * inv;
-        if (d0 == 0) a.part_lse[static_cast<size_t>(it.part) * kDecodeCols + cc] = lse_v;
-      }
+      pstart = pend;
     }
+    __syncthreads();  // the slots are free for the next batch
   }
 }
 

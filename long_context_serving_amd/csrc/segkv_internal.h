@@ -21,6 +21,7 @@ constexpr int kPrefillRows = 256;  // (query position, query head) rows per pref
 constexpr int kPrefillThreads = 512;  // 8 waves, 32 rows each, two per SIMD
 constexpr int kDecodeThreads = 512;  // 8 waves, two per SIMD
 constexpr int kDecodeCols = 16;    // query heads handled by one decode work item (GQA group, padded)
+constexpr int kDecodeSlots = 16;   // LDS partials of one decode workgroup: (piece, wave) pairs of a batch
 constexpr int kScatterThreads = 256;
 constexpr int kMergeThreads = 256;
 constexpr int kMergeUnroll = 4;    // (row, head) pairs in flight per lane of the merge kernel
