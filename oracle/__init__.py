@@ -14,4 +14,5 @@ Modules:
   rope       query-side rotary relocation by a per-head position offset
   merge      head-decomposition merge: per-(row, head) select or log-sum-exp merge
   fork       token-level model of copy-on-write forks of per-head segments
+  router     attention-mass token scores and their top-k (sparse-FFN routing)
 """
