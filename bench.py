@@ -26,6 +26,9 @@ In the same JSON line:
                 p50 / p95 of the prefill kernel time;
   decode        visible-KV GB/s of split-KV decode + combine at 32K x 31
                 sequences against 8 TB/s, and its all-global arm;
+  router        attention-mass token scores of the headline prefill (a second
+                MFMA pass over the visible pairs, QK only: 2 D FLOPs per pair)
+                and the top-k (k = L/4) that routes tokens to the dense FFN;
   merge         the head-decomposition merge of a reused 128K-token document
                 (offline Local-head partials, online Global heads and
                 protected rows, LSE merge on the window's boundary rows):
@@ -188,6 +191,39 @@ def decode_arm(w, dev, steps, warmup, windows=None, deltas=None):
 
 
 # ----------------------------------------------------------- cpu baseline
+
+def router_arm(w, dev, steps, warmup, flops_qk):
+    import torch
+    from long_context_serving_amd import runner as R
+    from long_context_serving_amd import segkv as S
+    run = R.WorkloadRun(w, dev).load()
+    o, lse = run.prefill()
+    scores = torch.empty(dev.q.shape[0], dtype=torch.float32, device=dev.q.device)
+    k = [n // 4 for n in w.q_lens]
+    idx = torch.empty(sum(k), dtype=torch.int32, device=dev.q.device)
+    for _ in range(warmup):
+        run.ctx.token_scores(0, run.seq_ids, w.q_lens, dev.q, lse, scores)
+        run.ctx.topk(w.q_lens, scores, k, idx)
+    sync()
+    run.ctx.set_timing(True, [S.KERNEL_SCORE, S.KERNEL_SCORE_REDUCE, S.KERNEL_TOPK])
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        run.ctx.token_scores(0, run.seq_ids, w.q_lens, dev.q, lse, scores)
+        run.ctx.topk(w.q_lens, scores, k, idx)
+    sync()
+    dt = (time.perf_counter() - t0) / steps
+    s_ms, _ = kernel_avg(run.ctx, S.KERNEL_SCORE)
+    r_ms, _ = kernel_avg(run.ctx, S.KERNEL_SCORE_REDUCE)
+    k_ms, _ = kernel_avg(run.ctx, S.KERNEL_TOPK)
+    run.ctx.set_timing(False)
+    run.close()
+    tf = flops_qk / (s_ms * 1e-3) / 1e12
+    return {"workload": w.name, "k_per_seq": k, "ms_per_call": dt * 1e3, "score_kernel_ms": s_ms,
+            "reduce_kernel_ms": r_ms, "topk_kernel_ms": k_ms, "qk_flops": flops_qk,
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tf / PEAK_BF16_TFLOPS, "traffic": None, "kernel": "score_kernel<128,64>",
+                         "avg_launch_ms": s_ms}}
+
 
 def merge_arm(mw, steps, warmup):
     import torch
@@ -378,6 +414,9 @@ def main():
             log(f"  {glob}")
             proto = paired_protocol(run_seg, run_glob)
             run_glob.close()
+            log("router (token scores + top-k)")
+            out["router"] = router_arm(headline, dev2, K, Wm, flops // 2)
+            log(f"  {out['router']}")
             log("prefill relocated")
             run_rel, rel = prefill_arm(headline, dev2, K, Wm, deltas=local_head_deltas(headline, RELOCATION_OFFSET))
             run_rel.close()

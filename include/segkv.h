@@ -61,7 +61,10 @@ enum segkv_kernel {
   SEGKV_KERNEL_DECODE_SPLIT = 2,  /* split-KV decode, partial (o, lse)      */
   SEGKV_KERNEL_COMBINE = 3,       /* log-sum-exp combine of split partials   */
   SEGKV_KERNEL_MERGE = 4,         /* head-decomposition merge (segkv_merge)  */
-  SEGKV_KERNEL_COUNT = 5
+  SEGKV_KERNEL_SCORE = 5,         /* attention-mass token scores, MFMA pass  */
+  SEGKV_KERNEL_SCORE_REDUCE = 6,  /* their fixed-order reduction              */
+  SEGKV_KERNEL_TOPK = 7,          /* per-sequence top-k selection             */
+  SEGKV_KERNEL_COUNT = 8
 };
 
 typedef struct segkv_ctx segkv_ctx;
@@ -221,6 +224,44 @@ int segkv_merge(segkv_ctx *ctx, int64_t n_rows, const void *o_a, const float *ls
  * SEGKV_E_STATE if dst is not empty.  Valid in a planning-only context.
  */
 int segkv_fork(segkv_ctx *ctx, int32_t src_seq, int32_t dst_seq);
+
+/*
+ * Attention-mass token scores, the router of the sparse FFN ("Xiaohongshu
+ * Open-Sources RedKnot" page, "What Happened" item 2 and "Why Sparse FFN
+ * Matters for Agent Workloads"; "RedKnot: Head-Aware KV Reuse and
+ * SegPagedAttention" page, "The Three Core Mechanisms in Detail", second
+ * mechanism: dense FFN only on the top-k tokens by attention score).
+ * A second pass after segkv_prefill with the same seq_ids, cu_q and q (and
+ * its lse): for each sequence b and each token j of its query chunk (as a
+ * key),
+ *   scores[cu_q[b] + (j - (kv_len - q_len))] = sum over the chunk's query
+ *   rows t and all query heads h that see j of exp(scale q_{t,h}.k_j -
+ *   lse_{t,h}),
+ * the attention mass j receives (fp32; each probability row sums to 1, so a
+ * sequence's scores add up to at most q_len * num_q_heads).  Relocation
+ * offsets apply as in the prefill.  The sum is taken in a fixed order:
+ * results are bitwise reproducible and do not depend on tuning knobs.
+ *   q      device bf16 [cu_q[n_seqs]][num_q_heads][head_dim]
+ *   lse    device fp32 [cu_q[n_seqs]][num_q_heads], from segkv_prefill
+ *   scores device fp32 [cu_q[n_seqs]]
+ * Same argument checks as segkv_prefill; seq_ids must be distinct.
+ */
+int segkv_token_scores(segkv_ctx *ctx, int32_t layer, int32_t n_seqs, const int32_t *seq_ids,
+                       const int32_t *cu_q, const void *q, const float *lse, float *scores);
+
+/*
+ * Top-k tokens of each sequence by score (for example segkv_token_scores'
+ * output): the k[b] highest of scores[cu_n[b] .. cu_n[b+1]), ties broken
+ * towards the lower index, written as indices local to the sequence (0 ..
+ * n_b - 1) in ascending order to out_idx[sum_{b'<b} k[b'] ..].  Scores must
+ * be >= 0 (they are ordered by their bit patterns).
+ *   cu_n    host int32 [n_seqs + 1], prefix sums of the per-sequence counts
+ *   scores  device fp32 [cu_n[n_seqs]]
+ *   k       host int32 [n_seqs], 0 <= k[b] <= n_b
+ *   out_idx device int32 [sum k]
+ */
+int segkv_topk(segkv_ctx *ctx, int32_t n_seqs, const int32_t *cu_n, const float *scores, const int32_t *k,
+               int32_t *out_idx);
 
 /* Drop every page reference of a sequence (all layers, all heads): pages no
  * other sequence holds return to the pool.  Resets its length to 0 and

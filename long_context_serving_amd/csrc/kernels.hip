@@ -483,6 +483,288 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
 }
 
 // ===========================================================================
+// Attention-mass token scores ("attention as a router" for the sparse FFN:
+// "Xiaohongshu Open-Sources RedKnot" page, "What Happened" item 2; "RedKnot:
+// Head-Aware KV Reuse and SegPagedAttention" page, "The Three Core
+// Mechanisms in Detail", second mechanism).  A second pass over the prefill's
+// work: with the rows' final LSE known, key j receives sum over rows (t, h)
+// of exp(scale q.k_j - lse).  The product is taken as S = Q K^T (operands of
+// the prefill's S^T swapped), so a lane holds one key column and 16 query
+// rows and the sum over queries is in-lane plus one lane-pair swap.  The 8
+// waves' per-tile key sums meet in a double-buffered LDS exchange that rides
+// on the K pipeline's per-tile barrier; one wave writes the tile's 64 sums
+// as a partial row.  Partial rows are added by score_reduce_kernel in a
+// fixed order, so the scores do not depend on the work order.
+// ===========================================================================
+
+template <int D, int P>
+__global__ __launch_bounds__(kPrefillThreads, 2) void score_kernel(ScoreArgs a) {
+  using L = PrefillLds<D>;
+  constexpr int NKK = D / 16;
+  constexpr int NW = kPrefillThreads / 64;
+  constexpr int K_INSTR = L::K_CHUNKS / kPrefillThreads;
+  constexpr int NSTAGE = 3;
+  constexpr int KSTAGE = L::K_CHUNKS * 16;  // bytes of one K tile
+  constexpr float kLog2e = 1.4426950408889634f;
+  static_assert(kPrefillRows == 32 * NW && K_INSTR >= 1, "tile layout");
+  __shared__ __attribute__((aligned(16))) uint4 smem4[NSTAGE * KSTAGE / 16];
+  __shared__ float sx[2][NW][kTileKeys];
+  char *smem = reinterpret_cast<char *>(smem4);
+
+  const PrefillItem it = a.items[blockIdx.x];
+  const SeqDesc sd = a.seqs[it.seq];
+  const SegDesc sg = a.segs[it.seq * a.num_kv_heads + it.kv_head];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int G = a.group;
+  const int rows = a.rows_per_tile;
+  const int t0 = it.qtile * rows;
+  const int t_last = min(t0 + rows, sd.q_len) - 1;
+  const int base = sd.kv_len - sd.q_len;
+  const int W = sg.window;
+  const int p_wmin = base + min(t0 + (wave * 32) / G, t_last);
+  const int p_wmax = base + min(t0 + (wave * 32 + 31) / G, t_last);
+
+  // Q operand (A of S = Q K^T): this lane supplies query row wave*32 + col.
+  bf16x8 qv[NKK];
+  {
+    const int r = wave * 32 + col;
+    const int po = r / G;
+    const int h = it.kv_head * G + (r - po * G);
+    const int t = t0 + po;
+    const bool valid = po < rows && t < sd.q_len;
+    const uint16_t *qrow = a.q + (static_cast<size_t>(sd.q_start + t) * a.num_q_heads + h) * D;
+    if (sg.rope_off < 0) {
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (valid) x = ld16(qrow + kk * 16 + half * 8);
+        qv[kk] = as_bf16x8(x);
+      }
+    } else {
+      const float *tab = a.rope.tables + sg.rope_off;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (valid) x = relocate_chunk<D>(qrow, kk * 16 + half * 8, tab, a.rope);
+        qv[kk] = as_bf16x8(x);
+      }
+    }
+  }
+  // The rows of S this lane holds: register v is row 8 (v/4) + 4 half + v%4
+  // of the wave.  Rows past the chunk get lse = +inf, hence probability 0.
+  float lse2[16];
+  int prow[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int r = wave * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+    const int po = r / G;
+    const int t = t0 + po;
+    const bool valid = po < rows && t < sd.q_len;
+    lse2[v] = valid ? a.lse[static_cast<size_t>(sd.q_start + t) * a.num_q_heads + it.kv_head * G + (r - po * G)] * kLog2e
+                    : __builtin_inff();
+    prow[v] = base + min(t, t_last);
+  }
+
+  const int last_page = sg.n_pages - 1;
+  auto issue_tile = [&](int tile, int stage) {
+    const int k0 = tile * kTileKeys;
+    char *st = smem + stage * KSTAGE;
+    int uni_page = 0;
+    if constexpr (P == kTileKeys) {
+      const int pi = min(max((k0 - sg.first_token) / P, 0), last_page);
+      uni_page = a.page_ids[sg.page_off + pi];
+    }
+#pragma unroll
+    for (int j = 0; j < K_INSTR; ++j) {
+      const int c = (j * NW + wave) * 64 + lane;
+      const int row = c / L::KCPR;
+      const int logical = (c % L::KCPR) ^ L::k_swz(row);
+      const uint16_t *src;
+      if constexpr (P == kTileKeys) {
+        src = a.k_pool + static_cast<size_t>(uni_page) * (P * D) + row * D + logical * 8;
+      } else {
+        const int rel = k0 + row - sg.first_token;
+        const int pi = rel >= 0 ? min(rel / P, last_page) : 0;
+        const int slot = rel >= 0 && rel / P <= last_page ? rel % P : 0;
+        src = a.k_pool + (static_cast<size_t>(a.page_ids[sg.page_off + pi]) * P + slot) * D + logical * 8;
+      }
+      lds_dma16(src, st + (j * NW + wave) * 1024);
+    }
+  };
+
+  const int kswz = L::k_swz(col);  // keys col and col + 32 share it
+  // Key sums of one tile over this wave's 32 rows: c0 for key k0 + col, c1
+  // for key k0 + 32 + col (both lanes of a pair end with the full sums).
+  auto process = [&](const char *st, int k0, auto mask_tag, float &c0, float &c1) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const int c = (2 * kk + half) ^ kswz;
+      const bf16x8 kb0 = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + (col * L::KCPR + c) * 16));
+      const bf16x8 kb1 = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + ((col + 32) * L::KCPR + c) * 16));
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qv[kk], kb0, s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qv[kk], kb1, s1, 0, 0, 0);
+    }
+    float e0 = 0.f, e1 = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      float x0 = fmaf(s0[v], a.scale_log2, -lse2[v]);
+      float x1 = fmaf(s1[v], a.scale_log2, -lse2[v]);
+      if constexpr (MASK) {
+        const int key0 = k0 + col, key1 = key0 + 32;
+        const int lo = W > 0 ? prow[v] - W + 1 : 0;
+        if (key0 > prow[v] || key0 < lo) x0 = kNegInf;
+        if (key1 > prow[v] || key1 < lo) x1 = kNegInf;
+      }
+      e0 += fast_exp2(x0);
+      e1 += fast_exp2(x1);
+    }
+    c0 = e0 + __shfl_xor(e0, 32);
+    c1 = e1 + __shfl_xor(e1, 32);
+  };
+  // Tile i's sums of all waves are in sx[i % 2] after the barrier ending
+  // iteration i; wave i % NW adds them (fixed order) during iteration i + 1.
+  auto flush = [&](int i) {
+    if (wave == i % NW) {
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) acc += sx[i & 1][w][lane];
+      a.part[(static_cast<size_t>(it.part) + i) * kTileKeys + lane] = acc;
+    }
+  };
+
+  constexpr int LOADS_PER_TILE = K_INSTR;
+  const int tb = it.tile_begin, te = it.tile_end;
+  if (tb < te) issue_tile(tb, 0);
+  if (tb + 1 < te) {
+    issue_tile(tb + 1, 1);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS_PER_TILE) : "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  __syncthreads();
+  for (int tile = tb; tile < te; ++tile) {
+    const int i = tile - tb;
+    const bool ahead2 = tile + 2 < te;
+    if (ahead2) issue_tile(tile + 2, (i + 2) % NSTAGE);
+    if (i > 0) flush(i - 1);
+    const char *st = smem + (i % NSTAGE) * KSTAGE;
+    const int k0 = tile * kTileKeys;
+    const bool empty = k0 > p_wmax || (W > 0 && k0 + kTileKeys - 1 < p_wmin - W + 1);
+    const bool full = k0 + kTileKeys - 1 <= p_wmin && (W == 0 || k0 >= p_wmax - W + 1);
+    float c0 = 0.f, c1 = 0.f;
+    if (!empty) {
+      if (full)
+        process(st, k0, std::integral_constant<bool, false>{}, c0, c1);
+      else
+        process(st, k0, std::integral_constant<bool, true>{}, c0, c1);
+    }
+    sx[i & 1][wave][half * 32 + col] = half ? c1 : c0;
+    if (ahead2)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS_PER_TILE) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+  if (te > tb) flush(te - tb - 1);
+}
+
+// Scores of the chunk's keys: partial rows added in the host's fixed order.
+__global__ __launch_bounds__(256) void score_reduce_kernel(ScoreReduceArgs a) {
+  const int ri = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (ri >= a.n_rows) return;
+  const int lane = threadIdx.x & 63;
+  const ScoreRow row = a.rows[ri];
+  const SeqDesc sd = a.seqs[row.seq];
+  float acc = 0.f;
+  for (int i = row.begin; i < row.end; ++i) acc += a.part[static_cast<size_t>(a.part_idx[i]) * kTileKeys + lane];
+  const int key = row.tile * kTileKeys + lane;
+  const int base = sd.kv_len - sd.q_len;
+  if (key >= base && key < sd.kv_len) a.scores[sd.q_start + key - base] = acc;
+}
+
+// Top-k per sequence by radix select on the score bits (scores are >= 0, so
+// their bit patterns order like the values), ties to the lower index; the
+// kept indices are written in ascending order.  One workgroup per sequence.
+__device__ __forceinline__ int block_excl_scan(int x, int *s_wave, int *total) {
+  // exclusive prefix sum of a 0/1 flag over the workgroup, in thread order
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t bal = __builtin_amdgcn_ballot_w64(x != 0);
+  const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
+                                              __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0));
+  if (lane == 0) s_wave[wave] = __builtin_popcountll(bal);
+  __syncthreads();
+  int off = 0, tot = 0;
+  for (int w = 0; w < kTopkThreads / 64; ++w) {
+    const int c = s_wave[w];
+    if (w < wave) off += c;
+    tot += c;
+  }
+  __syncthreads();
+  *total = tot;
+  return off + below;
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
+  __shared__ int hist[256];
+  __shared__ int s_wave[kTopkThreads / 64];
+  __shared__ int s_pick[2];
+  const int b = blockIdx.x;
+  const int n = a.cu[b + 1] - a.cu[b];
+  const int k = a.k[b];
+  const uint32_t *key = reinterpret_cast<const uint32_t *>(a.scores + a.cu[b]);
+  int32_t *out = a.out + a.out_off[b];
+  if (k <= 0) return;
+  uint32_t prefix = 0, mask = 0;
+  int need = k;  // how many of the keys matching prefix/mask are still to take
+  if (k < n) {
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int i = threadIdx.x; i < 256; i += kTopkThreads) hist[i] = 0;
+      __syncthreads();
+      for (int j = threadIdx.x; j < n; j += kTopkThreads) {
+        const uint32_t x = key[j];
+        if ((x & mask) == prefix) atomicAdd(&hist[(x >> shift) & 255], 1);
+      }
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        int cum = 0, bk = 255;
+        for (; bk > 0; --bk) {
+          if (cum + hist[bk] >= need) break;
+          cum += hist[bk];
+        }
+        s_pick[0] = bk;
+        s_pick[1] = need - cum;
+      }
+      __syncthreads();
+      prefix |= static_cast<uint32_t>(s_pick[0]) << shift;
+      mask |= 255u << shift;
+      need = s_pick[1];
+      __syncthreads();
+    }
+  }
+  // Keep key > prefix, and the first `need` keys equal to prefix in index
+  // order (k >= n keeps everything).
+  int taken = 0, equal_seen = 0;
+  for (int j0 = 0; j0 < n; j0 += kTopkThreads) {
+    const int j = j0 + threadIdx.x;
+    const uint32_t x = j < n ? key[j] : 0u;
+    const bool in = j < n;
+    const bool eq = in && k < n && x == prefix;
+    int eq_tot;
+    const int eq_rank = block_excl_scan(eq, s_wave, &eq_tot);
+    const bool take = in && (k >= n || x > prefix || (eq && equal_seen + eq_rank < need));
+    int take_tot;
+    const int pos = block_excl_scan(take, s_wave, &take_tot);
+    if (take) out[taken + pos] = j;
+    taken += take_tot;
+    equal_seen += eq_tot;
+  }
+}
+
+// ===========================================================================
 // Decode (stream-K): the visible pages of every (sequence, KV head) segment
 // of the batch form one list, cut into equal contiguous shares, one per
 // workgroup.  A share may cover the end of one segment and the start of the
@@ -922,6 +1204,24 @@ hipError_t launch_combine(const CombineArgs &a, int n_items, int max_entries, in
   if (head_dim == 64) hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(256), 0, s, a);
   else if (head_dim == 128) hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(256), 0, s, a);
   else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_score(const ScoreArgs &a, int n_items, int head_dim, int page_size, hipStream_t s) {
+  if (n_items <= 0) return hipSuccess;
+  SEGKV_DISPATCH_DP(score_kernel, head_dim, page_size, dim3(n_items), dim3(kPrefillThreads), s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_reduce(const ScoreReduceArgs &a, hipStream_t s) {
+  if (a.n_rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(score_reduce_kernel, dim3((a.n_rows + 3) / 4), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const TopkArgs &a, int n_seqs, hipStream_t s) {
+  if (n_seqs <= 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_kernel, dim3(n_seqs), dim3(kTopkThreads), 0, s, a);
   return hipGetLastError();
 }
 

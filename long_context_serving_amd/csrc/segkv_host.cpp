@@ -1107,6 +1107,211 @@ int segkv_decode(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq
   return timed_end(c, &t2);
 }
 
+int segkv_token_scores(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_ids, const int32_t *cu_q,
+                       const void *q, const float *lse, float *scores) {
+  if (!c) return SEGKV_E_INVAL;
+  if (c->planning) return c->fail(SEGKV_E_STATE, "token scores need device pools (planning-only context)");
+  int rc = check_layer_seqs(c, layer, n_seqs, seq_ids);
+  if (rc) return rc;
+  if (n_seqs == 0) return SEGKV_OK;
+  if (!cu_q) return c->fail(SEGKV_E_INVAL, "cu_q is NULL");
+  if (cu_q[0] != 0) return c->fail(SEGKV_E_INVAL, "cu_q[0] must be 0");
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    const int32_t ql = cu_q[b + 1] - cu_q[b];
+    const SeqLayer &s = c->sl(layer, seq_ids[b]);
+    if (ql < 0) return c->fail(SEGKV_E_INVAL, "cu_q must be non-decreasing");
+    if (ql > s.kv_len) return c->fail(SEGKV_E_INVAL, "q_len %d > kv_len %d (seq %d)", ql, s.kv_len, seq_ids[b]);
+    if (ql > 0 && s.kv_len - ql < s.pending_from)
+      return c->fail(SEGKV_E_INVAL, "seq %d: queries start before the earliest pending query", seq_ids[b]);
+    for (int32_t b2 = 0; b2 < b; ++b2)
+      if (seq_ids[b2] == seq_ids[b]) return c->fail(SEGKV_E_INVAL, "duplicate seq id %d", seq_ids[b]);
+  }
+  if (cu_q[n_seqs] == 0) return SEGKV_OK;
+  if (!q || !lse || !scores) return c->fail(SEGKV_E_INVAL, "q / lse / scores is NULL");
+
+  // Items over the chunk's tiles only, in canonical order (sequence, KV
+  // head, q tile, tile range); long items are cut like the prefill's.
+  const int32_t G = c->G;
+  const int32_t rows = kPrefillRows / G;
+  std::vector<PrefillItem> items;
+  int64_t total_cost = 0;
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    const int32_t ql = cu_q[b + 1] - cu_q[b];
+    const SeqLayer &s = c->sl(layer, seq_ids[b]);
+    const int32_t base = s.kv_len - ql;
+    for (int32_t g = 0; g < c->Hkv; ++g) {
+      const int32_t w = c->win(layer, g);
+      for (int32_t qt = 0; qt * rows < ql; ++qt) {
+        const int32_t p_min = base + qt * rows;
+        const int32_t p_max = base + std::min((qt + 1) * rows, ql) - 1;
+        const int32_t lo = w > 0 ? std::max(0, p_min - w + 1) : 0;
+        const int32_t tb = std::max(lo, base) / kTileKeys;
+        const int32_t te = p_max / kTileKeys + 1;
+        items.push_back(PrefillItem{b, g, qt, tb, te, 0, 0, 0});
+        total_cost += te - tb;
+      }
+    }
+  }
+  int64_t split = c->prefill_split_tiles;
+  if (split <= 0) {
+    const int64_t slots = std::max<int64_t>(1, static_cast<int64_t>(c->num_cus) * kPrefillWgPerCu);
+    split = std::max<int64_t>(kMinSplitTiles, ceil_div(total_cost, slots));
+  }
+  std::vector<PrefillItem> cut;
+  int32_t n_part_rows = 0;
+  for (const PrefillItem &x : items) {
+    const int32_t per = static_cast<int32_t>(std::min<int64_t>(split, std::max(1, x.tile_end - x.tile_begin)));
+    for (int32_t t0 = x.tile_begin; t0 < x.tile_end; t0 += per) {
+      const int32_t t1 = std::min(x.tile_end, t0 + per);
+      cut.push_back(PrefillItem{x.seq, x.kv_head, x.qtile, t0, t1, n_part_rows, 0, 0});
+      n_part_rows += t1 - t0;
+    }
+  }
+  // Reduction lists: per (sequence, chunk tile), the partial rows covering
+  // it in canonical item order.
+  std::vector<ScoreRow> srows;
+  std::vector<int32_t> pidx;
+  {
+    size_t first = 0;
+    for (int32_t b = 0; b < n_seqs; ++b) {
+      const int32_t ql = cu_q[b + 1] - cu_q[b];
+      size_t last = first;
+      while (last < cut.size() && cut[last].seq == b) ++last;
+      if (ql > 0) {
+        const SeqLayer &s = c->sl(layer, seq_ids[b]);
+        const int32_t ct0 = (s.kv_len - ql) / kTileKeys, ct1 = (s.kv_len - 1) / kTileKeys + 1;
+        for (int32_t t = ct0; t < ct1; ++t) {
+          ScoreRow r{b, t, static_cast<int32_t>(pidx.size()), 0};
+          for (size_t i = first; i < last; ++i)
+            if (cut[i].tile_begin <= t && t < cut[i].tile_end) pidx.push_back(cut[i].part + (t - cut[i].tile_begin));
+          r.end = static_cast<int32_t>(pidx.size());
+          srows.push_back(r);
+        }
+      }
+      first = last;
+    }
+  }
+  // Schedule longest first (the sums do not depend on it).
+  std::stable_sort(cut.begin(), cut.end(), [](const PrefillItem &x, const PrefillItem &y) {
+    return x.tile_end - x.tile_begin > y.tile_end - y.tile_begin;
+  });
+
+  const SeqTables tl = seq_tables_layout(c, layer, n_seqs, seq_ids);
+  const size_t tbytes = align_up(tl.bytes, 16);
+  const size_t ibytes = align_up(sizeof(PrefillItem) * cut.size(), 16);
+  const size_t rbytes = align_up(sizeof(ScoreRow) * srows.size(), 16);
+  const size_t pbytes = sizeof(int32_t) * pidx.size();
+  const size_t bytes = tbytes + ibytes + rbytes + pbytes;
+  char *stage = nullptr;
+  int slot = 0;
+  rc = acquire_stage(c, bytes, &stage, &slot);
+  if (rc) return rc;
+  rc = ensure_device_buffer(c, &c->d_meta, &c->d_meta_cap, bytes, "hipMalloc(tables)");
+  if (rc) return rc;
+  rc = ensure_device_buffer(c, reinterpret_cast<char **>(&c->d_part), &c->d_part_cap,
+                            static_cast<size_t>(std::max(n_part_rows, 1)) * kTileKeys * sizeof(float),
+                            "hipMalloc(partials)");
+  if (rc) return rc;
+  std::vector<int32_t> qs(n_seqs), qlv(n_seqs);
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    qs[b] = cu_q[b];
+    qlv[b] = cu_q[b + 1] - cu_q[b];
+  }
+  write_seq_tables(c, layer, n_seqs, seq_ids, qs.data(), qlv.data(), tl, stage);
+  std::memcpy(stage + tbytes, cut.data(), sizeof(PrefillItem) * cut.size());
+  std::memcpy(stage + tbytes + ibytes, srows.data(), sizeof(ScoreRow) * srows.size());
+  if (pbytes) std::memcpy(stage + tbytes + ibytes + rbytes, pidx.data(), pbytes);
+  rc = upload(c, slot, bytes);
+  if (rc) return rc;
+
+  ScoreArgs a;
+  a.q = static_cast<const uint16_t *>(q);
+  a.lse = lse;
+  a.k_pool = c->k_pool;
+  a.seqs = reinterpret_cast<const SeqDesc *>(c->d_meta);
+  a.segs = reinterpret_cast<const SegDesc *>(c->d_meta + tl.seg_off);
+  a.page_ids = reinterpret_cast<const int32_t *>(c->d_meta + tl.pid_off);
+  a.rope = rope_args(c, tl);
+  a.items = reinterpret_cast<const PrefillItem *>(c->d_meta + tbytes);
+  a.part = c->d_part;
+  a.num_q_heads = c->Hq;
+  a.num_kv_heads = c->Hkv;
+  a.group = G;
+  a.rows_per_tile = rows;
+  a.scale_log2 = c->scale * 1.4426950408889634f;
+  TimedLaunch t{};
+  rc = timed_begin(c, &t, SEGKV_KERNEL_SCORE);
+  if (rc) return rc;
+  hipError_t e = launch_score(a, static_cast<int>(cut.size()), c->D, c->P, c->stream);
+  if (e != hipSuccess) return c->device_fail(e, "score launch");
+  rc = timed_end(c, &t);
+  if (rc) return rc;
+  ScoreReduceArgs ra;
+  ra.part = c->d_part;
+  ra.part_idx = reinterpret_cast<const int32_t *>(c->d_meta + tbytes + ibytes + rbytes);
+  ra.rows = reinterpret_cast<const ScoreRow *>(c->d_meta + tbytes + ibytes);
+  ra.seqs = a.seqs;
+  ra.scores = scores;
+  ra.n_rows = static_cast<int32_t>(srows.size());
+  TimedLaunch t2{};
+  rc = timed_begin(c, &t2, SEGKV_KERNEL_SCORE_REDUCE);
+  if (rc) return rc;
+  e = launch_score_reduce(ra, c->stream);
+  if (e != hipSuccess) return c->device_fail(e, "score reduce launch");
+  return timed_end(c, &t2);
+}
+
+int segkv_topk(segkv_ctx *c, int32_t n_seqs, const int32_t *cu_n, const float *scores, const int32_t *k,
+               int32_t *out_idx) {
+  if (!c) return SEGKV_E_INVAL;
+  if (c->planning) return c->fail(SEGKV_E_STATE, "top-k needs a device context (planning-only context)");
+  if (n_seqs < 0) return c->fail(SEGKV_E_INVAL, "n_seqs < 0");
+  if (n_seqs == 0) return SEGKV_OK;
+  if (!cu_n || !k) return c->fail(SEGKV_E_INVAL, "cu_n / k is NULL");
+  if (cu_n[0] != 0) return c->fail(SEGKV_E_INVAL, "cu_n[0] must be 0");
+  int64_t total_k = 0;
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    if (cu_n[b + 1] < cu_n[b]) return c->fail(SEGKV_E_INVAL, "cu_n must be non-decreasing");
+    if (k[b] < 0 || k[b] > cu_n[b + 1] - cu_n[b])
+      return c->fail(SEGKV_E_INVAL, "k[%d] = %d must be in [0, %d]", b, k[b], cu_n[b + 1] - cu_n[b]);
+    total_k += k[b];
+  }
+  if (total_k == 0) return SEGKV_OK;
+  if (!scores || !out_idx) return c->fail(SEGKV_E_INVAL, "scores / out_idx is NULL");
+  const size_t nb = static_cast<size_t>(n_seqs);
+  const size_t cu_bytes = align_up(sizeof(int32_t) * (nb + 1), 16);
+  const size_t k_bytes = align_up(sizeof(int32_t) * nb, 16);
+  const size_t bytes = cu_bytes + 2 * k_bytes;
+  char *stage = nullptr;
+  int slot = 0;
+  int rc = acquire_stage(c, bytes, &stage, &slot);
+  if (rc) return rc;
+  rc = ensure_device_buffer(c, &c->d_meta, &c->d_meta_cap, bytes, "hipMalloc(tables)");
+  if (rc) return rc;
+  std::memcpy(stage, cu_n, sizeof(int32_t) * (nb + 1));
+  std::memcpy(stage + cu_bytes, k, sizeof(int32_t) * nb);
+  int32_t *off = reinterpret_cast<int32_t *>(stage + cu_bytes + k_bytes);
+  int32_t acc = 0;
+  for (size_t b = 0; b < nb; ++b) {
+    off[b] = acc;
+    acc += k[b];
+  }
+  rc = upload(c, slot, bytes);
+  if (rc) return rc;
+  TopkArgs a;
+  a.scores = scores;
+  a.cu = reinterpret_cast<const int32_t *>(c->d_meta);
+  a.k = reinterpret_cast<const int32_t *>(c->d_meta + cu_bytes);
+  a.out_off = reinterpret_cast<const int32_t *>(c->d_meta + cu_bytes + k_bytes);
+  a.out = out_idx;
+  TimedLaunch t{};
+  rc = timed_begin(c, &t, SEGKV_KERNEL_TOPK);
+  if (rc) return rc;
+  hipError_t e = launch_topk(a, n_seqs, c->stream);
+  if (e != hipSuccess) return c->device_fail(e, "top-k launch");
+  return timed_end(c, &t);
+}
+
 int segkv_merge(segkv_ctx *c, int64_t n_rows, const void *o_a, const float *lse_a, const void *o_b,
                 const float *lse_b, const uint8_t *mode, void *o, float *lse) {
   if (!c) return SEGKV_E_INVAL;

@@ -24,6 +24,7 @@ constexpr int kDecodeCols = 16;    // query heads handled by one decode work ite
 constexpr int kDecodeSlots = 16;   // LDS partials of one decode workgroup: (piece, wave) pairs of a batch
 constexpr int kScatterThreads = 256;
 constexpr int kMergeThreads = 256;
+constexpr int kTopkThreads = 1024;
 constexpr int kMergeUnroll = 4;    // (row, head) pairs in flight per lane of the merge kernel
 constexpr int kPrefillWgPerCu = 1;  // resident prefill workgroups per CU (96 KiB of LDS each)
 constexpr int kDecodeWgPerCu = 1;   // resident decode workgroups per CU (the stream-K grid size)
@@ -181,6 +182,52 @@ struct CombineArgs {
   int32_t slot_rows;
 };
 
+// Attention-mass token scores.  Work items are PrefillItems over the tiles
+// of the query chunk; PrefillItem::part is the item's first partial row (one
+// row = the 64 key sums of one tile).
+struct ScoreArgs {
+  const uint16_t *q;
+  const float *lse;      // [sum q][num_q_heads], natural log, from the prefill of the same queries
+  const uint16_t *k_pool;
+  const SeqDesc *seqs;
+  const SegDesc *segs;
+  const int32_t *page_ids;
+  const PrefillItem *items;
+  float *part;           // [partial rows][64]
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;
+  int32_t rows_per_tile;
+  float scale_log2;
+  RopeArgs rope;
+};
+
+// One 64-key tile of one sequence's chunk: its key sums are the partial rows
+// part_idx[begin .. end), added in that order.
+struct ScoreRow {
+  int32_t seq;
+  int32_t tile;
+  int32_t begin;
+  int32_t end;
+};
+
+struct ScoreReduceArgs {
+  const float *part;
+  const int32_t *part_idx;
+  const ScoreRow *rows;
+  const SeqDesc *seqs;
+  float *scores;  // [sum q]
+  int32_t n_rows;
+};
+
+struct TopkArgs {
+  const float *scores;
+  const int32_t *cu;       // [n + 1] offsets of each sequence's scores
+  const int32_t *k;        // [n]
+  const int32_t *out_off;  // [n] offsets into out
+  int32_t *out;
+};
+
 struct MergeArgs {
   const uint16_t *o_a;
   const float *lse_a;
@@ -198,6 +245,9 @@ hipError_t launch_prefill(const PrefillArgs &a, int n_items, int head_dim, int p
 hipError_t launch_decode(const DecodeArgs &a, int n_wgs, int head_dim, int page_size, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, int n_items, int max_entries, int head_dim, hipStream_t s);
 hipError_t launch_merge(const MergeArgs &a, int n_wgs, int head_dim, hipStream_t s);
+hipError_t launch_score(const ScoreArgs &a, int n_items, int head_dim, int page_size, hipStream_t s);
+hipError_t launch_score_reduce(const ScoreReduceArgs &a, hipStream_t s);
+hipError_t launch_topk(const TopkArgs &a, int n_seqs, hipStream_t s);
 // bytes are rounded up to 16; both buffers must hold the rounded size
 hipError_t launch_upload(void *dst, const void *src_pinned, size_t bytes, hipStream_t s);
 

@@ -28,6 +28,9 @@ KERNEL_PREFILL = 1
 KERNEL_DECODE_SPLIT = 2
 KERNEL_COMBINE = 3
 KERNEL_MERGE = 4
+KERNEL_SCORE = 5
+KERNEL_SCORE_REDUCE = 6
+KERNEL_TOPK = 7
 
 TUNE_DECODE_MIN_PAGES = 0
 TUNE_PREFILL_SPLIT_TILES = 1
@@ -38,7 +41,7 @@ EXPORTED = (
     "segkv_create", "segkv_destroy", "segkv_append_pages", "segkv_prefill", "segkv_decode",
     "segkv_release", "segkv_page_table", "segkv_free_pages", "segkv_set_timing",
     "segkv_read_timing", "segkv_set_tuning", "segkv_last_error", "segkv_set_relocation", "segkv_merge",
-    "segkv_fork",
+    "segkv_fork", "segkv_token_scores", "segkv_topk",
 )
 
 MERGE_TAKE_A = 0
@@ -114,6 +117,10 @@ def load_library(path: Optional[str] = None):
     lib.segkv_read_timing.restype = ctypes.c_int
     lib.segkv_set_tuning.argtypes = [vp, i32, i64]
     lib.segkv_set_tuning.restype = ctypes.c_int
+    lib.segkv_token_scores.argtypes = [vp, i32, i32, pi32, pi32, vp, vp, vp]
+    lib.segkv_token_scores.restype = ctypes.c_int
+    lib.segkv_topk.argtypes = [vp, i32, pi32, vp, pi32, vp]
+    lib.segkv_topk.restype = ctypes.c_int
     lib.segkv_fork.argtypes = [vp, i32, i32]
     lib.segkv_fork.restype = ctypes.c_int
     lib.segkv_merge.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp]
@@ -279,6 +286,48 @@ class SegKV:
         self._check(self._lib.segkv_prefill(self._h, layer, len(ids), ids_p, cu_p, q.data_ptr(), o.data_ptr(),
                                             lse.data_ptr() if lse is not None else None))
         return o, lse
+
+    def token_scores(self, layer: int, seq_ids, q_lens, q, lse, scores=None):
+        """Attention mass each query-chunk token receives (fp32 [sum q_lens]);
+        q and lse as given to / returned by prefill."""
+        import torch
+        ids, ids_p = _i32(seq_ids)
+        cu, cu_p = _i32(np.concatenate([[0], np.cumsum(np.asarray(q_lens, dtype=np.int64))]))
+        if len(cu) != len(ids) + 1:
+            raise ValueError("seq_ids and q_lens must have the same length")
+        nq = int(cu[-1])
+        _check_dev(q, "q", torch.bfloat16)
+        _check_dev(lse, "lse", torch.float32)
+        if tuple(q.shape) != (nq, self.num_q_heads, self.head_dim) or tuple(lse.shape) != (nq, self.num_q_heads):
+            raise ValueError("q must be [sum q_lens, Hq, D] and lse [sum q_lens, Hq]")
+        if scores is None:
+            scores = torch.empty(nq, dtype=torch.float32, device=q.device)
+        _check_dev(scores, "scores", torch.float32)
+        if tuple(scores.shape) != (nq,):
+            raise ValueError("scores must be [sum q_lens]")
+        self._check(self._lib.segkv_token_scores(self._h, layer, len(ids), ids_p, cu_p, q.data_ptr(), lse.data_ptr(),
+                                                 scores.data_ptr()))
+        return scores
+
+    def topk(self, counts, scores, k, out=None):
+        """Top-k indices (ascending, local to each sequence) of each
+        sequence's slice of scores; returns int32 [sum k]."""
+        import torch
+        cu, cu_p = _i32(np.concatenate([[0], np.cumsum(np.asarray(counts, dtype=np.int64))]))
+        kk, k_p = _i32(k)
+        if len(kk) != len(cu) - 1:
+            raise ValueError("counts and k must have the same length")
+        _check_dev(scores, "scores", torch.float32)
+        if tuple(scores.shape) != (int(cu[-1]),):
+            raise ValueError("scores must be [sum counts]")
+        total = int(kk.sum())
+        if out is None:
+            out = torch.empty(total, dtype=torch.int32, device=scores.device)
+        _check_dev(out, "out", torch.int32)
+        if tuple(out.shape) != (total,):
+            raise ValueError("out must be [sum k]")
+        self._check(self._lib.segkv_topk(self._h, len(kk), cu_p, scores.data_ptr(), k_p, out.data_ptr()))
+        return out
 
     def decode(self, layer: int, seq_ids, q, o=None, lse=None, want_lse: bool = True):
         """One-token decode; q bf16 [n_seqs][Hq][D].  Returns (o, lse)."""

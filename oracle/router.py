@@ -51,12 +51,25 @@ def probabilities(q, k, windows, scale):
 
 def token_scores(q, k, windows, scale, all_keys=False):
     """Attention mass received by each key of the query chunk (or by every
-    key when all_keys is set)."""
-    probs = probabilities(q, k, windows, scale)
-    mass = probs.sum(axis=(0, 1))
+    key when all_keys is set).  The same probabilities as ``probabilities``,
+    added up one query head at a time so that large inputs fit in memory."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    q_len, hq, _ = q.shape
+    kv_len, hkv, _ = k.shape
+    group = hq // hkv
+    pos = A.query_positions(kv_len, q_len)
+    mass = np.zeros(kv_len)
+    for h in range(hq):
+        g = h // group
+        mask = A.visibility_mask(pos, kv_len, windows[g])
+        s = np.where(mask, scale * (q[:, h, :] @ k[:, g, :].T), -np.inf)
+        s -= s.max(axis=1, keepdims=True)
+        np.exp(s, out=s)
+        s /= s.sum(axis=1, keepdims=True)
+        mass += s.sum(axis=0)
     if all_keys:
         return mass
-    kv_len, q_len = k.shape[0], q.shape[0]
     return mass[kv_len - q_len:]
 
 

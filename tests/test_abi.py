@@ -138,3 +138,12 @@ def test_merge_refused_in_planning_context(lib):
     kv = S.SegKV(planning=True, **_cfg())
     assert lib.segkv_merge(kv._h, 4, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, None) == S.SEGKV_E_STATE
     assert lib.segkv_merge(None, 4, None, None, None, None, None, None, None) == S.SEGKV_E_INVAL
+
+
+def test_scores_and_topk_refused_in_planning_context(lib):
+    kv = S.SegKV(planning=True, **_cfg())
+    ids = (ctypes.c_int32 * 1)(0)
+    cu = (ctypes.c_int32 * 2)(0, 1)
+    k = (ctypes.c_int32 * 1)(1)
+    assert lib.segkv_token_scores(kv._h, 0, 1, ids, cu, None, None, None) == S.SEGKV_E_STATE
+    assert lib.segkv_topk(kv._h, 1, cu, None, k, None) == S.SEGKV_E_STATE
