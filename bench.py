@@ -361,7 +361,7 @@ def main():
     # with its own W untimed steps.
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "merge"], default="all",
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "merge", "router"], default="all",
                     help="profiling runs: only the segmented headline prefill, or only segmented decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the varlen and 128K prefill workloads")
@@ -455,6 +455,12 @@ def main():
         })
         del dev2
 
+    if args.only == "router":
+        log(f"inputs {headline.name}")
+        dev2 = R.to_device(headline, wl.make_inputs(headline))
+        out["router"] = router_arm(headline, dev2, K, Wm, flops // 2)
+        del dev2
+
     if args.only in ("all", "decode"):
         dw = wl.DECODE_32K
         log(f"inputs {dw.name}")
@@ -534,6 +540,12 @@ def main():
     elif "value" in out:
         out["cpu_baseline"] = None
 
+    if "value" not in out and args.only == "router":  # profiling runs still print one line
+        m = out["router"]
+        out = {"metric": METRIC, "value": m["roofline"]["achieved"], "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+               "warmup": Wm, "ms_per_step": m["ms_per_call"], "higher_is_better": True, "scaling": "weak",
+               "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": {"workload": m["workload"]},
+               "roofline": m["roofline"], "cpu_baseline": None, "router": m}
     if "value" not in out and args.only == "merge":  # profiling runs still print one line
         m = out["merge"]
         out = {"metric": METRIC, "value": m["value"], "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": Wm,

@@ -672,18 +672,30 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void score_kernel(ScoreArgs a) 
   if (te > tb) flush(te - tb - 1);
 }
 
-// Scores of the chunk's keys: partial rows added in the host's fixed order.
+// Scores of the chunk's keys: one workgroup per 64-key tile.  The tile's
+// partial rows are dealt to 4 lane groups x 4 accumulators (entry i to
+// accumulator i mod 16), which are then added in a fixed tree: the sum is
+// the same on every run, and 16 loads per lane are in flight.
 __global__ __launch_bounds__(256) void score_reduce_kernel(ScoreReduceArgs a) {
-  const int ri = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (ri >= a.n_rows) return;
-  const int lane = threadIdx.x & 63;
-  const ScoreRow row = a.rows[ri];
-  const SeqDesc sd = a.seqs[row.seq];
-  float acc = 0.f;
-  for (int i = row.begin; i < row.end; ++i) acc += a.part[static_cast<size_t>(a.part_idx[i]) * kTileKeys + lane];
-  const int key = row.tile * kTileKeys + lane;
-  const int base = sd.kv_len - sd.q_len;
-  if (key >= base && key < sd.kv_len) a.scores[sd.q_start + key - base] = acc;
+  __shared__ float red[4][kTileKeys];
+  const ScoreRow row = a.rows[blockIdx.x];
+  const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  int i = row.begin + 4 * grp;
+  for (; i + 3 < row.end; i += 16) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] += a.part[static_cast<size_t>(a.part_idx[i + u]) * kTileKeys + lane];
+  }
+  for (int u = 0; u < 4 && i + u < row.end; ++u) acc[u] += a.part[static_cast<size_t>(a.part_idx[i + u]) * kTileKeys + lane];
+  red[grp][lane] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  __syncthreads();
+  if (grp == 0) {
+    const float total = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
+    const SeqDesc sd = a.seqs[row.seq];
+    const int key = row.tile * kTileKeys + lane;
+    const int base = sd.kv_len - sd.q_len;
+    if (key >= base && key < sd.kv_len) a.scores[sd.q_start + key - base] = total;
+  }
 }
 
 // Top-k per sequence by radix select on the score bits (scores are >= 0, so
@@ -1215,7 +1227,7 @@ hipError_t launch_score(const ScoreArgs &a, int n_items, int head_dim, int page_
 
 hipError_t launch_score_reduce(const ScoreReduceArgs &a, hipStream_t s) {
   if (a.n_rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(score_reduce_kernel, dim3((a.n_rows + 3) / 4), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(score_reduce_kernel, dim3(a.n_rows), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
