@@ -306,11 +306,11 @@ int segkv_read_timing(segkv_ctx *ctx, int32_t kernel, double *total_ms, int64_t 
  *                                      batch's total tiles over the GPU's
  *                                      resident workgroup slots (at least
  *                                      16); a huge value disables splitting.
- *   SEGKV_TUNE_PREFILL_ORDER           0 (default): longest-first order;
- *                                      1: XCD-aware order, each XCD (workgroup
- *                                      i runs on XCD i % 8) gets a
- *                                      cost-balanced run of the work list
- *                                      grouped by head, longest first.
+ *   SEGKV_TUNE_PREFILL_ORDER           0 (default): the work list is taken
+ *                                      longest first; 1: the list is cut into
+ *                                      eight cost-balanced runs grouped by
+ *                                      head, each sorted longest first, and
+ *                                      the runs are interleaved.
  * Results do not depend on the knobs beyond fp32 rounding of split merges.
  */
 enum segkv_tune {

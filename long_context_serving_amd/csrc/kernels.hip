@@ -156,8 +156,11 @@ __global__ __launch_bounds__(kScatterThreads) void scatter_kernel(ScatterArgs a)
 }
 
 // ===========================================================================
-// Prefill: one workgroup = 128 (query position, query head) rows of one
-// (sequence, KV head) over a range of 64-key tiles.
+// Prefill: a persistent grid, one workgroup per CU.  Each workgroup takes
+// work items from a queue in list order (longest first); an item is 256
+// (query position, query head) rows of one (sequence, KV head group) over a
+// range of 64-key tiles.  The K/V tile loads run two tiles ahead across item
+// boundaries, so a workgroup never waits for its next item's first tiles.
 //
 // Products are done transposed, S^T = K Q^T and O^T += V^T P^T, with the
 // gfx950 MFMA v_mfma_f32_32x32x16_bf16 (wave64; lane l holds operand row
@@ -238,84 +241,62 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
   constexpr int K_INSTR = L::K_CHUNKS / kPrefillThreads;  // direct loads per lane per tile (K)
   constexpr int V_INSTR = L::V_CHUNKS / kPrefillThreads;  // (V^T)
   constexpr int NSTAGE = 3;
+  constexpr int LOADS_PER_TILE = K_INSTR + V_INSTR;
   static_assert(kPrefillRows == 32 * NW, "one 32-row column block per wave");
   static_assert(K_INSTR >= 1 && V_INSTR >= 1, "tile smaller than one load per lane");
   __shared__ __attribute__((aligned(16))) uint4 smem4[NSTAGE * L::STAGE_BYTES / 16];
+  __shared__ int s_next[2];  // item indices fetched by thread 0; consecutive fetches alternate slots
   char *smem = reinterpret_cast<char *>(smem4);
 
-  const PrefillItem it = a.items[blockIdx.x];
-  if (it.qtile < 0) return;  // empty slot of the XCD-ordered work list (uniform for the workgroup)
-  const SeqDesc sd = a.seqs[it.seq];
-  const SegDesc sg = a.segs[it.seq * a.num_kv_heads + it.kv_head];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
   const int G = a.group;
   const int rows = a.rows_per_tile;
-
-  // Query row of this lane's column.
-  const int r = wave * 32 + col;
+  const int n_items = a.n_items;
+  const int r = wave * 32 + col;  // this lane's row of the item
   const int pos_off = r / G;
-  const int h = it.kv_head * G + (r - pos_off * G);
-  const int t0 = it.qtile * rows;
-  const int t_last = min(t0 + rows, sd.q_len) - 1;  // last valid query of the tile
-  const int t = t0 + pos_off;
-  const bool valid = pos_off < rows && t < sd.q_len;
-  const int base = sd.kv_len - sd.q_len;
-  const int p = base + min(t, t_last);  // invalid columns mimic the last valid row
-  const int W = sg.window;
-  const int vis_lo = W > 0 ? p - W + 1 : 0;
-  // Wave-wide position range (positions grow with r).
-  const int p_wmin = base + min(t0 + (wave * 32) / G, t_last);
-  const int p_wmax = base + min(t0 + (wave * 32 + 31) / G, t_last);
 
-  // Q^T operand, held in registers for the whole item.
-  bf16x8 qv[NKK];
-  {
-    const uint16_t *qrow = a.q + (static_cast<size_t>(sd.q_start + t) * a.num_q_heads + h) * D;
-    if (sg.rope_off < 0) {
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (valid) x = ld16(qrow + kk * 16 + half * 8);
-        qv[kk] = as_bf16x8(x);
-      }
-    } else {
-      const float *tab = a.rope.tables + sg.rope_off;
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (valid) x = relocate_chunk<D>(qrow, kk * 16 + half * 8, tab, a.rope);
-        qv[kk] = as_bf16x8(x);
-      }
-    }
-  }
+  // Work queue: each workgroup takes items in list order (longest first).
+  // cur is being computed; nxt is the next item this workgroup owns (-1
+  // while its index is still in flight through LDS).
+  if (tid == 0) s_next[0] = atomicAdd(a.counter, 1);
+  __syncthreads();
+  int cur = __builtin_amdgcn_readfirstlane(s_next[0]);  // uniform: descriptors load through the scalar cache
+  if (cur >= n_items) return;
+  // The next item is taken late (three tiles before the current one ends),
+  // so the list is handed out longest first; its index arrives through LDS.
+  int nxt = -1;
+  int fslot = 1;  // slot of the next fetch: a slot is rewritten only after every wave passed a later barrier
 
-  f32x16 oacc[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
-  float m = kNegInf;  // running (lazy) max of raw scores of this column
-  float l = 0.f;      // this lane's share of the running sum
-
-  // Direct global->LDS tile loads.  Load j of wave w fills LDS chunks
-  // (j*NW + w)*64 + lane of the stage's K (or V^T) region; the lane fetches
-  // the global chunk that the swizzle places there.  A key outside the
-  // segment (edge tiles only) reads the nearest live page: its score is
-  // masked and every live slot holds finite data.
-  const int last_page = sg.n_pages - 1;
-  auto page_of = [&](int rel, int *slot) {
-    const int pi = rel >= 0 ? min(rel / P, last_page) : 0;
-    *slot = rel >= 0 && rel / P <= last_page ? rel % P : 0;
-    return a.page_ids[sg.page_off + pi];
+  // Producer: global->LDS tile loads run up to two tiles ahead of the
+  // consumer along the sequence of this workgroup's items, so the next
+  // item's first tiles load while the current one finishes.
+  int p_item = cur, p_tile = a.items[cur].tile_begin;  // next tile to issue (p_item < 0: waiting for nxt)
+  int p_end = a.items[cur].tile_end;
+  SegDesc psg = a.segs[a.items[cur].seq * a.num_kv_heads + a.items[cur].kv_head];
+  auto p_set = [&](int idx) {  // point the producer at item idx (descriptors read once per item)
+    const PrefillItem pi_ = a.items[idx];
+    p_item = idx;
+    p_tile = pi_.tile_begin;
+    p_end = pi_.tile_end;
+    psg = a.segs[pi_.seq * a.num_kv_heads + pi_.kv_head];
   };
+  int issued = 0, consumed = 0;                      // tiles issued / computed so far
   auto issue_tile = [&](int tile, int stage) {
     const int k0 = tile * kTileKeys;
+    const int last_page = psg.n_pages - 1;
     char *st = smem + stage * L::STAGE_BYTES;
     int uni_page = 0;
     if constexpr (P == kTileKeys) {
-      const int pi = min(max((k0 - sg.first_token) / P, 0), last_page);
-      uni_page = a.page_ids[sg.page_off + pi];  // uniform: one page per tile
+      const int pg = min(max((k0 - psg.first_token) / P, 0), last_page);
+      uni_page = a.page_ids[psg.page_off + pg];  // uniform: one page per tile
     }
+    auto page_of = [&](int rel, int *slot) {
+      const int pg = rel >= 0 ? min(rel / P, last_page) : 0;
+      *slot = rel >= 0 && rel / P <= last_page ? rel % P : 0;
+      return a.page_ids[psg.page_off + pg];
+    };
 #pragma unroll
     for (int j = 0; j < K_INSTR; ++j) {
       const int c = (j * NW + wave) * 64 + lane;
@@ -326,7 +307,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
         src = a.k_pool + static_cast<size_t>(uni_page) * (P * D) + row * D + logical * 8;
       } else {
         int slot;
-        const int page = page_of(k0 + row - sg.first_token, &slot);
+        const int page = page_of(k0 + row - psg.first_token, &slot);
         src = a.k_pool + (static_cast<size_t>(page) * P + slot) * D + logical * 8;
       }
       lds_dma16(src, st + (j * NW + wave) * 1024);
@@ -341,144 +322,219 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
         src = a.v_pool + static_cast<size_t>(uni_page) * (P * D) + d * P + logical * 8;
       } else {
         int slot;
-        const int page = page_of(k0 + logical * 8 - sg.first_token, &slot);
+        const int page = page_of(k0 + logical * 8 - psg.first_token, &slot);
         src = a.v_pool + static_cast<size_t>(page) * (P * D) + d * P + slot;
       }
       lds_dma16(src, st + L::K_CHUNKS * 16 + (j * NW + wave) * 1024);
     }
   };
+  auto produce = [&](int limit) {
+    while (issued < limit && p_item >= 0) {
+      issue_tile(p_tile, issued % NSTAGE);
+      ++issued;
+      if (++p_tile == p_end) {
+        if (p_item == cur && nxt >= 0 && nxt < n_items)
+          p_set(nxt);
+        else
+          p_item = -1;  // resumes once the consumer knows the item after this one
+      }
+    }
+  };
+  // Wait until the newest `pending` issued tiles are the only loads in flight.
+  auto wait_pending = [&](int pending) {
+    if (pending >= 2)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LOADS_PER_TILE) : "memory");
+    else if (pending == 1)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS_PER_TILE) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+
+  produce(2);
+  wait_pending(issued - 1);
+  __syncthreads();
 
   const int key_a0 = st_row_key(col);  // K row this lane feeds to block 0 (block 1: +32)
   const int vrow_swz = L::v_swz(col);  // V^T rows db*32 + col share it
 
-  // One 64-key tile: S^T = K Q^T, (mask), lazy online softmax, O^T += V^T P^T.
-  auto process = [&](const char *st, int k0, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    f32x16 s0 = f32x16{}, s1 = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const int c = (2 * kk + half) ^ L::k_swz(key_a0);
-      const bf16x8 ka0 = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + (key_a0 * L::KCPR + c) * 16));
-      const bf16x8 ka1 = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + ((key_a0 + 32) * L::KCPR + c) * 16));
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0, qv[kk], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qv[kk], s1, 0, 0, 0);
-    }
-    if constexpr (MASK) {
-      // key = k0 + 16 (v/8) + 8 half + v%8 (+32 for block 1); visible iff
-      // vis_lo <= key <= p, tested as one unsigned range compare.
-      const unsigned lo_rel = static_cast<unsigned>(vis_lo - k0 - 8 * half);
-      const unsigned span = static_cast<unsigned>(p - vis_lo);
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int off = ((v >> 3) << 4) + (v & 7);
-        if (static_cast<unsigned>(off) - lo_rel > span) s0[v] = kNegInf;
-        if (static_cast<unsigned>(off + 32) - lo_rel > span) s1[v] = kNegInf;
-      }
-    }
-    float mx = max32(s0, s1);
+  while (true) {
+    const PrefillItem it = a.items[cur];
+    const SeqDesc sd = a.seqs[it.seq];
+    const SegDesc sg = a.segs[it.seq * a.num_kv_heads + it.kv_head];
+    const int h = it.kv_head * G + (r - pos_off * G);
+    const int t0 = it.qtile * rows;
+    const int t_last = min(t0 + rows, sd.q_len) - 1;  // last valid query of the tile
+    const int t = t0 + pos_off;
+    const bool valid = pos_off < rows && t < sd.q_len;
+    const int base = sd.kv_len - sd.q_len;
+    const int p = base + min(t, t_last);  // invalid columns mimic the last valid row
+    const int W = sg.window;
+    const int vis_lo = W > 0 ? p - W + 1 : 0;
+    const int p_wmin = base + min(t0 + (wave * 32) / G, t_last);
+    const int p_wmax = base + min(t0 + (wave * 32 + 31) / G, t_last);
+
+    // Q^T operand, held in registers for the whole item.
+    bf16x8 qv[NKK];
     {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    // Lazy running max (the lane pair of a column takes the same decision).
-    const bool bump = mx * a.scale_log2 > m * a.scale_log2 + kRescaleLog2;
-    const float m_new = bump ? mx : m;
-    const float msc = m_new == kNegInf ? 0.f : m_new * a.scale_log2;
-    // Rare after the first tiles: a scalar branch on the wave's ballot.
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(bump) != 0, 0)) {
-      const float alpha = bump ? fast_exp2(m * a.scale_log2 - msc) : 1.f;
-      l *= alpha;
+      const uint16_t *qrow = a.q + (static_cast<size_t>(sd.q_start + t) * a.num_q_heads + h) * D;
+      if (sg.rope_off < 0) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-    }
-    m = m_new;
+        for (int kk = 0; kk < NKK; ++kk) {
+          u32x4 x = {0u, 0u, 0u, 0u};
+          if (valid) x = ld16(qrow + kk * 16 + half * 8);
+          qv[kk] = as_bf16x8(x);
+        }
+      } else {
+        const float *tab = a.rope.tables + sg.rope_off;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      s0[v] = fast_exp2(fmaf(s0[v], a.scale_log2, -msc));
-      s1[v] = fast_exp2(fmaf(s1[v], a.scale_log2, -msc));
-    }
-    l += sum32(s0, s1);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const f32x16 &sv = kb ? s1 : s0;
-        const bf16x8 pb = pack8_bf16(sv[8 * s + 0], sv[8 * s + 1], sv[8 * s + 2], sv[8 * s + 3], sv[8 * s + 4],
-                                     sv[8 * s + 5], sv[8 * s + 6], sv[8 * s + 7]);
-        const int c = (kb * 4 + s * 2 + half) ^ vrow_swz;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const bf16x8 va =
-              as_bf16x8(*reinterpret_cast<const u32x4 *>(st + ((L::K_CHUNKS + (db * 32 + col) * 8) + c) * 16));
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[db], 0, 0, 0);
+        for (int kk = 0; kk < NKK; ++kk) {
+          u32x4 x = {0u, 0u, 0u, 0u};
+          if (valid) x = relocate_chunk<D>(qrow, kk * 16 + half * 8, tab, a.rope);
+          qv[kk] = as_bf16x8(x);
         }
       }
     }
-  };
 
-  // Three-stage ring: tile i + 2 is in flight while tile i is computed; the
-  // wait before each barrier lets only the newest tile's loads stay pending.
-  constexpr int LOADS_PER_TILE = K_INSTR + V_INSTR;
-  const int tb = it.tile_begin, te = it.tile_end;
-  if (tb < te) issue_tile(tb, 0);
-  if (tb + 1 < te) {
-    issue_tile(tb + 1, 1);
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS_PER_TILE) : "memory");
-  } else {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
-  __syncthreads();
-  for (int tile = tb; tile < te; ++tile) {
-    const int i = tile - tb;
-    const bool ahead2 = tile + 2 < te;
-    if (ahead2) issue_tile(tile + 2, (i + 2) % NSTAGE);
-    const char *st = smem + (i % NSTAGE) * L::STAGE_BYTES;
-    const int k0 = tile * kTileKeys;
-    const bool empty = k0 > p_wmax || (W > 0 && k0 + kTileKeys - 1 < p_wmin - W + 1);
-    const bool full = k0 + kTileKeys - 1 <= p_wmin && (W == 0 || k0 >= p_wmax - W + 1);
-    if (!empty) {
-      if (full)
-        process(st, k0, std::integral_constant<bool, false>{});
-      else
-        process(st, k0, std::integral_constant<bool, true>{});
-    }
-    if (ahead2)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS_PER_TILE) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  }
+    f32x16 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+    float m = kNegInf;  // running (lazy) max of raw scores of this column
+    float l = 0.f;      // this lane's share of the running sum
 
-  const float l_tot = l + __shfl_xor(l, 32);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const float lse_val = l_tot > 0.f ? m * a.scale + logf(l_tot) : kNegInf;
-  if (it.part < 0) {
-    if (!valid) return;
-    uint16_t *orow = a.o + (static_cast<size_t>(sd.q_start + t) * a.num_q_heads + h) * D;
+    // One 64-key tile: S^T = K Q^T, (mask), lazy online softmax, O^T += V^T P^T.
+    auto process = [&](const char *st, int k0, auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+      for (int kk = 0; kk < NKK; ++kk) {
+        const int c = (2 * kk + half) ^ L::k_swz(key_a0);
+        const bf16x8 ka0 = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + (key_a0 * L::KCPR + c) * 16));
+        const bf16x8 ka1 = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + ((key_a0 + 32) * L::KCPR + c) * 16));
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0, qv[kk], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qv[kk], s1, 0, 0, 0);
+      }
+      if constexpr (MASK) {
+        // key = k0 + 16 (v/8) + 8 half + v%8 (+32 for block 1); visible iff
+        // vis_lo <= key <= p, tested as one unsigned range compare.
+        const unsigned lo_rel = static_cast<unsigned>(vis_lo - k0 - 8 * half);
+        const unsigned span = static_cast<unsigned>(p - vis_lo);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d0 = db * 32 + i * 8 + half * 4;
-        *reinterpret_cast<u32x2 *>(orow + d0) =
-            pack4_bf16(oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv, oacc[db][4 * i + 2] * inv,
-                       oacc[db][4 * i + 3] * inv);
+        for (int v = 0; v < 16; ++v) {
+          const int off = ((v >> 3) << 4) + (v & 7);
+          if (static_cast<unsigned>(off) - lo_rel > span) s0[v] = kNegInf;
+          if (static_cast<unsigned>(off + 32) - lo_rel > span) s1[v] = kNegInf;
+        }
+      }
+      float mx = max32(s0, s1);
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      // Lazy running max (the lane pair of a column takes the same decision).
+      const bool bump = mx * a.scale_log2 > m * a.scale_log2 + kRescaleLog2;
+      const float m_new = bump ? mx : m;
+      const float msc = m_new == kNegInf ? 0.f : m_new * a.scale_log2;
+      // Rare after the first tiles: a scalar branch on the wave's ballot.
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(bump) != 0, 0)) {
+        const float alpha = bump ? fast_exp2(m * a.scale_log2 - msc) : 1.f;
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      }
+      m = m_new;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        s0[v] = fast_exp2(fmaf(s0[v], a.scale_log2, -msc));
+        s1[v] = fast_exp2(fmaf(s1[v], a.scale_log2, -msc));
+      }
+      l += sum32(s0, s1);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const f32x16 &sv = kb ? s1 : s0;
+          const bf16x8 pb = pack8_bf16(sv[8 * s + 0], sv[8 * s + 1], sv[8 * s + 2], sv[8 * s + 3], sv[8 * s + 4],
+                                       sv[8 * s + 5], sv[8 * s + 6], sv[8 * s + 7]);
+          const int c = (kb * 4 + s * 2 + half) ^ vrow_swz;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const bf16x8 va =
+                as_bf16x8(*reinterpret_cast<const u32x4 *>(st + ((L::K_CHUNKS + (db * 32 + col) * 8) + c) * 16));
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[db], 0, 0, 0);
+          }
+        }
+      }
+    };
+
+    // Tiles of this item.  The wait before each barrier leaves only the
+    // loads issued after the next tile pending.
+    const int fetch_tile = max(it.tile_begin, it.tile_end - 3);
+    for (int tile = it.tile_begin; tile < it.tile_end; ++tile) {
+      if (tile == fetch_tile && tid == 0) s_next[fslot] = atomicAdd(a.counter, 1);
+      if (issued <= consumed) {  // the producer fell behind (short items): load this tile now
+        produce(consumed + 1);
+        wait_pending(issued - consumed - 1);
+        __syncthreads();
+      }
+      produce(consumed + 3);
+      const char *st = smem + (consumed % NSTAGE) * L::STAGE_BYTES;
+      const int k0 = tile * kTileKeys;
+      const bool empty = k0 > p_wmax || (W > 0 && k0 + kTileKeys - 1 < p_wmin - W + 1);
+      const bool full = k0 + kTileKeys - 1 <= p_wmin && (W == 0 || k0 >= p_wmax - W + 1);
+      if (!empty) {
+        if (full)
+          process(st, k0, std::integral_constant<bool, false>{});
+        else
+          process(st, k0, std::integral_constant<bool, true>{});
+      }
+      wait_pending(issued - consumed - 2);
+      __syncthreads();
+      ++consumed;
+      if (tile == fetch_tile) {  // the index fetched in this iteration is visible after its barrier
+        nxt = __builtin_amdgcn_readfirstlane(s_next[fslot]);
+        fslot ^= 1;
+        if (p_item < 0 && nxt < n_items) p_set(nxt);
       }
     }
-    if (half == 0 && a.lse) a.lse[static_cast<size_t>(sd.q_start + t) * a.num_q_heads + h] = lse_val;
-  } else {
-    float *prow = a.part_o + (static_cast<size_t>(it.part) * kPrefillRows + r) * D;
+
+    const float l_tot = l + __shfl_xor(l, 32);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float lse_val = l_tot > 0.f ? m * a.scale + logf(l_tot) : kNegInf;
+    if (it.part < 0) {
+      if (valid) {
+        uint16_t *orow = a.o + (static_cast<size_t>(sd.q_start + t) * a.num_q_heads + h) * D;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+        for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d0 = db * 32 + i * 8 + half * 4;
-        f32x4 x = {oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv, oacc[db][4 * i + 2] * inv,
-                   oacc[db][4 * i + 3] * inv};
-        *reinterpret_cast<f32x4 *>(prow + d0) = x;
+          for (int i = 0; i < 4; ++i) {
+            const int d0 = db * 32 + i * 8 + half * 4;
+            *reinterpret_cast<u32x2 *>(orow + d0) =
+                pack4_bf16(oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv, oacc[db][4 * i + 2] * inv,
+                           oacc[db][4 * i + 3] * inv);
+          }
+        }
+        if (half == 0 && a.lse) a.lse[static_cast<size_t>(sd.q_start + t) * a.num_q_heads + h] = lse_val;
       }
+    } else {
+      float *prow = a.part_o + (static_cast<size_t>(it.part) * kPrefillRows + r) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d0 = db * 32 + i * 8 + half * 4;
+          f32x4 x = {oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv, oacc[db][4 * i + 2] * inv,
+                     oacc[db][4 * i + 3] * inv};
+          *reinterpret_cast<f32x4 *>(prow + d0) = x;
+        }
+      }
+      if (half == 0) a.part_lse[static_cast<size_t>(it.part) * kPrefillRows + r] = lse_val;
     }
-    if (half == 0) a.part_lse[static_cast<size_t>(it.part) * kPrefillRows + r] = lse_val;
+
+    // Next item.  Its index was fetched during the previous item; fetch the
+    // one after it now (read after the first tile's barrier).
+    if (nxt >= n_items) break;
+    cur = nxt;
+    nxt = -1;
   }
 }
 

@@ -832,10 +832,9 @@ int segkv_prefill(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *se
     }
     items.swap(expanded);
   }
-  // Order: longest first.  XCD-aware order additionally gives each XCD (its
-  // own L2) a contiguous, cost-balanced run of the list, so the workgroups
-  // sharing an L2 read the same few heads' K/V; queue x holds the items at
-  // positions x, x + 8, x + 16, ... (empty slots padded with qtile = -1).
+  // Order: longest first (the persistent workgroups take the list in order).
+  // Order 1 cuts the list into eight cost-balanced runs grouped by head, sorts
+  // each longest first and interleaves them (item x of run k at 8x + k).
   auto lpt_sort = [&](std::vector<PrefillItem> &v) {
     std::vector<int32_t> &cnt = c->scratch_i32;
     cnt.assign(static_cast<size_t>(max_cost) + 2, 0);
@@ -866,9 +865,10 @@ int segkv_prefill(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *se
       lpt_sort(v);
       n_q = std::max(n_q, v.size());
     }
-    items.assign(n_q * kXcds, PrefillItem{0, 0, -1, 0, 0, -1, 0, 0});
-    for (int x = 0; x < kXcds; ++x)
-      for (size_t j = 0; j < q[x].size(); ++j) items[j * kXcds + x] = q[x][j];
+    items.clear();
+    for (size_t j = 0; j < n_q; ++j)
+      for (int x = 0; x < kXcds; ++x)
+        if (j < q[x].size()) items.push_back(q[x][j]);
   } else {
     lpt_sort(items);
   }
@@ -876,8 +876,8 @@ int segkv_prefill(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *se
   const SeqTables tl = seq_tables_layout(c, layer, n_seqs, seq_ids);
   const size_t tbytes = align_up(tl.bytes, 16);
   const size_t ibytes = align_up(sizeof(PrefillItem) * items.size(), 16);
-  const size_t cbytes = sizeof(CombineItem) * citems.size();
-  const size_t bytes = tbytes + ibytes + cbytes;
+  const size_t cbytes = align_up(sizeof(CombineItem) * citems.size(), 16);
+  const size_t bytes = tbytes + ibytes + cbytes + 16;  // + the work-queue counter
   char *stage = nullptr;
   int slot = 0;
   rc = acquire_stage(c, bytes, &stage, &slot);
@@ -897,7 +897,8 @@ int segkv_prefill(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *se
   }
   write_seq_tables(c, layer, n_seqs, seq_ids, qs.data(), ql.data(), tl, stage);
   std::memcpy(stage + tbytes, items.data(), sizeof(PrefillItem) * items.size());
-  if (cbytes) std::memcpy(stage + tbytes + ibytes, citems.data(), cbytes);
+  if (!citems.empty()) std::memcpy(stage + tbytes + ibytes, citems.data(), sizeof(CombineItem) * citems.size());
+  std::memset(stage + tbytes + ibytes + cbytes, 0, 16);
   rc = upload(c, slot, bytes);
   if (rc) return rc;
 
@@ -920,10 +921,14 @@ int segkv_prefill(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *se
   a.rows_per_tile = rows;
   a.scale = c->scale;
   a.scale_log2 = c->scale * 1.4426950408889634f;
+  a.n_items = static_cast<int32_t>(items.size());
+  a.counter = reinterpret_cast<int32_t *>(c->d_meta + tbytes + ibytes + cbytes);
+  const int64_t n_wgs = std::min<int64_t>(static_cast<int64_t>(items.size()),
+                                          std::max<int64_t>(1, static_cast<int64_t>(c->num_cus) * kPrefillWgPerCu));
   TimedLaunch t{};
   rc = timed_begin(c, &t, SEGKV_KERNEL_PREFILL);
   if (rc) return rc;
-  hipError_t e = launch_prefill(a, static_cast<int>(items.size()), c->D, c->P, c->stream);
+  hipError_t e = launch_prefill(a, static_cast<int>(n_wgs), c->D, c->P, c->stream);
   if (e != hipSuccess) return c->device_fail(e, "prefill launch");
   rc = timed_end(c, &t);
   if (rc) return rc;

@@ -26,7 +26,7 @@ constexpr int kScatterThreads = 256;
 constexpr int kMergeThreads = 256;
 constexpr int kTopkThreads = 1024;
 constexpr int kMergeUnroll = 4;    // (row, head) pairs in flight per lane of the merge kernel
-constexpr int kPrefillWgPerCu = 1;  // resident prefill workgroups per CU (96 KiB of LDS each)
+constexpr int kPrefillWgPerCu = 1;  // resident prefill workgroups per CU (96 KiB of LDS each): the persistent grid
 constexpr int kDecodeWgPerCu = 1;   // resident decode workgroups per CU (the stream-K grid size)
 constexpr int kXcds = 8;           // MI355X: workgroup i of a launch runs on XCD i % 8
 
@@ -76,10 +76,9 @@ struct ScatterItem {
   int32_t pad1;
 };
 
-// One prefill workgroup: rows [qtile*rows_per_tile ...) of (sequence, KV head
+// One prefill work item: rows [qtile*rows_per_tile ...) of (sequence, KV head
 // group) over KV tiles [tile_begin, tile_end).  part >= 0 writes fp32
 // partial results to partial slot `part` instead of the final output.
-// qtile < 0 marks an empty slot of the XCD-ordered list (the workgroup exits).
 struct PrefillItem {
   int32_t seq;
   int32_t kv_head;
@@ -146,6 +145,8 @@ struct PrefillArgs {
   float scale_log2;       // softmax scale * log2(e)
   float scale;
   RopeArgs rope;
+  int32_t n_items;        // work items; workgroups take them in list order from *counter
+  int32_t *counter;       // zero at launch (part of the uploaded tables)
 };
 
 struct DecodeArgs {
