@@ -214,3 +214,19 @@ def test_kernel_timing_mask():
     with pytest.raises(S.SegKVError):
         run.ctx._check(run.ctx._lib.segkv_set_timing(run.ctx._h, 1 << 9))
     run.close()
+
+
+@pytest.mark.parametrize("case", [
+    # many one-tile items (the work queue's producer falls behind) mixed with long ones
+    (tuple(range(1, 61)), tuple(range(1, 61)), 8, 2, 128, 64, (0, 16)),
+    (tuple(3 + (7 * i) % 50 for i in range(90)) + (1500,), tuple(min(1 + (3 * i) % 5, 3 + (7 * i) % 50) for i in range(90)) + (700,),
+     16, 4, 64, 16, (0, 5, 64, 300)),
+    ((1,) * 40 + (2000,), (1,) * 40 + (2000,), 4, 1, 128, 32, (0,)),
+])
+def test_prefill_many_short_items(case):
+    kv, q, hq, hkv, d, p, windows = case
+    w = small("short_items", kv, q, hq, hkv, d, p, windows, seed=len(kv) + d)
+    x = wl.make_inputs(w)
+    o, lse = gpu_run(w, x)
+    rows = [sample_rows(w, b, n_random=64) for b in range(w.n_seqs)]
+    compare(w, x, o, lse, rows_per_seq=rows)
