@@ -230,6 +230,7 @@ def merge_arm(mw, steps, warmup):
     from long_context_serving_amd import metrics as M
     from long_context_serving_amd import segkv as S
     from long_context_serving_amd import workloads as wl
+    torch.cuda.empty_cache()  # fresh allocations for the multi-GB buffers, whatever ran before
     mi = wl.make_merge_inputs(mw)
     by = M.merge_bytes(mi.mode, mw.head_dim)
     ctx = S.SegKV(1, mw.num_q_heads, mw.num_kv_heads, mw.head_dim, 64, 1, 4, [0] * mw.num_kv_heads)
@@ -266,6 +267,7 @@ def fork_arm(dw, steps, warmup, pages_unshared):
     from long_context_serving_amd import segkv as S
     from long_context_serving_amd import workloads as wl
     n, L = dw.n_seqs, dw.kv_lens[0]
+    torch.cuda.empty_cache()
     fw = wl.Workload("fork_parent", (L - 1 + n,), (n,), dw.num_q_heads, dw.num_kv_heads, dw.head_dim,
                      dw.page_size, dw.windows, seed=dw.seed + 50)
     x = wl.make_inputs(fw)
