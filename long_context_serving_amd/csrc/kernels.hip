@@ -756,16 +756,22 @@ __global__ __launch_bounds__(256) void score_reduce_kernel(ScoreReduceArgs a) {
 
 // Top-k per sequence by radix select on the score bits (scores are >= 0, so
 // their bit patterns order like the values), ties to the lower index; the
-// kept indices are written in ascending order.  One workgroup per sequence.
+// kept indices are written in ascending order.  One workgroup per sequence;
+// each thread holds kTopkRun consecutive keys per batch, so one batch of
+// loads is in flight per pass rather than one load per 1024 keys.
 __device__ __forceinline__ int block_excl_scan(int x, int *s_wave, int *total) {
-  // exclusive prefix sum of a 0/1 flag over the workgroup, in thread order
+  // exclusive prefix sum of x over the workgroup, in thread order
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint64_t bal = __builtin_amdgcn_ballot_w64(x != 0);
-  const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
-                                              __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0));
-  if (lane == 0) s_wave[wave] = __builtin_popcountll(bal);
+  int inc = x;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(inc, d);
+    if (lane >= d) inc += t;
+  }
+  if (lane == 63) s_wave[wave] = inc;
   __syncthreads();
   int off = 0, tot = 0;
+#pragma unroll
   for (int w = 0; w < kTopkThreads / 64; ++w) {
     const int c = s_wave[w];
     if (w < wave) off += c;
@@ -773,38 +779,63 @@ __device__ __forceinline__ int block_excl_scan(int x, int *s_wave, int *total) {
   }
   __syncthreads();
   *total = tot;
-  return off + below;
+  return off + inc - x;
 }
 
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
-  __shared__ int hist[256];
-  __shared__ int s_wave[kTopkThreads / 64];
+  constexpr int NWV = kTopkThreads / 64;
+  constexpr int R = kTopkRun;
+  constexpr int BATCH = kTopkThreads * R;
+  static_assert(BATCH < 65536, "per-batch counts are packed in 16 bits");
+  __shared__ int hist[NWV][256];  // one histogram per wave
+  __shared__ int s_wave[NWV];
   __shared__ int s_pick[2];
   const int b = blockIdx.x;
   const int n = a.cu[b + 1] - a.cu[b];
   const int k = a.k[b];
   const uint32_t *key = reinterpret_cast<const uint32_t *>(a.scores + a.cu[b]);
   int32_t *out = a.out + a.out_off[b];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (k <= 0) return;
   uint32_t prefix = 0, mask = 0;
   int need = k;  // how many of the keys matching prefix/mask are still to take
   if (k < n) {
     for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int i = threadIdx.x; i < 256; i += kTopkThreads) hist[i] = 0;
+      for (int i = threadIdx.x; i < NWV * 256; i += kTopkThreads) (&hist[0][0])[i] = 0;
       __syncthreads();
-      for (int j = threadIdx.x; j < n; j += kTopkThreads) {
-        const uint32_t x = key[j];
-        if ((x & mask) == prefix) atomicAdd(&hist[(x >> shift) & 255], 1);
+      for (int base = 0; base < n; base += BATCH) {
+        const int j0 = base + threadIdx.x * R;
+        uint32_t x[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) x[r] = j0 + r < n ? key[j0 + r] : 0u;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          if (j0 + r < n && (x[r] & mask) == prefix) atomicAdd(&hist[wave][(x[r] >> shift) & 255u], 1);
       }
       __syncthreads();
-      if (threadIdx.x == 0) {
-        int cum = 0, bk = 255;
-        for (; bk > 0; --bk) {
-          if (cum + hist[bk] >= need) break;
-          cum += hist[bk];
+      // Per-bin totals, then suffix sums (keys with a bin >= b) by a shuffle
+      // scan in each of the first four waves; the one bin where the suffix
+      // reaches `need` is the k-th key's bin.
+      int cnt = 0, sfx = 0;
+      if (threadIdx.x < 256) {
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) cnt += hist[w][threadIdx.x];
+        sfx = cnt;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const int t = __shfl_down(sfx, d);
+          if (lane + d < 64) sfx += t;
         }
-        s_pick[0] = bk;
-        s_pick[1] = need - cum;
+        if (lane == 0) s_wave[wave] = sfx;  // total of this wave's 64 bins
+      }
+      __syncthreads();
+      if (threadIdx.x < 256) {
+        for (int w = wave + 1; w < 4; ++w) sfx += s_wave[w];
+        const int above = sfx - cnt;  // keys in higher bins
+        if (sfx >= need && above < need) {
+          s_pick[0] = threadIdx.x;
+          s_pick[1] = need - above;
+        }
       }
       __syncthreads();
       prefix |= static_cast<uint32_t>(s_pick[0]) << shift;
@@ -813,22 +844,39 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
       __syncthreads();
     }
   }
-  // Keep key > prefix, and the first `need` keys equal to prefix in index
-  // order (k >= n keeps everything).
-  int taken = 0, equal_seen = 0;
-  for (int j0 = 0; j0 < n; j0 += kTopkThreads) {
-    const int j = j0 + threadIdx.x;
-    const uint32_t x = j < n ? key[j] : 0u;
-    const bool in = j < n;
-    const bool eq = in && k < n && x == prefix;
-    int eq_tot;
-    const int eq_rank = block_excl_scan(eq, s_wave, &eq_tot);
-    const bool take = in && (k >= n || x > prefix || (eq && equal_seen + eq_rank < need));
-    int take_tot;
-    const int pos = block_excl_scan(take, s_wave, &take_tot);
-    if (take) out[taken + pos] = j;
-    taken += take_tot;
-    equal_seen += eq_tot;
+  // Keep every key > prefix and the first `need` keys equal to prefix in
+  // index order (k >= n keeps everything).  A kept key's output slot is the
+  // number of greater keys before it plus min(equal keys before it, need);
+  // both counts come from one scan of the packed per-thread counts.
+  int gt_seen = 0, eq_seen = 0;
+  for (int base = 0; base < n; base += BATCH) {
+    const int j0 = base + threadIdx.x * R;
+    uint32_t x[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) x[r] = j0 + r < n ? key[j0 + r] : 0u;
+    int gt_c = 0, eq_c = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const bool in = j0 + r < n;
+      gt_c += in && (k >= n || x[r] > prefix);
+      eq_c += in && k < n && x[r] == prefix;
+    }
+    int tot;
+    const int ex = block_excl_scan(gt_c | (eq_c << 16), s_wave, &tot);
+    int g = gt_seen + (ex & 0xffff), e = eq_seen + (ex >> 16);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const bool in = j0 + r < n;
+      if (in && (k >= n || x[r] > prefix)) {
+        out[g + min(e, need)] = j0 + r;
+        ++g;
+      } else if (in && k < n && x[r] == prefix) {
+        if (e < need) out[g + e] = j0 + r;
+        ++e;
+      }
+    }
+    gt_seen += tot & 0xffff;
+    eq_seen += tot >> 16;
   }
 }
 
