@@ -31,6 +31,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kNegInf = -__builtin_inff();
 
@@ -208,9 +210,41 @@ __device__ __forceinline__ float sum32(const f32x16 &x, const f32x16 &y) {
 
 // Direct global->LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4):
 // lane i writes bytes [16 i, 16 i + 16) after the wave-uniform LDS address
-// lds_dst.  Completion is tracked by vmcnt.
+// lds_dst (taken from M0).  Completion is tracked by vmcnt, and every caller
+// waits for it explicitly (s_waitcnt vmcnt(N) before the barrier that
+// publishes a tile).  Issued as asm so that the compiler does not add its
+// own wait for all outstanding LDS copies before each LDS read: it cannot
+// tell the stage being read from the stages still loading, and would
+// drain the prefetch.  The asm has no output registers; the LDS address
+// escapes through it, so reads of the tiles are not folded away.
 __device__ __forceinline__ void lds_dma16(const void *src, void *lds_dst) {
-  __builtin_amdgcn_global_load_lds(const_cast<void *>(src), lds_dst, 16, 0, 0);
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_dst)));
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0));
+}
+
+// Load of a per-call table entry (4, 16 or 32 bytes at a wave-uniform,
+// 4-byte aligned address; no kernel writes these tables) through the scalar
+// cache.  Written as asm because the compiler turns such reads into vector
+// loads once the kernel stores to global memory, and a vector load's wait
+// also waits for every tile load issued before it (vector loads complete in
+// issue order).  The asm waits for its own result; lgkmcnt also covers this
+// wave's outstanding LDS operations.
+template <typename T>
+__device__ __forceinline__ T sload(const T *p) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 16 || sizeof(T) == 32, "scalar table loads are 1, 4 or 8 dwords");
+  if constexpr (sizeof(T) == 32) {
+    i32x8 v;
+    asm volatile("s_load_dwordx8 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
+    return __builtin_bit_cast(T, v);
+  } else if constexpr (sizeof(T) == 16) {
+    i32x4 v;
+    asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
+    return __builtin_bit_cast(T, v);
+  } else {
+    int32_t v;
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
+    return __builtin_bit_cast(T, v);
+  }
 }
 
 // LDS layout of one prefill stage: the K tile (64 keys x D) and then the V^T
@@ -272,30 +306,38 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
   // Producer: global->LDS tile loads run up to two tiles ahead of the
   // consumer along the sequence of this workgroup's items, so the next
   // item's first tiles load while the current one finishes.
-  int p_item = cur, p_tile = a.items[cur].tile_begin;  // next tile to issue (p_item < 0: waiting for nxt)
-  int p_end = a.items[cur].tile_end;
-  SegDesc psg = a.segs[a.items[cur].seq * a.num_kv_heads + a.items[cur].kv_head];
+  int p_item = -1, p_tile = 0, p_end = 0;  // next tile to issue (p_item < 0: waiting for nxt)
+  SegDesc psg;
   auto p_set = [&](int idx) {  // point the producer at item idx (descriptors read once per item)
-    const PrefillItem pi_ = a.items[idx];
+    const PrefillItem pi_ = sload(a.items + idx);
     p_item = idx;
     p_tile = pi_.tile_begin;
     p_end = pi_.tile_end;
-    psg = a.segs[pi_.seq * a.num_kv_heads + pi_.kv_head];
+    psg = sload(a.segs + pi_.seq * a.num_kv_heads + pi_.kv_head);
   };
+  p_set(cur);
   int issued = 0, consumed = 0;                      // tiles issued / computed so far
   auto issue_tile = [&](int tile, int stage) {
     const int k0 = tile * kTileKeys;
     const int last_page = psg.n_pages - 1;
     char *st = smem + stage * L::STAGE_BYTES;
-    int uni_page = 0;
-    if constexpr (P == kTileKeys) {
-      const int pg = min(max((k0 - psg.first_token) / P, 0), last_page);
-      uni_page = a.page_ids[psg.page_off + pg];  // uniform: one page per tile
-    }
-    auto page_of = [&](int rel, int *slot) {
-      const int pg = rel >= 0 ? min(rel / P, last_page) : 0;
-      *slot = rel >= 0 && rel / P <= last_page ? rel % P : 0;
-      return a.page_ids[psg.page_off + pg];
+    // The tile's keys lie on NP whole pages (first_token is page aligned);
+    // their ids are uniform, read by scalar loads.  Keys before the first
+    // stored page or after the last one (never visible) read slot 0 of the
+    // nearest stored page.
+    constexpr int NP = kTileKeys / P;
+    int pid[NP];
+    const int pg0 = (k0 - psg.first_token) / P;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) pid[i] = sload(a.page_ids + psg.page_off + min(max(pg0 + i, 0), last_page));
+    auto page_of = [&](int key_in_tile, int *slot) {
+      const int rel = k0 + key_in_tile - psg.first_token;
+      *slot = rel >= 0 && rel / P <= last_page ? key_in_tile % P : 0;
+      int page = pid[0];
+#pragma unroll
+      for (int i = 1; i < NP; ++i)
+        if (key_in_tile / P == i) page = pid[i];
+      return page;
     };
 #pragma unroll
     for (int j = 0; j < K_INSTR; ++j) {
@@ -304,10 +346,10 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
       const int logical = (c % L::KCPR) ^ L::k_swz(row);
       const uint16_t *src;
       if constexpr (P == kTileKeys) {
-        src = a.k_pool + static_cast<size_t>(uni_page) * (P * D) + row * D + logical * 8;
+        src = a.k_pool + static_cast<size_t>(pid[0]) * (P * D) + row * D + logical * 8;
       } else {
         int slot;
-        const int page = page_of(k0 + row - psg.first_token, &slot);
+        const int page = page_of(row, &slot);
         src = a.k_pool + (static_cast<size_t>(page) * P + slot) * D + logical * 8;
       }
       lds_dma16(src, st + (j * NW + wave) * 1024);
@@ -319,10 +361,10 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
       const int logical = (c % 8) ^ L::v_swz(d);
       const uint16_t *src;
       if constexpr (P == kTileKeys) {
-        src = a.v_pool + static_cast<size_t>(uni_page) * (P * D) + d * P + logical * 8;
+        src = a.v_pool + static_cast<size_t>(pid[0]) * (P * D) + d * P + logical * 8;
       } else {
         int slot;
-        const int page = page_of(k0 + logical * 8 - psg.first_token, &slot);
+        const int page = page_of(logical * 8, &slot);
         src = a.v_pool + static_cast<size_t>(page) * (P * D) + d * P + slot;
       }
       lds_dma16(src, st + L::K_CHUNKS * 16 + (j * NW + wave) * 1024);
@@ -340,27 +382,31 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
       }
     }
   };
-  // Wait until the newest `pending` issued tiles are the only loads in flight.
-  auto wait_pending = [&](int pending) {
+  // Workgroup barrier that leaves the newest `pending` issued tiles' loads
+  // in flight: this wave's LDS operations and older tile loads complete
+  // first.  (__syncthreads would wait for every outstanding global load,
+  // the prefetched tiles included.)  Other vector memory operations that
+  // are still outstanding only make the wait longer, never shorter, since
+  // loads complete in issue order.
+  auto sync_tiles = [&](int pending) {
     if (pending >= 2)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LOADS_PER_TILE) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * LOADS_PER_TILE) : "memory");
     else if (pending == 1)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS_PER_TILE) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LOADS_PER_TILE) : "memory");
     else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
 
   produce(2);
-  wait_pending(issued - 1);
-  __syncthreads();
+  sync_tiles(issued - 1);
 
   const int key_a0 = st_row_key(col);  // K row this lane feeds to block 0 (block 1: +32)
   const int vrow_swz = L::v_swz(col);  // V^T rows db*32 + col share it
 
   while (true) {
-    const PrefillItem it = a.items[cur];
-    const SeqDesc sd = a.seqs[it.seq];
-    const SegDesc sg = a.segs[it.seq * a.num_kv_heads + it.kv_head];
+    const PrefillItem it = sload(a.items + cur);
+    const SeqDesc sd = sload(a.seqs + it.seq);
+    const SegDesc sg = sload(a.segs + it.seq * a.num_kv_heads + it.kv_head);
     const int h = it.kv_head * G + (r - pos_off * G);
     const int t0 = it.qtile * rows;
     const int t_last = min(t0 + rows, sd.q_len) - 1;  // last valid query of the tile
@@ -393,6 +439,11 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
           qv[kk] = as_bf16x8(x);
         }
       }
+      // Wait for Q here, once per item; the tile loop then carries no wait
+      // on it (the compiler cannot prove the load done inside the loop and
+      // would drain every prefetched tile before each product).
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+v"(qv[kk]));
     }
 
     f32x16 oacc[NDB];
@@ -473,8 +524,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
       if (tile == fetch_tile && tid == 0) s_next[fslot] = atomicAdd(a.counter, 1);
       if (issued <= consumed) {  // the producer fell behind (short items): load this tile now
         produce(consumed + 1);
-        wait_pending(issued - consumed - 1);
-        __syncthreads();
+        sync_tiles(issued - consumed - 1);
       }
       produce(consumed + 3);
       const char *st = smem + (consumed % NSTAGE) * L::STAGE_BYTES;
@@ -487,8 +537,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
         else
           process(st, k0, std::integral_constant<bool, true>{});
       }
-      wait_pending(issued - consumed - 2);
-      __syncthreads();
+      sync_tiles(issued - consumed - 2);
       ++consumed;
       if (tile == fetch_tile) {  // the index fetched in this iteration is visible after its barrier
         nxt = __builtin_amdgcn_readfirstlane(s_next[fslot]);
