@@ -121,12 +121,29 @@ __global__ __launch_bounds__(kScatterThreads) void scatter_kernel(ScatterArgs a)
     }
   }
 
-  // K rows, and V rows staged in LDS for the transpose.
-  for (int c = tid; c < n_rows * CPR; c += kScatterThreads) {
-    const int row = c / CPR, dc = c - row * CPR;
-    const size_t src = (static_cast<size_t>(it.src_row + row) * a.num_kv_heads + it.kv_head) * D + dc * 8;
-    *reinterpret_cast<u32x4 *>(kpage + static_cast<size_t>(it.slot_begin + row) * D + dc * 8) = ld16(a.k_new + src);
-    *reinterpret_cast<u32x4 *>(sv + (it.slot_begin + row) * D + dc * 8) = ld16(a.v_new + src);
+  // K rows, and V rows staged in LDS for the transpose.  All of a thread's
+  // loads are issued before any store (the pools and the new rows may
+  // alias as far as the compiler knows, so it would not batch them).
+  constexpr int ITER = (P * CPR + kScatterThreads - 1) / kScatterThreads;
+  u32x4 kx[ITER], vx[ITER];
+#pragma unroll
+  for (int i = 0; i < ITER; ++i) {
+    const int c = tid + i * kScatterThreads;
+    if (c < n_rows * CPR) {
+      const int row = c / CPR, dc = c - row * CPR;
+      const size_t src = (static_cast<size_t>(it.src_row + row) * a.num_kv_heads + it.kv_head) * D + dc * 8;
+      kx[i] = ld16(a.k_new + src);
+      vx[i] = ld16(a.v_new + src);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < ITER; ++i) {
+    const int c = tid + i * kScatterThreads;
+    if (c < n_rows * CPR) {
+      const int row = c / CPR, dc = c - row * CPR;
+      *reinterpret_cast<u32x4 *>(kpage + static_cast<size_t>(it.slot_begin + row) * D + dc * 8) = kx[i];
+      *reinterpret_cast<u32x4 *>(sv + (it.slot_begin + row) * D + dc * 8) = vx[i];
+    }
   }
   if (it.zero_tail) {
     const u32x4 z = {0u, 0u, 0u, 0u};
@@ -137,17 +154,28 @@ __global__ __launch_bounds__(kScatterThreads) void scatter_kernel(ScatterArgs a)
     }
   }
   __syncthreads();
-  // V^T rows: channel d holds slots [slot_begin, wend) contiguously.
+  // V^T rows: channel d holds slots [slot_begin, wend) contiguously.  A
+  // lane takes a channel pair and 8 consecutive slots: one 4-byte LDS read
+  // per slot (consecutive lanes read consecutive words: no bank conflict)
+  // and two 16-byte stores.
   const int wend = it.zero_tail ? P : it.slot_end;
   const int n = wend - it.slot_begin;
   if ((it.slot_begin & 7) == 0 && (n & 7) == 0) {
-    const int cpr = n / 8;
-    for (int c = tid; c < D * cpr; c += kScatterThreads) {
-      const int d = c / cpr, s0 = it.slot_begin + (c - d * cpr) * 8;
-      uint16_t tmp[8];
+    constexpr int NPAIR = D / 2;
+    const int groups = n / 8;
+    for (int c = tid; c < NPAIR * groups; c += kScatterThreads) {
+      const int dp = c % NPAIR, s0 = it.slot_begin + (c / NPAIR) * 8;
+      uint32_t w[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) tmp[e] = sv[(s0 + e) * D + d];
-      *reinterpret_cast<u32x4 *>(vpage + static_cast<size_t>(d) * P + s0) = *reinterpret_cast<const u32x4 *>(tmp);
+      for (int e = 0; e < 8; ++e) w[e] = *reinterpret_cast<const uint32_t *>(sv + (s0 + e) * D + 2 * dp);
+      u32x4 lo, hi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lo[e] = (w[2 * e] & 0xffffu) | (w[2 * e + 1] << 16);
+        hi[e] = (w[2 * e] >> 16) | (w[2 * e + 1] & 0xffff0000u);
+      }
+      *reinterpret_cast<u32x4 *>(vpage + static_cast<size_t>(2 * dp) * P + s0) = lo;
+      *reinterpret_cast<u32x4 *>(vpage + static_cast<size_t>(2 * dp + 1) * P + s0) = hi;
     }
   } else {
     for (int c = tid; c < D * n; c += kScatterThreads) {
