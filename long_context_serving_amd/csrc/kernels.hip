@@ -450,21 +450,23 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
     // Q^T operand, held in registers for the whole item.
     bf16x8 qv[NKK];
     {
-      const uint16_t *qrow = a.q + (static_cast<size_t>(sd.q_start + t) * a.num_q_heads + h) * D;
+      // Loads are unconditional (an invalid row reads the tile's last valid
+      // row and is zeroed afterwards), so they are in flight together.
+      const uint16_t *qrow = a.q + (static_cast<size_t>(sd.q_start + min(t, t_last)) * a.num_q_heads + h) * D;
       if (sg.rope_off < 0) {
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-          u32x4 x = {0u, 0u, 0u, 0u};
-          if (valid) x = ld16(qrow + kk * 16 + half * 8);
-          qv[kk] = as_bf16x8(x);
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          const u32x4 x = ld16(qrow + kk * 16 + half * 8);
+          qv[kk] = as_bf16x8(valid ? x : z);
         }
       } else {
         const float *tab = a.rope.tables + sg.rope_off;
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-          u32x4 x = {0u, 0u, 0u, 0u};
-          if (valid) x = relocate_chunk<D>(qrow, kk * 16 + half * 8, tab, a.rope);
-          qv[kk] = as_bf16x8(x);
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          const u32x4 x = relocate_chunk<D>(qrow, kk * 16 + half * 8, tab, a.rope);
+          qv[kk] = as_bf16x8(valid ? x : z);
         }
       }
       // Wait for Q here, once per item; the tile loop then carries no wait
@@ -644,9 +646,9 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void score_kernel(ScoreArgs a) 
   __shared__ float sx[2][NW][kTileKeys];
   char *smem = reinterpret_cast<char *>(smem4);
 
-  const PrefillItem it = a.items[blockIdx.x];
-  const SeqDesc sd = a.seqs[it.seq];
-  const SegDesc sg = a.segs[it.seq * a.num_kv_heads + it.kv_head];
+  const PrefillItem it = sload(a.items + blockIdx.x);
+  const SeqDesc sd = sload(a.seqs + it.seq);
+  const SegDesc sg = sload(a.segs + it.seq * a.num_kv_heads + it.kv_head);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
@@ -667,21 +669,23 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void score_kernel(ScoreArgs a) 
     const int h = it.kv_head * G + (r - po * G);
     const int t = t0 + po;
     const bool valid = po < rows && t < sd.q_len;
-    const uint16_t *qrow = a.q + (static_cast<size_t>(sd.q_start + t) * a.num_q_heads + h) * D;
+    // Loads are unconditional (an invalid row reads the tile's last valid
+    // row and is zeroed afterwards), so they are in flight together.
+    const uint16_t *qrow = a.q + (static_cast<size_t>(sd.q_start + min(t, t_last)) * a.num_q_heads + h) * D;
     if (sg.rope_off < 0) {
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (valid) x = ld16(qrow + kk * 16 + half * 8);
-        qv[kk] = as_bf16x8(x);
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        const u32x4 x = ld16(qrow + kk * 16 + half * 8);
+        qv[kk] = as_bf16x8(valid ? x : z);
       }
     } else {
       const float *tab = a.rope.tables + sg.rope_off;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (valid) x = relocate_chunk<D>(qrow, kk * 16 + half * 8, tab, a.rope);
-        qv[kk] = as_bf16x8(x);
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        const u32x4 x = relocate_chunk<D>(qrow, kk * 16 + half * 8, tab, a.rope);
+        qv[kk] = as_bf16x8(valid ? x : z);
       }
     }
   }
@@ -695,20 +699,32 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void score_kernel(ScoreArgs a) 
     const int po = r / G;
     const int t = t0 + po;
     const bool valid = po < rows && t < sd.q_len;
-    lse2[v] = valid ? a.lse[static_cast<size_t>(sd.q_start + t) * a.num_q_heads + it.kv_head * G + (r - po * G)] * kLog2e
-                    : __builtin_inff();
+    // Unconditional load (an invalid row reads the tile's last valid row),
+    // so the 16 loads are in flight together.
+    const float raw = a.lse[static_cast<size_t>(sd.q_start + min(t, t_last)) * a.num_q_heads + it.kv_head * G +
+                            (r - po * G)];
+    lse2[v] = valid ? raw * kLog2e : __builtin_inff();
     prow[v] = base + min(t, t_last);
   }
+  // Wait for Q and the LSE values once, here; inside the tile loop the
+  // compiler would otherwise wait for every outstanding load (the
+  // prefetched tiles included) before their first use in each tile.
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+v"(qv[kk]));
+#pragma unroll
+  for (int v = 0; v < 16; ++v) asm volatile("" : "+v"(lse2[v]));
 
   const int last_page = sg.n_pages - 1;
   auto issue_tile = [&](int tile, int stage) {
     const int k0 = tile * kTileKeys;
     char *st = smem + stage * KSTAGE;
-    int uni_page = 0;
-    if constexpr (P == kTileKeys) {
-      const int pi = min(max((k0 - sg.first_token) / P, 0), last_page);
-      uni_page = a.page_ids[sg.page_off + pi];
-    }
+    // Page ids of the tile's NP whole pages by scalar loads (as in the
+    // prefill); keys outside the stored pages read slot 0 of the nearest.
+    constexpr int NP = kTileKeys / P;
+    int pid[NP];
+    const int pg0 = (k0 - sg.first_token) / P;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) pid[i] = sload(a.page_ids + sg.page_off + min(max(pg0 + i, 0), last_page));
 #pragma unroll
     for (int j = 0; j < K_INSTR; ++j) {
       const int c = (j * NW + wave) * 64 + lane;
@@ -716,12 +732,15 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void score_kernel(ScoreArgs a) 
       const int logical = (c % L::KCPR) ^ L::k_swz(row);
       const uint16_t *src;
       if constexpr (P == kTileKeys) {
-        src = a.k_pool + static_cast<size_t>(uni_page) * (P * D) + row * D + logical * 8;
+        src = a.k_pool + static_cast<size_t>(pid[0]) * (P * D) + row * D + logical * 8;
       } else {
         const int rel = k0 + row - sg.first_token;
-        const int pi = rel >= 0 ? min(rel / P, last_page) : 0;
-        const int slot = rel >= 0 && rel / P <= last_page ? rel % P : 0;
-        src = a.k_pool + (static_cast<size_t>(a.page_ids[sg.page_off + pi]) * P + slot) * D + logical * 8;
+        const int slot = rel >= 0 && rel / P <= last_page ? row % P : 0;
+        int page = pid[0];
+#pragma unroll
+        for (int i = 1; i < NP; ++i)
+          if (row / P == i) page = pid[i];
+        src = a.k_pool + (static_cast<size_t>(page) * P + slot) * D + logical * 8;
       }
       lds_dma16(src, st + (j * NW + wave) * 1024);
     }
@@ -771,14 +790,14 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void score_kernel(ScoreArgs a) 
 
   constexpr int LOADS_PER_TILE = K_INSTR;
   const int tb = it.tile_begin, te = it.tile_end;
+  // Barriers leave the newest tile's loads in flight (see the prefill).
   if (tb < te) issue_tile(tb, 0);
   if (tb + 1 < te) {
     issue_tile(tb + 1, 1);
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS_PER_TILE) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LOADS_PER_TILE) : "memory");
   } else {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
-  __syncthreads();
   for (int tile = tb; tile < te; ++tile) {
     const int i = tile - tb;
     const bool ahead2 = tile + 2 < te;
@@ -797,10 +816,9 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void score_kernel(ScoreArgs a) 
     }
     sx[i & 1][wave][half * 32 + col] = half ? c1 : c0;
     if (ahead2)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS_PER_TILE) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LOADS_PER_TILE) : "memory");
     else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
   if (te > tb) flush(te - tb - 1);
 }
@@ -1030,21 +1048,24 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
 
       bf16x8 qv[NKK];
       {
-        const uint16_t *qrow = a.q + (static_cast<size_t>(sd.q_start) * a.num_q_heads + it.kv_head * G + c16) * D;
+        // Unconditional loads (lanes past the group read its last head and
+        // are zeroed), so they are in flight together.
+        const uint16_t *qrow =
+            a.q + (static_cast<size_t>(sd.q_start) * a.num_q_heads + it.kv_head * G + min(c16, G - 1)) * D;
         if (sg.rope_off < 0) {
 #pragma unroll
           for (int kk = 0; kk < NKK; ++kk) {
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (c16 < G) x = ld16(qrow + kk * 32 + u * 8);
-            qv[kk] = as_bf16x8(x);
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            const u32x4 x = ld16(qrow + kk * 32 + u * 8);
+            qv[kk] = as_bf16x8(c16 < G ? x : z);
           }
         } else {
           const float *tab = a.rope.tables + sg.rope_off;
 #pragma unroll
           for (int kk = 0; kk < NKK; ++kk) {
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (c16 < G) x = relocate_chunk<D>(qrow, kk * 32 + u * 8, tab, a.rope);
-            qv[kk] = as_bf16x8(x);
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            const u32x4 x = relocate_chunk<D>(qrow, kk * 32 + u * 8, tab, a.rope);
+            qv[kk] = as_bf16x8(c16 < G ? x : z);
           }
         }
       }
