@@ -486,14 +486,33 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
     auto process = [&](const char *st, int k0, auto mask_tag) {
       constexpr bool MASK = decltype(mask_tag)::value;
       f32x16 s0 = f32x16{}, s1 = f32x16{};
+      // K operands stream two k-steps ahead of the products (scheduling
+      // fences keep the compiler from loading all of them up front).
+      bf16x8 kr[NKK][2];
+      auto kread = [&](int kk) {
+        const int c = (2 * kk + half) ^ L::k_swz(key_a0);
+        kr[kk][0] = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + (key_a0 * L::KCPR + c) * 16));
+        kr[kk][1] = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + ((key_a0 + 32) * L::KCPR + c) * 16));
+      };
+      kread(0);
+      kread(1);
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        const int c = (2 * kk + half) ^ L::k_swz(key_a0);
-        const bf16x8 ka0 = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + (key_a0 * L::KCPR + c) * 16));
-        const bf16x8 ka1 = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + ((key_a0 + 32) * L::KCPR + c) * 16));
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0, qv[kk], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qv[kk], s1, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[kk][0], qv[kk], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[kk][1], qv[kk], s1, 0, 0, 0);
+        if (kk + 2 < NKK) kread(kk + 2);
       }
+      // V^T operands of the first 32 keys, read now so that their latency
+      // is hidden behind the softmax.
+      bf16x8 vpre[2][NDB];
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          vpre[sh][db] = as_bf16x8(*reinterpret_cast<const u32x4 *>(
+              st + ((L::K_CHUNKS + (db * 32 + col) * 8) + ((sh * 2 + half) ^ vrow_swz)) * 16));
+      __builtin_amdgcn_sched_barrier(0);
       if constexpr (MASK) {
         // key = k0 + 16 (v/8) + 8 half + v%8 (+32 for block 1); visible iff
         // vis_lo <= key <= p, tested as one unsigned range compare.
@@ -539,7 +558,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
           const int c = (kb * 4 + s * 2 + half) ^ vrow_swz;
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
-            const bf16x8 va =
+            const bf16x8 va = kb == 0 ? vpre[s][db] :
                 as_bf16x8(*reinterpret_cast<const u32x4 *>(st + ((L::K_CHUNKS + (db * 32 + col) * 8) + c) * 16));
             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[db], 0, 0, 0);
           }
