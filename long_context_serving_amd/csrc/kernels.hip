@@ -771,14 +771,24 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void score_kernel(ScoreArgs a) 
   auto process = [&](const char *st, int k0, auto mask_tag, float &c0, float &c1) {
     constexpr bool MASK = decltype(mask_tag)::value;
     f32x16 s0 = f32x16{}, s1 = f32x16{};
+    // K operands stream two k-steps ahead of the products (scheduling
+    // fences keep the compiler from loading all of them up front).
+    bf16x8 kr[NKK][2];
+    auto kread = [&](int kk) {
+      const int c = (2 * kk + half) ^ kswz;
+      kr[kk][0] = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + (col * L::KCPR + c) * 16));
+      kr[kk][1] = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + ((col + 32) * L::KCPR + c) * 16));
+    };
+    kread(0);
+    kread(1);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      const int c = (2 * kk + half) ^ kswz;
-      const bf16x8 kb0 = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + (col * L::KCPR + c) * 16));
-      const bf16x8 kb1 = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + ((col + 32) * L::KCPR + c) * 16));
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qv[kk], kb0, s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qv[kk], kb1, s1, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qv[kk], kr[kk][0], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qv[kk], kr[kk][1], s1, 0, 0, 0);
+      if (kk + 2 < NKK) kread(kk + 2);
     }
+    __builtin_amdgcn_sched_barrier(0);
     float e0 = 0.f, e1 = 0.f;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
