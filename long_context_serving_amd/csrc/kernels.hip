@@ -69,29 +69,61 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast
 // ("RedKnot-MLA: Multi-Head Offline-Online Reuse for DeepSeek-V4 Long-Context
 // Serving" review, "Summary"): channel c becomes cos[c] q[c] + ssin[c]
 // q[partner(c)] in fp32 (tab = cos[D] then signed sin[D] of the segment's
-// offset), rounded once to bf16.  ch0 is a multiple of 8.
+// offset), rounded once to bf16.  ch0 is a multiple of 8.  Split into the
+// loads and the arithmetic so that callers can put several chunks' loads
+// in flight before the first rotation.
+struct RelocIn {
+  u32x4 x, y;         // the chunk and its partner chunk (bf16 pairs)
+  f32x4 c0, c1, s0, s1;  // cos and signed sin of its 8 channels
+};
+
 template <int D>
-__device__ __forceinline__ u32x4 relocate_chunk(const uint16_t *qrow, int ch0, const float *tab, const RopeArgs &r) {
-  const u32x4 x = ld16(qrow + ch0);
+__device__ __forceinline__ RelocIn reloc_load(const uint16_t *qrow, int ch0, const float *tab, const RopeArgs &r) {
+  RelocIn in;
+  in.x = ld16(qrow + ch0);
   int pc = ch0;
   if (r.style == 0 && ch0 >= r.lo) pc = ch0 - r.lo < r.half ? ch0 + r.half : ch0 - r.half;
-  const u32x4 y = ld16(qrow + pc);
-  const f32x4 c0 = *reinterpret_cast<const f32x4 *>(tab + ch0);
-  const f32x4 c1 = *reinterpret_cast<const f32x4 *>(tab + ch0 + 4);
-  const f32x4 s0 = *reinterpret_cast<const f32x4 *>(tab + D + ch0);
-  const f32x4 s1 = *reinterpret_cast<const f32x4 *>(tab + D + ch0 + 4);
-  const float cs[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-  const float sn[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+  in.y = ld16(qrow + pc);
+  in.c0 = *reinterpret_cast<const f32x4 *>(tab + ch0);
+  in.c1 = *reinterpret_cast<const f32x4 *>(tab + ch0 + 4);
+  in.s0 = *reinterpret_cast<const f32x4 *>(tab + D + ch0);
+  in.s1 = *reinterpret_cast<const f32x4 *>(tab + D + ch0 + 4);
+  return in;
+}
+
+__device__ __forceinline__ u32x4 reloc_apply(const RelocIn &in, const RopeArgs &r) {
+  const float cs[8] = {in.c0[0], in.c0[1], in.c0[2], in.c0[3], in.c1[0], in.c1[1], in.c1[2], in.c1[3]};
+  const float sn[8] = {in.s0[0], in.s0[1], in.s0[2], in.s0[3], in.s1[0], in.s1[1], in.s1[2], in.s1[3]};
   float out[8];
   const bool swap = r.style == 1;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    const float xl = bf16_lo(x[w]), xh = bf16_hi(x[w]);
-    const float yl = bf16_lo(y[w]), yh = bf16_hi(y[w]);
+    const float xl = bf16_lo(in.x[w]), xh = bf16_hi(in.x[w]);
+    const float yl = bf16_lo(in.y[w]), yh = bf16_hi(in.y[w]);
     out[2 * w] = cs[2 * w] * xl + sn[2 * w] * (swap ? yh : yl);
     out[2 * w + 1] = cs[2 * w + 1] * xh + sn[2 * w + 1] * (swap ? yl : yh);
   }
   return __builtin_bit_cast(u32x4, pack8_bf16(out[0], out[1], out[2], out[3], out[4], out[5], out[6], out[7]));
+}
+
+// Relocated Q operand chunks kk = 0 .. NKK-1 of one row (chunk kk starts at
+// channel kk * step + off), four chunks' loads in flight at a time; rows
+// that are not valid get zeros.
+template <int D, int NKK>
+__device__ __forceinline__ void relocate_row(bf16x8 (&qv)[NKK], const uint16_t *qrow, int step, int off, bool valid,
+                                             const float *tab, const RopeArgs &r) {
+  constexpr int B = NKK < 4 ? NKK : 4;
+  static_assert(NKK % B == 0, "chunk batches");
+  const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int k0 = 0; k0 < NKK; k0 += B) {
+    RelocIn in[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j) in[j] = reloc_load<D>(qrow, (k0 + j) * step + off, tab, r);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < B; ++j) qv[k0 + j] = as_bf16x8(valid ? reloc_apply(in[j], r) : z);
+  }
 }
 
 // ===========================================================================
@@ -461,13 +493,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
           qv[kk] = as_bf16x8(valid ? x : z);
         }
       } else {
-        const float *tab = a.rope.tables + sg.rope_off;
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          const u32x4 z = {0u, 0u, 0u, 0u};
-          const u32x4 x = relocate_chunk<D>(qrow, kk * 16 + half * 8, tab, a.rope);
-          qv[kk] = as_bf16x8(valid ? x : z);
-        }
+        relocate_row<D, NKK>(qv, qrow, 16, half * 8, valid, a.rope.tables + sg.rope_off, a.rope);
       }
       // Wait for Q here, once per item; the tile loop then carries no wait
       // on it (the compiler cannot prove the load done inside the loop and
@@ -699,13 +725,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void score_kernel(ScoreArgs a) 
         qv[kk] = as_bf16x8(valid ? x : z);
       }
     } else {
-      const float *tab = a.rope.tables + sg.rope_off;
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        const u32x4 x = relocate_chunk<D>(qrow, kk * 16 + half * 8, tab, a.rope);
-        qv[kk] = as_bf16x8(valid ? x : z);
-      }
+      relocate_row<D, NKK>(qv, qrow, 16, half * 8, valid, a.rope.tables + sg.rope_off, a.rope);
     }
   }
   // The rows of S this lane holds: register v is row 8 (v/4) + 4 half + v%4
@@ -1089,13 +1109,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
             qv[kk] = as_bf16x8(c16 < G ? x : z);
           }
         } else {
-          const float *tab = a.rope.tables + sg.rope_off;
-#pragma unroll
-          for (int kk = 0; kk < NKK; ++kk) {
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            const u32x4 x = relocate_chunk<D>(qrow, kk * 32 + u * 8, tab, a.rope);
-            qv[kk] = as_bf16x8(c16 < G ? x : z);
-          }
+          relocate_row<D, NKK>(qv, qrow, 32, u * 8, c16 < G, a.rope.tables + sg.rope_off, a.rope);
         }
       }
 
