@@ -69,27 +69,13 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast
 // ("RedKnot-MLA: Multi-Head Offline-Online Reuse for DeepSeek-V4 Long-Context
 // Serving" review, "Summary"): channel c becomes cos[c] q[c] + ssin[c]
 // q[partner(c)] in fp32 (tab = cos[D] then signed sin[D] of the segment's
-// offset), rounded once to bf16.  ch0 is a multiple of 8.  Split into the
-// loads and the arithmetic so that callers can put several chunks' loads
-// in flight before the first rotation.
+// offset), rounded once to bf16.  ch0 is a multiple of 8.  The loaded data
+// and the arithmetic are kept apart so that several chunks' loads can be in
+// flight before the first rotation.
 struct RelocIn {
   u32x4 x, y;         // the chunk and its partner chunk (bf16 pairs)
   f32x4 c0, c1, s0, s1;  // cos and signed sin of its 8 channels
 };
-
-template <int D>
-__device__ __forceinline__ RelocIn reloc_load(const uint16_t *qrow, int ch0, const float *tab, const RopeArgs &r) {
-  RelocIn in;
-  in.x = ld16(qrow + ch0);
-  int pc = ch0;
-  if (r.style == 0 && ch0 >= r.lo) pc = ch0 - r.lo < r.half ? ch0 + r.half : ch0 - r.half;
-  in.y = ld16(qrow + pc);
-  in.c0 = *reinterpret_cast<const f32x4 *>(tab + ch0);
-  in.c1 = *reinterpret_cast<const f32x4 *>(tab + ch0 + 4);
-  in.s0 = *reinterpret_cast<const f32x4 *>(tab + D + ch0);
-  in.s1 = *reinterpret_cast<const f32x4 *>(tab + D + ch0 + 4);
-  return in;
-}
 
 __device__ __forceinline__ u32x4 reloc_apply(const RelocIn &in, const RopeArgs &r) {
   const float cs[8] = {in.c0[0], in.c0[1], in.c0[2], in.c0[3], in.c1[0], in.c1[1], in.c1[2], in.c1[3]};
@@ -107,19 +93,37 @@ __device__ __forceinline__ u32x4 reloc_apply(const RelocIn &in, const RopeArgs &
 }
 
 // Relocated Q operand chunks kk = 0 .. NKK-1 of one row (chunk kk starts at
-// channel kk * step + off), four chunks' loads in flight at a time; rows
-// that are not valid get zeros.
+// channel kk * step + off); rows that are not valid get zeros.  The
+// segment's cos/sin table is first copied into this wave's LDS (wtab, 2 * D
+// floats; one coalesced 16-byte load per lane): every lane of a wave reads
+// the same few table entries, which as vector loads from memory would be
+// processed lane by lane, but as LDS reads are broadcasts.  A wave's own LDS
+// operations complete in order, so no barrier is needed.  Four chunks' loads
+// are in flight before the first rotation.
 template <int D, int NKK>
 __device__ __forceinline__ void relocate_row(bf16x8 (&qv)[NKK], const uint16_t *qrow, int step, int off, bool valid,
-                                             const float *tab, const RopeArgs &r) {
+                                             const float *tab, float *wtab, const RopeArgs &r) {
   constexpr int B = NKK < 4 ? NKK : 4;
   static_assert(NKK % B == 0, "chunk batches");
+  const int lane = threadIdx.x & 63;
+  for (int i = lane; i < D / 2; i += 64)
+    *reinterpret_cast<f32x4 *>(wtab + 4 * i) = *reinterpret_cast<const f32x4 *>(tab + 4 * i);
   const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int k0 = 0; k0 < NKK; k0 += B) {
     RelocIn in[B];
 #pragma unroll
-    for (int j = 0; j < B; ++j) in[j] = reloc_load<D>(qrow, (k0 + j) * step + off, tab, r);
+    for (int j = 0; j < B; ++j) {
+      const int ch0 = (k0 + j) * step + off;
+      int pc = ch0;
+      if (r.style == 0 && ch0 >= r.lo) pc = ch0 - r.lo < r.half ? ch0 + r.half : ch0 - r.half;
+      in[j].x = ld16(qrow + ch0);
+      in[j].y = ld16(qrow + pc);
+      in[j].c0 = *reinterpret_cast<const f32x4 *>(wtab + ch0);
+      in[j].c1 = *reinterpret_cast<const f32x4 *>(wtab + ch0 + 4);
+      in[j].s0 = *reinterpret_cast<const f32x4 *>(wtab + D + ch0);
+      in[j].s1 = *reinterpret_cast<const f32x4 *>(wtab + D + ch0 + 4);
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < B; ++j) qv[k0 + j] = as_bf16x8(valid ? reloc_apply(in[j], r) : z);
@@ -340,6 +344,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
   static_assert(K_INSTR >= 1 && V_INSTR >= 1, "tile smaller than one load per lane");
   __shared__ __attribute__((aligned(16))) uint4 smem4[NSTAGE * L::STAGE_BYTES / 16];
   __shared__ int s_next[2];  // item indices fetched by thread 0; consecutive fetches alternate slots
+  __shared__ __attribute__((aligned(16))) float s_rope[NW][2 * D];  // per-wave relocation table
   char *smem = reinterpret_cast<char *>(smem4);
 
   const int tid = threadIdx.x;
@@ -493,7 +498,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
           qv[kk] = as_bf16x8(valid ? x : z);
         }
       } else {
-        relocate_row<D, NKK>(qv, qrow, 16, half * 8, valid, a.rope.tables + sg.rope_off, a.rope);
+        relocate_row<D, NKK>(qv, qrow, 16, half * 8, valid, a.rope.tables + sg.rope_off, s_rope[wave], a.rope);
       }
       // Wait for Q here, once per item; the tile loop then carries no wait
       // on it (the compiler cannot prove the load done inside the loop and
@@ -689,6 +694,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void score_kernel(ScoreArgs a) 
   static_assert(kPrefillRows == 32 * NW && K_INSTR >= 1, "tile layout");
   __shared__ __attribute__((aligned(16))) uint4 smem4[NSTAGE * KSTAGE / 16];
   __shared__ float sx[2][NW][kTileKeys];
+  __shared__ __attribute__((aligned(16))) float s_rope[NW][2 * D];  // per-wave relocation table
   char *smem = reinterpret_cast<char *>(smem4);
 
   const PrefillItem it = sload(a.items + blockIdx.x);
@@ -725,7 +731,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void score_kernel(ScoreArgs a) 
         qv[kk] = as_bf16x8(valid ? x : z);
       }
     } else {
-      relocate_row<D, NKK>(qv, qrow, 16, half * 8, valid, a.rope.tables + sg.rope_off, a.rope);
+      relocate_row<D, NKK>(qv, qrow, 16, half * 8, valid, a.rope.tables + sg.rope_off, s_rope[wave], a.rope);
     }
   }
   // The rows of S this lane holds: register v is row 8 (v/4) + 4 half + v%4
@@ -1058,6 +1064,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
   __shared__ float s_m[NSLOT][kDecodeCols];
   __shared__ float s_l[NSLOT][kDecodeCols];
   __shared__ __attribute__((aligned(16))) float s_o[NSLOT][kDecodeCols][D];
+  __shared__ __attribute__((aligned(16))) float s_rope[NW][2 * D];  // per-wave relocation table
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1109,7 +1116,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
             qv[kk] = as_bf16x8(c16 < G ? x : z);
           }
         } else {
-          relocate_row<D, NKK>(qv, qrow, 32, u * 8, c16 < G, a.rope.tables + sg.rope_off, a.rope);
+          relocate_row<D, NKK>(qv, qrow, 32, u * 8, c16 < G, a.rope.tables + sg.rope_off, s_rope[wave], a.rope);
         }
       }
 
