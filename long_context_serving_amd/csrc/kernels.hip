@@ -294,8 +294,14 @@ __device__ __forceinline__ void lds_dma16(const void *src, void *lds_dst) {
 // issue order).  The asm waits for its own result; lgkmcnt also covers this
 // wave's outstanding LDS operations.
 template <typename T>
-__device__ __forceinline__ T sload(const T *p) {
+__device__ __forceinline__ T sload(const T *q) {
   static_assert(sizeof(T) == 4 || sizeof(T) == 16 || sizeof(T) == 32, "scalar table loads are 1, 4 or 8 dwords");
+  // The address is wave-uniform at every call; reading it from the first
+  // lane lets it sit in SGPRs even where the compiler cannot prove that.
+  const uint64_t a = reinterpret_cast<uint64_t>(q);
+  const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a)));
+  const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32)));
+  const T *p = reinterpret_cast<const T *>(lo | (hi << 32));
   if constexpr (sizeof(T) == 32) {
     i32x8 v;
     asm volatile("s_load_dwordx8 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
