@@ -27,7 +27,7 @@ constexpr int kMergeThreads = 256;
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkRun = 8;  // consecutive keys per thread per batch
 constexpr int kMergeUnroll = 4;    // (row, head) pairs in flight per lane of the merge kernel
-constexpr int kPrefillWgPerCu = 1;  // resident prefill workgroups per CU (96 KiB of LDS each): the persistent grid
+constexpr int kPrefillWgPerCu = 1;  // resident prefill workgroups per CU (104 KiB of LDS each at D = 128): the persistent grid
 constexpr int kDecodeWgPerCu = 1;   // resident decode workgroups per CU (the stream-K grid size)
 constexpr int kXcds = 8;           // MI355X: workgroup i of a launch runs on XCD i % 8
 
