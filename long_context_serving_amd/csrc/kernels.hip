@@ -953,6 +953,20 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   int32_t *out = a.out + a.out_off[b];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (k <= 0) return;
+  // A sequence of at most BATCH keys is loaded once and kept in registers
+  // for every pass; longer ones are read again in each pass.
+  const bool one = n <= BATCH;
+  uint32_t xk[R];
+  if (one) {
+    const int j0 = threadIdx.x * R;
+#pragma unroll
+    for (int r = 0; r < R; ++r) xk[r] = j0 + r < n ? key[j0 + r] : 0u;
+  }
+  auto load_batch = [&](int base, uint32_t (&x)[R]) {
+    const int j0 = base + threadIdx.x * R;
+#pragma unroll
+    for (int r = 0; r < R; ++r) x[r] = one ? xk[r] : (j0 + r < n ? key[j0 + r] : 0u);
+  };
   uint32_t prefix = 0, mask = 0;
   int need = k;  // how many of the keys matching prefix/mask are still to take
   if (k < n) {
@@ -962,11 +976,21 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
       for (int base = 0; base < n; base += BATCH) {
         const int j0 = base + threadIdx.x * R;
         uint32_t x[R];
+        load_batch(base, x);
+        // Runs of equal bins among a thread's keys are added at once (in
+        // the first pass most keys share one bin).
+        int run_bin = -1, run_len = 0;
 #pragma unroll
-        for (int r = 0; r < R; ++r) x[r] = j0 + r < n ? key[j0 + r] : 0u;
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-          if (j0 + r < n && (x[r] & mask) == prefix) atomicAdd(&hist[wave][(x[r] >> shift) & 255u], 1);
+        for (int r = 0; r < R; ++r) {
+          const int bin = j0 + r < n && (x[r] & mask) == prefix ? static_cast<int>((x[r] >> shift) & 255u) : -1;
+          if (bin != run_bin) {
+            if (run_len > 0) atomicAdd(&hist[wave][run_bin], run_len);
+            run_bin = bin;
+            run_len = 0;
+          }
+          if (bin >= 0) ++run_len;
+        }
+        if (run_len > 0) atomicAdd(&hist[wave][run_bin], run_len);
       }
       __syncthreads();
       // Per-bin totals, then suffix sums (keys with a bin >= b) by a shuffle
@@ -1008,8 +1032,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   for (int base = 0; base < n; base += BATCH) {
     const int j0 = base + threadIdx.x * R;
     uint32_t x[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) x[r] = j0 + r < n ? key[j0 + r] : 0u;
+    load_batch(base, x);
     int gt_c = 0, eq_c = 0;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
