@@ -884,29 +884,56 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void score_kernel(ScoreArgs a) 
   if (te > tb) flush(te - tb - 1);
 }
 
-// Scores of the chunk's keys: one workgroup per 64-key tile.  The tile's
-// partial rows are dealt to 4 lane groups x 4 accumulators (entry i to
-// accumulator i mod 16), which are then added in a fixed tree: the sum is
-// the same on every run, and 16 loads per lane are in flight.
-__global__ __launch_bounds__(256) void score_reduce_kernel(ScoreReduceArgs a) {
-  __shared__ float red[4][kTileKeys];
-  const ScoreRow row = a.rows[blockIdx.x];
-  const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  int i = row.begin + 4 * grp;
-  for (; i + 3 < row.end; i += 16) {
+// Scores of the chunk's keys: one workgroup per 64-key tile, 16 waves.  A
+// pass of wave w covers the 64 partial rows part_idx[base .. base + 64) with
+// base = begin + 64 w + 1024 j: each lane loads one of the 64 row indices,
+// and load u of lane l (u < 16) reads 16 bytes (keys 4 (l % 16) ..) of row
+// 4 u + l / 16, with the row index taken from the lane that loaded it.  The
+// sums go lane by lane in load order, then over the 4 lanes of one key
+// group and over the 16 waves in a fixed tree, so the result is the same on
+// every run for the same partial rows in the same order.
+constexpr int kReduceWaves = 16;
+
+__global__ __launch_bounds__(64 * kReduceWaves) void score_reduce_kernel(ScoreReduceArgs a) {
+  __shared__ f32x4 red[kReduceWaves][kTileKeys / 4];
+  const ScoreRow row = sload(a.rows + blockIdx.x);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int sub = lane >> 4, chunk = lane & 15;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int base = row.begin + 64 * w; base < row.end; base += 64 * kReduceWaves) {
+    const int idx = a.part_idx[min(base + lane, row.end - 1)];
+    f32x4 v[16];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc[u] += a.part[static_cast<size_t>(a.part_idx[i + u]) * kTileKeys + lane];
+    for (int u = 0; u < 16; ++u) {
+      const int pi = __shfl(idx, 4 * u + sub);
+      v[u] = *reinterpret_cast<const f32x4 *>(a.part + static_cast<size_t>(pi) * kTileKeys + 4 * chunk);
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (base + 4 * u + sub < row.end) acc += v[u];
   }
-  for (int u = 0; u < 4 && i + u < row.end; ++u) acc[u] += a.part[static_cast<size_t>(a.part_idx[i + u]) * kTileKeys + lane];
-  red[grp][lane] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+#pragma unroll
+  for (int x = 16; x <= 32; x <<= 1) {
+    f32x4 o;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[c] = __shfl_xor(acc[c], x);
+    acc += o;
+  }
+  if (lane < 16) red[w][chunk] = acc;
   __syncthreads();
-  if (grp == 0) {
-    const float total = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
-    const SeqDesc sd = a.seqs[row.seq];
+  if (w == 0) {
+    const float *r = reinterpret_cast<const float *>(red);
+    float t[kReduceWaves];
+#pragma unroll
+    for (int i = 0; i < kReduceWaves; ++i) t[i] = r[i * kTileKeys + lane];
+#pragma unroll
+    for (int h = kReduceWaves / 2; h >= 1; h >>= 1)
+#pragma unroll
+      for (int i = 0; i < h; ++i) t[i] += t[i + h];
+    const SeqDesc sd = sload(a.seqs + row.seq);
     const int key = row.tile * kTileKeys + lane;
-    const int base = sd.kv_len - sd.q_len;
-    if (key >= base && key < sd.kv_len) a.scores[sd.q_start + key - base] = total;
+    const int kbase = sd.kv_len - sd.q_len;
+    if (key >= kbase && key < sd.kv_len) a.scores[sd.q_start + key - kbase] = t[0];
   }
 }
 
@@ -1508,7 +1535,7 @@ hipError_t launch_score(const ScoreArgs &a, int n_items, int head_dim, int page_
 
 hipError_t launch_score_reduce(const ScoreReduceArgs &a, hipStream_t s) {
   if (a.n_rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(score_reduce_kernel, dim3(a.n_rows), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(score_reduce_kernel, dim3(a.n_rows), dim3(64 * kReduceWaves), 0, s, a);
   return hipGetLastError();
 }
 

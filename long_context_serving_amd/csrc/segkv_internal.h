@@ -205,7 +205,7 @@ struct ScoreArgs {
 };
 
 // One 64-key tile of one sequence's chunk: its key sums are the partial rows
-// part_idx[begin .. end), added in that order.
+// part_idx[begin .. end), added in an order fixed by their positions there.
 struct ScoreRow {
   int32_t seq;
   int32_t tile;
