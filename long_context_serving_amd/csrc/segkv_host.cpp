@@ -30,7 +30,8 @@ namespace {
 
 thread_local std::string g_create_error;
 
-constexpr int kStages = 4;
+constexpr int kStages = 32;     // pinned staging slots, used in ring order
+constexpr int kStageGroup = 8;  // slots covered by one completion event
 constexpr int kDefaultDecodeMinPages = 8;
 constexpr int kDefaultPrefillSplitTiles = 0;  // automatic
 constexpr int64_t kMinSplitTiles = 16;
@@ -97,8 +98,8 @@ struct segkv_ctx {
   char *h_stage[kStages] = {};
   char *h_stage_dev[kStages] = {};  // the same pinned memory as seen by kernels
   size_t h_stage_cap[kStages] = {};
-  hipEvent_t stage_ev[kStages] = {};
-  bool stage_used[kStages] = {};
+  hipEvent_t stage_ev[kStages / kStageGroup] = {};  // recorded when the ring leaves the group
+  bool stage_used[kStages / kStageGroup] = {};
   int stage_next = 0;
   float *d_part = nullptr;
   size_t d_part_cap = 0;  // bytes
@@ -175,12 +176,28 @@ int32_t local_segment_start(int32_t kv_len, int32_t n_query, int32_t window, int
 
 // ---- staging / upload --------------------------------------------------
 
+// Every call that stages tables takes the next pinned buffer of a ring of
+// kStages; its kernels read the buffer in place or through the upload
+// kernel.  One completion event covers a group of kStageGroup buffers, so
+// most calls record no event: an event marker between two kernels on the
+// stream lengthens the gap between them.
 int acquire_stage(segkv_ctx *c, size_t bytes, char **out, int *slot_out) {
   int slot = c->stage_next;
   c->stage_next = (c->stage_next + 1) % kStages;
-  if (c->stage_used[slot]) {
-    hipError_t e = hipEventSynchronize(c->stage_ev[slot]);
-    if (e != hipSuccess) return c->device_fail(e, "hipEventSynchronize(stage)");
+  if (slot % kStageGroup == 0) {
+    // Entering group g: the work enqueued so far is all the work that reads
+    // the previous group's slots, so one event marks them free.  Group g
+    // itself is reused once the event recorded when the ring left it fires.
+    constexpr int n_groups = kStages / kStageGroup;
+    const int g = slot / kStageGroup;
+    const int prev = (g + n_groups - 1) % n_groups;
+    hipError_t e = hipEventRecord(c->stage_ev[prev], c->stream);
+    if (e != hipSuccess) return c->device_fail(e, "hipEventRecord(stage)");
+    c->stage_used[prev] = true;
+    if (c->stage_used[g]) {
+      e = hipEventSynchronize(c->stage_ev[g]);
+      if (e != hipSuccess) return c->device_fail(e, "hipEventSynchronize(stage)");
+    }
   }
   if (c->h_stage_cap[slot] < bytes) {
     if (c->h_stage[slot]) {
@@ -219,21 +236,12 @@ int ensure_device_buffer(segkv_ctx *c, char **buf, size_t *cap, size_t bytes, co
   return SEGKV_OK;
 }
 
-int stage_done(segkv_ctx *c, int slot);
-
 // Tables go to device memory through a small copy kernel on the context's
 // stream (it reads the pinned staging buffer directly): a DMA-engine copy
 // between kernels costs a queue hand-off that is several times the copy.
 int upload(segkv_ctx *c, int slot, size_t bytes) {
   hipError_t e = launch_upload(c->d_meta, c->h_stage_dev[slot], bytes, c->stream);
   if (e != hipSuccess) return c->device_fail(e, "upload launch");
-  return stage_done(c, slot);
-}
-
-int stage_done(segkv_ctx *c, int slot) {
-  hipError_t e = hipEventRecord(c->stage_ev[slot], c->stream);
-  if (e != hipSuccess) return c->device_fail(e, "hipEventRecord(stage)");
-  c->stage_used[slot] = true;
   return SEGKV_OK;
 }
 
@@ -471,7 +479,7 @@ int segkv_create(const segkv_config *cfg, segkv_ctx **out) {
       segkv_destroy(c);
       return SEGKV_E_DEVICE;
     }
-    for (int i = 0; i < kStages; ++i) {
+    for (int i = 0; i < kStages / kStageGroup; ++i) {
       hipError_t e = hipEventCreateWithFlags(&c->stage_ev[i], hipEventDisableTiming);
       if (e != hipSuccess) {
         g_create_error = std::string("hipEventCreate: ") + hipGetErrorString(e);
@@ -493,10 +501,10 @@ void segkv_destroy(segkv_ctx *c) {
       (void)hipEventDestroy(t.stop);
     }
     for (hipEvent_t e : c->event_pool) (void)hipEventDestroy(e);
-    for (int i = 0; i < kStages; ++i) {
+    for (int i = 0; i < kStages / kStageGroup; ++i)
       if (c->stage_ev[i]) (void)hipEventDestroy(c->stage_ev[i]);
+    for (int i = 0; i < kStages; ++i)
       if (c->h_stage[i]) (void)hipHostFree(c->h_stage[i]);
-    }
     if (c->d_meta) (void)hipFree(c->d_meta);
     if (c->d_part) (void)hipFree(c->d_part);
   }
@@ -747,9 +755,7 @@ int segkv_append_pages(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_
   if (rc) return rc;
   hipError_t e = launch_scatter(a, static_cast<int>(n_items), c->D, c->P, c->stream);
   if (e != hipSuccess) return c->device_fail(e, "scatter launch");
-  rc = timed_end(c, &t);
-  if (rc) return rc;
-  return stage_done(c, slot);
+  return timed_end(c, &t);
 }
 
 int segkv_prefill(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_ids, const int32_t *cu_q,
