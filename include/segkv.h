@@ -64,7 +64,8 @@ enum segkv_kernel {
   SEGKV_KERNEL_SCORE = 5,         /* attention-mass token scores, MFMA pass  */
   SEGKV_KERNEL_SCORE_REDUCE = 6,  /* their fixed-order reduction              */
   SEGKV_KERNEL_TOPK = 7,          /* per-sequence top-k selection             */
-  SEGKV_KERNEL_COUNT = 8
+  SEGKV_KERNEL_UPLOAD = 8,        /* copy of a call's tables to the device    */
+  SEGKV_KERNEL_COUNT = 9
 };
 
 typedef struct segkv_ctx segkv_ctx;

@@ -137,8 +137,13 @@ __device__ __forceinline__ void relocate_row(bf16x8 (&qv)[NKK], const uint16_t *
 template <int D, int P>
 __global__ __launch_bounds__(kScatterThreads) void scatter_kernel(ScatterArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sv[P * D];
-  const ScatterItem it = a.items[blockIdx.x];
   const int tid = threadIdx.x;
+  if (static_cast<int>(blockIdx.x) < a.copy_wgs) {  // staged tables of the next call
+    for (int i = blockIdx.x * kScatterThreads + tid; i < a.copy_n16; i += a.copy_wgs * kScatterThreads)
+      a.copy_dst[i] = a.copy_src[i];
+    return;
+  }
+  const ScatterItem it = a.items[blockIdx.x - a.copy_wgs];
   constexpr int CPR = D / 8;  // 16-byte chunks per row
   const int n_rows = it.slot_end - it.slot_begin;
   uint16_t *kpage = a.k_pool + static_cast<size_t>(it.page_id) * P * D;
@@ -1487,7 +1492,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
 
 hipError_t launch_scatter(const ScatterArgs &a, int n_items, int head_dim, int page_size, hipStream_t s) {
   if (n_items <= 0) return hipSuccess;
-  SEGKV_DISPATCH_DP(scatter_kernel, head_dim, page_size, dim3(n_items), dim3(kScatterThreads), s, a);
+  SEGKV_DISPATCH_DP(scatter_kernel, head_dim, page_size, dim3(n_items + a.copy_wgs), dim3(kScatterThreads), s, a);
   return hipGetLastError();
 }
 

@@ -33,6 +33,7 @@ thread_local std::string g_create_error;
 constexpr int kStages = 32;     // pinned staging slots, used in ring order
 constexpr int kStageGroup = 8;  // slots covered by one completion event
 constexpr int kDefaultDecodeMinPages = 8;
+constexpr size_t kPrestageRoom = 64 << 10;  // initial room for prefill tables staged by an append
 constexpr int kDefaultPrefillSplitTiles = 0;  // automatic
 constexpr int64_t kMinSplitTiles = 16;
 
@@ -103,6 +104,11 @@ struct segkv_ctx {
   int stage_next = 0;
   float *d_part = nullptr;
   size_t d_part_cap = 0;  // bytes
+  // Prefill tables put on the device by an append's scatter launch: valid
+  // while nothing else has written d_meta since (pre_buf = their bytes).
+  std::vector<char> pre_buf, plan_buf;
+  bool pre_valid = false;
+  size_t pre_room = kPrestageRoom;  // staging room an append keeps for them
   int32_t num_cus = 0;
 
   // tuning
@@ -220,6 +226,7 @@ int acquire_stage(segkv_ctx *c, size_t bytes, char **out, int *slot_out) {
 
 int ensure_device_buffer(segkv_ctx *c, char **buf, size_t *cap, size_t bytes, const char *what) {
   if (*cap >= bytes) return SEGKV_OK;
+  if (buf == &c->d_meta) c->pre_valid = false;
   hipError_t e;
   if (*buf) {
     e = hipStreamSynchronize(c->stream);  // the old buffer may still be read
@@ -236,13 +243,20 @@ int ensure_device_buffer(segkv_ctx *c, char **buf, size_t *cap, size_t bytes, co
   return SEGKV_OK;
 }
 
+int timed_begin(segkv_ctx *c, TimedLaunch *t, int kernel);
+int timed_end(segkv_ctx *c, TimedLaunch *t);
+
 // Tables go to device memory through a small copy kernel on the context's
 // stream (it reads the pinned staging buffer directly): a DMA-engine copy
 // between kernels costs a queue hand-off that is several times the copy.
 int upload(segkv_ctx *c, int slot, size_t bytes) {
+  c->pre_valid = false;
+  TimedLaunch t{};
+  int rc = timed_begin(c, &t, SEGKV_KERNEL_UPLOAD);
+  if (rc) return rc;
   hipError_t e = launch_upload(c->d_meta, c->h_stage_dev[slot], bytes, c->stream);
   if (e != hipSuccess) return c->device_fail(e, "upload launch");
-  return SEGKV_OK;
+  return timed_end(c, &t);
 }
 
 // ---- timing --------------------------------------------------------------
@@ -377,6 +391,138 @@ void write_seq_tables(const segkv_ctx *c, int32_t layer, int32_t n_seqs, const i
       off += sg.n_live();
     }
   }
+}
+
+// A prefill call's device tables, in upload order: sequence tables, work
+// items, combine items, then the work-queue counter (16 bytes, zero).
+struct PrefillPlan {
+  SeqTables tl;
+  size_t tbytes = 0, ibytes = 0, cbytes = 0, bytes = 0;
+  int32_t n_items = 0, n_parts = 0;
+};
+
+// Plans a prefill of the queries cu_q over the current state: the work list
+// (c->scratch_pitems, c->scratch_citems) and the tables, written to out
+// (resized to pp->bytes).  Bytes the tables do not set are zero, so two
+// equal plans are equal byte for byte.
+void build_prefill_plan(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_ids, const int32_t *cu_q,
+                        PrefillPlan *pp, std::vector<char> *out) {
+  // Work items: (seq, kv head, q tile) over the KV tiles the rows can see.
+  const int32_t G = c->G;
+  const int32_t rows = kPrefillRows / G;  // query positions per workgroup
+  std::vector<PrefillItem> &items = c->scratch_pitems;
+  std::vector<CombineItem> &citems = c->scratch_citems;
+  items.clear();
+  citems.clear();
+  int64_t total_cost = 0;
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    const int32_t ql = cu_q[b + 1] - cu_q[b];
+    const SeqLayer &s = c->sl(layer, seq_ids[b]);
+    for (int32_t g = 0; g < c->Hkv; ++g) {
+      const int32_t w = c->win(layer, g);
+      // Last q tile first: for a global head the longest rows come first.
+      for (int32_t qt = (ql + rows - 1) / rows - 1; qt >= 0; --qt) {
+        const int32_t p_min = s.kv_len - ql + qt * rows;
+        const int32_t p_max = s.kv_len - ql + std::min((qt + 1) * rows, ql) - 1;
+        const int32_t lo = w > 0 ? std::max(0, p_min - w + 1) : 0;
+        const int32_t tb = lo / kTileKeys;
+        const int32_t te = p_max / kTileKeys + 1;
+        items.push_back(PrefillItem{b, g, qt, tb, te, -1, 0, 0});
+        total_cost += te - tb;
+      }
+    }
+  }
+  // Split rows that would outlast the average share of one workgroup slot;
+  // their parts are merged by the combine kernel.
+  int64_t split = c->prefill_split_tiles;
+  if (split <= 0) {
+    const int64_t slots = std::max<int64_t>(1, static_cast<int64_t>(c->num_cus) * kPrefillWgPerCu);
+    split = std::max<int64_t>(kMinSplitTiles, ceil_div(total_cost, slots));
+  }
+  int32_t n_parts = 0;
+  int64_t max_cost = 0;
+  {
+    std::vector<PrefillItem> expanded;
+    expanded.reserve(items.size() + items.size() / 4);
+    for (const PrefillItem &x : items) {
+      const int64_t cost = x.tile_end - x.tile_begin;
+      if (cost > split) {
+        const int32_t ns = static_cast<int32_t>(ceil_div(cost, split));
+        const int32_t per = static_cast<int32_t>(ceil_div(cost, ns));
+        const int32_t part0 = n_parts;
+        int32_t k = 0;
+        for (int32_t t0 = x.tile_begin; t0 < x.tile_end; t0 += per, ++k)
+          expanded.push_back(PrefillItem{x.seq, x.kv_head, x.qtile, t0, std::min(x.tile_end, t0 + per), n_parts++, 0, 0});
+        const int32_t ql = cu_q[x.seq + 1] - cu_q[x.seq];
+        citems.push_back(CombineItem{part0, k, cu_q[x.seq] + x.qtile * rows, std::min(rows, ql - x.qtile * rows),
+                                     x.kv_head * G, G, 0, 0});
+        max_cost = std::max<int64_t>(max_cost, per);
+      } else {
+        expanded.push_back(x);
+        max_cost = std::max(max_cost, cost);
+      }
+    }
+    items.swap(expanded);
+  }
+  // Order: longest first (the persistent workgroups take the list in order).
+  // Order 1 cuts the list into eight cost-balanced runs grouped by head, sorts
+  // each longest first and interleaves them (item x of run k at 8x + k).
+  auto lpt_sort = [&](std::vector<PrefillItem> &v) {
+    std::vector<int32_t> &cnt = c->scratch_i32;
+    cnt.assign(static_cast<size_t>(max_cost) + 2, 0);
+    for (const PrefillItem &x : v) cnt[static_cast<size_t>(max_cost - (x.tile_end - x.tile_begin))]++;
+    int32_t acc = 0;
+    for (int32_t &cv : cnt) {
+      int32_t t = cv;
+      cv = acc;
+      acc += t;
+    }
+    std::vector<PrefillItem> sorted(v.size());
+    for (const PrefillItem &x : v) sorted[static_cast<size_t>(cnt[static_cast<size_t>(max_cost - (x.tile_end - x.tile_begin))]++)] = x;
+    v.swap(sorted);
+  };
+  if (c->prefill_order == 1 && items.size() > static_cast<size_t>(kXcds)) {
+    int64_t tot = 0;
+    for (const PrefillItem &x : items) tot += x.tile_end - x.tile_begin;
+    std::vector<PrefillItem> q[kXcds];
+    int64_t prefix = 0;
+    for (const PrefillItem &x : items) {
+      const int64_t cost = x.tile_end - x.tile_begin;
+      const int64_t xcd = std::min<int64_t>(kXcds - 1, (2 * prefix + cost) * kXcds / (2 * std::max<int64_t>(tot, 1)));
+      q[xcd].push_back(x);
+      prefix += cost;
+    }
+    size_t n_q = 0;
+    for (auto &v : q) {
+      lpt_sort(v);
+      n_q = std::max(n_q, v.size());
+    }
+    items.clear();
+    for (size_t j = 0; j < n_q; ++j)
+      for (int x = 0; x < kXcds; ++x)
+        if (j < q[x].size()) items.push_back(q[x][j]);
+  } else {
+    lpt_sort(items);
+  }
+
+  const SeqTables tl = seq_tables_layout(c, layer, n_seqs, seq_ids);
+  pp->tl = tl;
+  pp->tbytes = align_up(tl.bytes, 16);
+  pp->ibytes = align_up(sizeof(PrefillItem) * items.size(), 16);
+  pp->cbytes = align_up(sizeof(CombineItem) * citems.size(), 16);
+  pp->bytes = pp->tbytes + pp->ibytes + pp->cbytes + 16;
+  pp->n_items = static_cast<int32_t>(items.size());
+  pp->n_parts = n_parts;
+  out->assign(pp->bytes, 0);
+  std::vector<int32_t> qs(n_seqs), ql(n_seqs);
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    qs[b] = cu_q[b];
+    ql[b] = cu_q[b + 1] - cu_q[b];
+  }
+  write_seq_tables(c, layer, n_seqs, seq_ids, qs.data(), ql.data(), tl, out->data());
+  std::memcpy(out->data() + pp->tbytes, items.data(), sizeof(PrefillItem) * items.size());
+  if (!citems.empty())
+    std::memcpy(out->data() + pp->tbytes + pp->ibytes, citems.data(), sizeof(CombineItem) * citems.size());
 }
 
 RopeArgs rope_args(const segkv_ctx *c, const SeqTables &t) {
@@ -680,12 +826,23 @@ int segkv_append_pages(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_
       }
     }
   }
+  // When the queries are a prefill chunk (some sequence has more than one),
+  // the tables of their prefill ride along: built after the state change
+  // into room kept behind the scatter items, and copied to the device by the
+  // scatter launch, so that the prefill call needs no upload of its own.
+  int64_t n_queries = 0;
+  for (int32_t b = 0; b < n_seqs; ++b) n_queries += n_query[b];
+  const bool prestage = !c->planning && n_items > 0 && n_queries > n_seqs;
   char *stage = nullptr;
   int slot = 0;
-  const size_t bytes = sizeof(ScatterItem) * static_cast<size_t>(n_items);
+  const size_t bytes = align_up(sizeof(ScatterItem) * static_cast<size_t>(n_items), 16);
   if (!c->planning && n_items > 0) {
-    rc = acquire_stage(c, bytes, &stage, &slot);
+    rc = acquire_stage(c, bytes + (prestage ? c->pre_room : 0), &stage, &slot);
     if (rc) return rc;
+    if (prestage) {
+      rc = ensure_device_buffer(c, &c->d_meta, &c->d_meta_cap, c->pre_room, "hipMalloc(tables)");
+      if (rc) return rc;
+    }
   }
 
   // Commit: trim, then copy shared tails and allocate, then record scatter
@@ -750,11 +907,34 @@ int segkv_append_pages(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_
   // (one 32-byte item per workgroup), so the append needs no upload.
   a.items = reinterpret_cast<const ScatterItem *>(c->h_stage_dev[slot]);
   a.num_kv_heads = c->Hkv;
+  a.copy_src = nullptr;
+  a.copy_dst = nullptr;
+  a.copy_n16 = 0;
+  a.copy_wgs = 0;
+  bool staged = false;
+  if (prestage) {
+    std::vector<int32_t> cu_q(static_cast<size_t>(n_seqs) + 1, 0);
+    for (int32_t b = 0; b < n_seqs; ++b) cu_q[b + 1] = cu_q[b] + n_query[b];
+    PrefillPlan pp;
+    build_prefill_plan(c, layer, n_seqs, seq_ids, cu_q.data(), &pp, &c->plan_buf);
+    if (bytes + pp.bytes <= c->h_stage_cap[slot] && pp.bytes <= c->d_meta_cap) {
+      std::memcpy(stage + bytes, c->plan_buf.data(), pp.bytes);
+      c->pre_buf.swap(c->plan_buf);
+      a.copy_src = reinterpret_cast<const uint4 *>(c->h_stage_dev[slot] + bytes);
+      a.copy_dst = reinterpret_cast<uint4 *>(c->d_meta);
+      a.copy_n16 = static_cast<int32_t>(pp.bytes / 16);
+      a.copy_wgs = static_cast<int32_t>(std::min<size_t>(kScatterCopyWgs, ceil_div(pp.bytes / 16, kScatterThreads)));
+      staged = true;
+    }
+    c->pre_room = std::max(c->pre_room, pp.bytes);  // the next append keeps room enough
+  }
+  c->pre_valid = false;
   TimedLaunch t{};
   rc = timed_begin(c, &t, SEGKV_KERNEL_SCATTER);
   if (rc) return rc;
   hipError_t e = launch_scatter(a, static_cast<int>(n_items), c->D, c->P, c->stream);
   if (e != hipSuccess) return c->device_fail(e, "scatter launch");
+  c->pre_valid = staged;
   return timed_end(c, &t);
 }
 
@@ -781,132 +961,37 @@ int segkv_prefill(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *se
   if (total_q == 0) return SEGKV_OK;
   if (!q || !o) return c->fail(SEGKV_E_INVAL, "q / o is NULL");
 
-  // Work items: (seq, kv head, q tile) over the KV tiles the rows can see.
-  const int32_t G = c->G;
-  const int32_t rows = kPrefillRows / G;  // query positions per workgroup
-  std::vector<PrefillItem> &items = c->scratch_pitems;
-  std::vector<CombineItem> &citems = c->scratch_citems;
-  items.clear();
-  citems.clear();
-  int64_t total_cost = 0;
-  for (int32_t b = 0; b < n_seqs; ++b) {
-    const int32_t ql = cu_q[b + 1] - cu_q[b];
-    const SeqLayer &s = c->sl(layer, seq_ids[b]);
-    for (int32_t g = 0; g < c->Hkv; ++g) {
-      const int32_t w = c->win(layer, g);
-      // Last q tile first: for a global head the longest rows come first.
-      for (int32_t qt = (ql + rows - 1) / rows - 1; qt >= 0; --qt) {
-        const int32_t p_min = s.kv_len - ql + qt * rows;
-        const int32_t p_max = s.kv_len - ql + std::min((qt + 1) * rows, ql) - 1;
-        const int32_t lo = w > 0 ? std::max(0, p_min - w + 1) : 0;
-        const int32_t tb = lo / kTileKeys;
-        const int32_t te = p_max / kTileKeys + 1;
-        items.push_back(PrefillItem{b, g, qt, tb, te, -1, 0, 0});
-        total_cost += te - tb;
-      }
-    }
+  PrefillPlan pp;
+  std::vector<char> &tables = c->plan_buf;
+  build_prefill_plan(c, layer, n_seqs, seq_ids, cu_q, &pp, &tables);
+  // The append that declared these queries may have put the same tables on
+  // the device already (its scatter launch copies them).
+  const bool staged = c->pre_valid && c->pre_buf.size() == pp.bytes &&
+                      std::memcmp(c->pre_buf.data(), tables.data(), pp.bytes) == 0;
+  c->pre_valid = false;  // this launch consumes the counters
+  if (!staged) {
+    char *stage = nullptr;
+    int slot = 0;
+    rc = acquire_stage(c, pp.bytes, &stage, &slot);
+    if (rc) return rc;
+    rc = ensure_device_buffer(c, &c->d_meta, &c->d_meta_cap, pp.bytes, "hipMalloc(tables)");
+    if (rc) return rc;
+    std::memcpy(stage, tables.data(), pp.bytes);
+    rc = upload(c, slot, pp.bytes);
+    if (rc) return rc;
   }
-  // Split rows that would outlast the average share of one workgroup slot;
-  // their parts are merged by the combine kernel.
-  int64_t split = c->prefill_split_tiles;
-  if (split <= 0) {
-    const int64_t slots = std::max<int64_t>(1, static_cast<int64_t>(c->num_cus) * kPrefillWgPerCu);
-    split = std::max<int64_t>(kMinSplitTiles, ceil_div(total_cost, slots));
-  }
-  int32_t n_parts = 0;
-  int64_t max_cost = 0;
-  {
-    std::vector<PrefillItem> expanded;
-    expanded.reserve(items.size() + items.size() / 4);
-    for (const PrefillItem &x : items) {
-      const int64_t cost = x.tile_end - x.tile_begin;
-      if (cost > split) {
-        const int32_t ns = static_cast<int32_t>(ceil_div(cost, split));
-        const int32_t per = static_cast<int32_t>(ceil_div(cost, ns));
-        const int32_t part0 = n_parts;
-        int32_t k = 0;
-        for (int32_t t0 = x.tile_begin; t0 < x.tile_end; t0 += per, ++k)
-          expanded.push_back(PrefillItem{x.seq, x.kv_head, x.qtile, t0, std::min(x.tile_end, t0 + per), n_parts++, 0, 0});
-        const int32_t ql = cu_q[x.seq + 1] - cu_q[x.seq];
-        citems.push_back(CombineItem{part0, k, cu_q[x.seq] + x.qtile * rows, std::min(rows, ql - x.qtile * rows),
-                                     x.kv_head * G, G, 0, 0});
-        max_cost = std::max<int64_t>(max_cost, per);
-      } else {
-        expanded.push_back(x);
-        max_cost = std::max(max_cost, cost);
-      }
-    }
-    items.swap(expanded);
-  }
-  // Order: longest first (the persistent workgroups take the list in order).
-  // Order 1 cuts the list into eight cost-balanced runs grouped by head, sorts
-  // each longest first and interleaves them (item x of run k at 8x + k).
-  auto lpt_sort = [&](std::vector<PrefillItem> &v) {
-    std::vector<int32_t> &cnt = c->scratch_i32;
-    cnt.assign(static_cast<size_t>(max_cost) + 2, 0);
-    for (const PrefillItem &x : v) cnt[static_cast<size_t>(max_cost - (x.tile_end - x.tile_begin))]++;
-    int32_t acc = 0;
-    for (int32_t &cv : cnt) {
-      int32_t t = cv;
-      cv = acc;
-      acc += t;
-    }
-    std::vector<PrefillItem> sorted(v.size());
-    for (const PrefillItem &x : v) sorted[static_cast<size_t>(cnt[static_cast<size_t>(max_cost - (x.tile_end - x.tile_begin))]++)] = x;
-    v.swap(sorted);
-  };
-  if (c->prefill_order == 1 && items.size() > static_cast<size_t>(kXcds)) {
-    int64_t tot = 0;
-    for (const PrefillItem &x : items) tot += x.tile_end - x.tile_begin;
-    std::vector<PrefillItem> q[kXcds];
-    int64_t prefix = 0;
-    for (const PrefillItem &x : items) {
-      const int64_t cost = x.tile_end - x.tile_begin;
-      const int64_t xcd = std::min<int64_t>(kXcds - 1, (2 * prefix + cost) * kXcds / (2 * std::max<int64_t>(tot, 1)));
-      q[xcd].push_back(x);
-      prefix += cost;
-    }
-    size_t n_q = 0;
-    for (auto &v : q) {
-      lpt_sort(v);
-      n_q = std::max(n_q, v.size());
-    }
-    items.clear();
-    for (size_t j = 0; j < n_q; ++j)
-      for (int x = 0; x < kXcds; ++x)
-        if (j < q[x].size()) items.push_back(q[x][j]);
-  } else {
-    lpt_sort(items);
-  }
-
-  const SeqTables tl = seq_tables_layout(c, layer, n_seqs, seq_ids);
-  const size_t tbytes = align_up(tl.bytes, 16);
-  const size_t ibytes = align_up(sizeof(PrefillItem) * items.size(), 16);
-  const size_t cbytes = align_up(sizeof(CombineItem) * citems.size(), 16);
-  const size_t bytes = tbytes + ibytes + cbytes + 16;  // + the work-queue counter
-  char *stage = nullptr;
-  int slot = 0;
-  rc = acquire_stage(c, bytes, &stage, &slot);
-  if (rc) return rc;
-  rc = ensure_device_buffer(c, &c->d_meta, &c->d_meta_cap, bytes, "hipMalloc(tables)");
-  if (rc) return rc;
+  const int32_t n_parts = pp.n_parts;
   const size_t part_bytes = static_cast<size_t>(n_parts) * kPrefillRows * (c->D + 1) * sizeof(float);
   if (n_parts > 0) {
     rc = ensure_device_buffer(c, reinterpret_cast<char **>(&c->d_part), &c->d_part_cap, part_bytes,
                               "hipMalloc(partials)");
     if (rc) return rc;
   }
-  std::vector<int32_t> qs(n_seqs), ql(n_seqs);
-  for (int32_t b = 0; b < n_seqs; ++b) {
-    qs[b] = cu_q[b];
-    ql[b] = cu_q[b + 1] - cu_q[b];
-  }
-  write_seq_tables(c, layer, n_seqs, seq_ids, qs.data(), ql.data(), tl, stage);
-  std::memcpy(stage + tbytes, items.data(), sizeof(PrefillItem) * items.size());
-  if (!citems.empty()) std::memcpy(stage + tbytes + ibytes, citems.data(), sizeof(CombineItem) * citems.size());
-  std::memset(stage + tbytes + ibytes + cbytes, 0, 16);
-  rc = upload(c, slot, bytes);
-  if (rc) return rc;
+  const SeqTables &tl = pp.tl;
+  const size_t tbytes = pp.tbytes, ibytes = pp.ibytes, cbytes = pp.cbytes;
+  const std::vector<CombineItem> &citems = c->scratch_citems;
+  const int32_t G = c->G;
+  const int32_t rows = kPrefillRows / G;
 
   PrefillArgs a;
   a.q = static_cast<const uint16_t *>(q);
@@ -927,9 +1012,9 @@ int segkv_prefill(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *se
   a.rows_per_tile = rows;
   a.scale = c->scale;
   a.scale_log2 = c->scale * 1.4426950408889634f;
-  a.n_items = static_cast<int32_t>(items.size());
+  a.n_items = pp.n_items;
   a.counter = reinterpret_cast<int32_t *>(c->d_meta + tbytes + ibytes + cbytes);
-  const int64_t n_wgs = std::min<int64_t>(static_cast<int64_t>(items.size()),
+  const int64_t n_wgs = std::min<int64_t>(static_cast<int64_t>(pp.n_items),
                                           std::max<int64_t>(1, static_cast<int64_t>(c->num_cus) * kPrefillWgPerCu));
   TimedLaunch t{};
   rc = timed_begin(c, &t, SEGKV_KERNEL_PREFILL);

@@ -23,6 +23,7 @@ constexpr int kDecodeThreads = 512;  // 8 waves, two per SIMD
 constexpr int kDecodeCols = 16;    // query heads handled by one decode work item (GQA group, padded)
 constexpr int kDecodeSlots = 16;   // LDS partials of one decode workgroup: (piece, wave) pairs of a batch
 constexpr int kScatterThreads = 256;
+constexpr int kScatterCopyWgs = 16;  // most workgroups of a scatter launch that copy staged tables
 constexpr int kMergeThreads = 256;
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkRun = 8;  // consecutive keys per thread per batch
@@ -118,12 +119,19 @@ struct CombineItem {
   int32_t pad0, pad1;
 };
 
+// Workgroups [0, copy_wgs) of a scatter launch copy copy_n16 16-byte words
+// from copy_src (pinned host memory) to copy_dst: the tables of the prefill
+// that follows the append.  The scatter items go to workgroups copy_wgs ..
 struct ScatterArgs {
   const uint16_t *k_new;
   const uint16_t *v_new;
   uint16_t *k_pool;
   uint16_t *v_pool;
   const ScatterItem *items;
+  const uint4 *copy_src;
+  uint4 *copy_dst;
+  int32_t copy_n16;
+  int32_t copy_wgs;
   int32_t num_kv_heads;
 };
 

@@ -31,6 +31,8 @@ KERNEL_MERGE = 4
 KERNEL_SCORE = 5
 KERNEL_SCORE_REDUCE = 6
 KERNEL_TOPK = 7
+KERNEL_UPLOAD = 8
+KERNEL_COUNT = 9
 
 TUNE_DECODE_MIN_PAGES = 0
 TUNE_PREFILL_SPLIT_TILES = 1
@@ -419,7 +421,7 @@ class SegKV:
         if not enable:
             mask = 0
         elif kernels is None:
-            mask = (1 << 4) - 1
+            mask = (1 << KERNEL_COUNT) - 1
         else:
             mask = 0
             for k in kernels:
