@@ -365,10 +365,24 @@ def cpu_baseline(w, x, budget_s=15.0):
         for _ in range(reps):
             _, flops, n = run(n)
         t = (time.perf_counter() - t0) / reps
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads or os.cpu_count(),
-            "kind": "oracle",
-            "sample": f"{n} of {q_len} query rows (seeded), all {w.num_q_heads} query heads, of "
-                      f"{w.name}; {t:.1f} s per pass, {reps} pass(es); fp64 numpy, BLAS threads={threads}, host cpus={os.cpu_count()}"}
+    out = {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads or os.cpu_count(),
+           "kind": "oracle",
+           "sample": f"{n} of {q_len} query rows (seeded), all {w.num_q_heads} query heads, of "
+                     f"{w.name}; {t:.1f} s per pass, {reps} pass(es); fp64 numpy, BLAS threads={threads}, host cpus={os.cpu_count()}"}
+    # The same oracle on one thread, on a smaller sample (about a third of the budget).
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:
+        return out
+    with threadpool_limits(limits=1):
+        n1 = 16
+        t1, f1, n1 = run(n1)
+        while t1 < budget_s / 9 and n1 < q_len:
+            n1 = int(min(q_len, n1 * max(2.0, min(8.0, budget_s / 3 / max(t1, 1e-3)))))
+            t1, f1, n1 = run(n1)
+    out["single_thread"] = {"value": f1 / t1 / 1e12, "unit": "TFLOP/s", "cores": 1,
+                            "sample": f"{n1} of {q_len} query rows (seeded), {t1:.1f} s"}
+    return out
 
 
 # ------------------------------------------------------------------ main
