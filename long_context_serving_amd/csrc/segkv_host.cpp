@@ -125,6 +125,7 @@ struct segkv_ctx {
 
   // scratch reused across calls
   std::vector<int32_t> scratch_i32;
+  std::vector<int32_t> scratch_cnt;  // counting sort of the prefill work list (an append plans a prefill too)
   std::vector<int32_t> scratch_deltas;  // distinct nonzero offsets of the current call
   std::vector<int32_t> scratch_release;  // pages whose reference an append drops after it allocated
   std::vector<PrefillItem> scratch_pitems;
@@ -468,7 +469,7 @@ void build_prefill_plan(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32
   // Order 1 cuts the list into eight cost-balanced runs grouped by head, sorts
   // each longest first and interleaves them (item x of run k at 8x + k).
   auto lpt_sort = [&](std::vector<PrefillItem> &v) {
-    std::vector<int32_t> &cnt = c->scratch_i32;
+    std::vector<int32_t> &cnt = c->scratch_cnt;
     cnt.assign(static_cast<size_t>(max_cost) + 2, 0);
     for (const PrefillItem &x : v) cnt[static_cast<size_t>(max_cost - (x.tile_end - x.tile_begin))]++;
     int32_t acc = 0;
