@@ -641,18 +641,33 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const float lse_val = l_tot > 0.f ? m * a.scale + logf(l_tot) : kNegInf;
     if (it.part < 0) {
+      // A lane holds 4-channel groups i of its row (channels db*32 + 8 i +
+      // 4 half ..); one swap with the partner lane gives each lane 8
+      // contiguous channels: lanes 0-31 the groups of even i, 32-63 odd i.
+      u32x4 w[NDB][2];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int ip = 0; ip < 2; ++ip) {
+          const f32x16 &ac = oacc[db];
+          const u32x2 p0 = pack4_bf16(ac[8 * ip] * inv, ac[8 * ip + 1] * inv, ac[8 * ip + 2] * inv, ac[8 * ip + 3] * inv);
+          const u32x2 p1 =
+              pack4_bf16(ac[8 * ip + 4] * inv, ac[8 * ip + 5] * inv, ac[8 * ip + 6] * inv, ac[8 * ip + 7] * inv);
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            // lanes 32-63 of the first operand trade with lanes 0-31 of the second
+            const auto sw = __builtin_amdgcn_permlane32_swap(p0[k], p1[k], false, false);
+            w[db][ip][k] = sw[0];
+            w[db][ip][2 + k] = sw[1];
+          }
+        }
+      }
       if (valid) {
         uint16_t *orow = a.o + (static_cast<size_t>(sd.q_start + t) * a.num_q_heads + h) * D;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int d0 = db * 32 + i * 8 + half * 4;
-            *reinterpret_cast<u32x2 *>(orow + d0) =
-                pack4_bf16(oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv, oacc[db][4 * i + 2] * inv,
-                           oacc[db][4 * i + 3] * inv);
-          }
-        }
+          for (int ip = 0; ip < 2; ++ip) *reinterpret_cast<u32x4 *>(orow + db * 32 + ip * 16 + half * 8) = w[db][ip];
         if (half == 0 && a.lse) a.lse[static_cast<size_t>(sd.q_start + t) * a.num_q_heads + h] = lse_val;
       }
     } else {
