@@ -145,6 +145,8 @@ __global__ __launch_bounds__(kScatterThreads) void scatter_kernel(ScatterArgs a)
   }
   const ScatterItem it = a.items[blockIdx.x - a.copy_wgs];
   constexpr int CPR = D / 8;  // 16-byte chunks per row
+  // 16-byte chunk c of staged V row `slot` sits at chunk c ^ (slot / 8 % CPR)
+  auto vswz = [](int slot, int c) { return c ^ ((slot >> 3) & (CPR - 1)); };
   const int n_rows = it.slot_end - it.slot_begin;
   uint16_t *kpage = a.k_pool + static_cast<size_t>(it.page_id) * P * D;
   uint16_t *vpage = a.v_pool + static_cast<size_t>(it.page_id) * P * D;
@@ -183,7 +185,7 @@ __global__ __launch_bounds__(kScatterThreads) void scatter_kernel(ScatterArgs a)
     if (c < n_rows * CPR) {
       const int row = c / CPR, dc = c - row * CPR;
       *reinterpret_cast<u32x4 *>(kpage + static_cast<size_t>(it.slot_begin + row) * D + dc * 8) = kx[i];
-      *reinterpret_cast<u32x4 *>(sv + (it.slot_begin + row) * D + dc * 8) = vx[i];
+      *reinterpret_cast<u32x4 *>(sv + (it.slot_begin + row) * D + vswz(it.slot_begin + row, dc) * 8) = vx[i];
     }
   }
   if (it.zero_tail) {
@@ -191,24 +193,27 @@ __global__ __launch_bounds__(kScatterThreads) void scatter_kernel(ScatterArgs a)
     for (int c = tid; c < (P - it.slot_end) * CPR; c += kScatterThreads) {
       const int row = c / CPR, dc = c - row * CPR;
       *reinterpret_cast<u32x4 *>(kpage + static_cast<size_t>(it.slot_end + row) * D + dc * 8) = z;
-      *reinterpret_cast<u32x4 *>(sv + (it.slot_end + row) * D + dc * 8) = z;
+      *reinterpret_cast<u32x4 *>(sv + (it.slot_end + row) * D + vswz(it.slot_end + row, dc) * 8) = z;
     }
   }
   __syncthreads();
   // V^T rows: channel d holds slots [slot_begin, wend) contiguously.  A
   // lane takes a channel pair and 8 consecutive slots: one 4-byte LDS read
-  // per slot (consecutive lanes read consecutive words: no bank conflict)
-  // and two 16-byte stores.
+  // per slot and two 16-byte stores.  Consecutive lanes take consecutive
+  // slot groups of one channel pair, so 8 lanes store a whole 128-byte
+  // channel row; the chunk swizzle of the staged rows spreads their LDS
+  // reads over the banks.
   const int wend = it.zero_tail ? P : it.slot_end;
   const int n = wend - it.slot_begin;
   if ((it.slot_begin & 7) == 0 && (n & 7) == 0) {
     constexpr int NPAIR = D / 2;
     const int groups = n / 8;
     for (int c = tid; c < NPAIR * groups; c += kScatterThreads) {
-      const int dp = c % NPAIR, s0 = it.slot_begin + (c / NPAIR) * 8;
+      const int dp = c / groups, s0 = it.slot_begin + (c % groups) * 8;
       uint32_t w[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) w[e] = *reinterpret_cast<const uint32_t *>(sv + (s0 + e) * D + 2 * dp);
+      for (int e = 0; e < 8; ++e)
+        w[e] = *reinterpret_cast<const uint32_t *>(sv + (s0 + e) * D + vswz(s0 + e, dp >> 2) * 8 + 2 * (dp & 3));
       u32x4 lo, hi;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -221,7 +226,7 @@ __global__ __launch_bounds__(kScatterThreads) void scatter_kernel(ScatterArgs a)
   } else {
     for (int c = tid; c < D * n; c += kScatterThreads) {
       const int d = c / n, s = it.slot_begin + (c - d * n);
-      vpage[static_cast<size_t>(d) * P + s] = sv[s * D + d];
+      vpage[static_cast<size_t>(d) * P + s] = sv[s * D + vswz(s, d >> 3) * 8 + (d & 7)];
     }
   }
 }
