@@ -767,19 +767,27 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void score_kernel(ScoreArgs a) 
   }
   // The rows of S this lane holds: register v is row 8 (v/4) + 4 half + v%4
   // of the wave.  Rows past the chunk get lse = +inf, hence probability 0.
+  // Each lane loads the LSE of its own row (one coalesced load: an invalid
+  // row reads the tile's last valid row and gets +inf); lane v's rows are
+  // then taken from the lanes that loaded them.
+  float lse_own;
+  {
+    const int r = wave * 32 + col;
+    const int po = r / G;
+    const int t = t0 + po;
+    const bool valid = po < rows && t < sd.q_len;
+    const float raw = a.lse[static_cast<size_t>(sd.q_start + min(t, t_last)) * a.num_q_heads + it.kv_head * G +
+                            (r - po * G)];
+    lse_own = valid ? raw * kLog2e : __builtin_inff();
+  }
   float lse2[16];
   int prow[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
-    const int r = wave * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-    const int po = r / G;
+    const int rw = 8 * (v >> 2) + 4 * half + (v & 3);  // row within the wave
+    const int po = (wave * 32 + rw) / G;
     const int t = t0 + po;
-    const bool valid = po < rows && t < sd.q_len;
-    // Unconditional load (an invalid row reads the tile's last valid row),
-    // so the 16 loads are in flight together.
-    const float raw = a.lse[static_cast<size_t>(sd.q_start + min(t, t_last)) * a.num_q_heads + it.kv_head * G +
-                            (r - po * G)];
-    lse2[v] = valid ? raw * kLog2e : __builtin_inff();
+    lse2[v] = __shfl(lse_own, rw);
     prow[v] = base + min(t, t_last);
   }
   // Wait for Q and the LSE values once, here; inside the tile loop the
