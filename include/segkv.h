@@ -125,6 +125,12 @@ void segkv_destroy(segkv_ctx *ctx);
  * the pool cannot hold the whole batch.  When new tokens land in a
  * partially filled page that a fork also holds (segkv_fork), the sequence
  * first gets a private copy of that page (copy-on-write, one extra page).
+ * When the queries form a prefill chunk (more queries than sequences), the
+ * append also builds the device tables of the prefill of exactly these
+ * queries and its scatter launch copies them to the device; a following
+ * segkv_prefill whose tables come out the same byte for byte, with no
+ * other call in between that writes tables, uses them instead of
+ * uploading its own.  Results are the same either way.
  */
 int segkv_append_pages(segkv_ctx *ctx, int32_t layer, int32_t n_seqs, const int32_t *seq_ids,
                        const int32_t *cu_new, const int32_t *n_query, const void *k_new,
