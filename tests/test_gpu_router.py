@@ -127,7 +127,9 @@ def split_out(out, ks):
 
 
 @pytest.mark.parametrize("counts,ks", [((10,), (3,)), ((1000, 1, 5000, 7), (1, 1, 2500, 0)), ((4096,), (4096,)),
-                                       ((200_000, 3333), (50_000, 17)), ((1025, 2047), (512, 1))])
+                                       ((200_000, 3333), (50_000, 17)), ((1025, 2047), (512, 1)),
+                                       # either side of the largest sequence kept in registers (8192 keys)
+                                       ((8192, 8193), (4096, 8192)), ((8192, 8193), (1, 1))])
 def test_topk_matches_oracle_exactly(counts, ks):
     rng = np.random.default_rng(sum(counts))
     s = rng.exponential(1.0, size=sum(counts)).astype(np.float32)
