@@ -1005,7 +1005,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   static_assert(BATCH < 65536, "per-batch counts are packed in 16 bits");
   __shared__ int hist[NWV][256];  // one histogram per wave
   __shared__ int s_wave[NWV];
-  __shared__ int s_pick[2];
+  __shared__ int s_pick[3];
   const int b = blockIdx.x;
   const int n = a.cu[b + 1] - a.cu[b];
   const int k = a.k[b];
@@ -1075,17 +1075,22 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
         if (sfx >= need && above < need) {
           s_pick[0] = threadIdx.x;
           s_pick[1] = need - above;
+          s_pick[2] = cnt;
         }
       }
       __syncthreads();
       prefix |= static_cast<uint32_t>(s_pick[0]) << shift;
       mask |= 255u << shift;
       need = s_pick[1];
+      const bool whole_bin = s_pick[2] == need;  // every key of the bin is kept: no lower digit matters
       __syncthreads();
+      if (whole_bin) break;
     }
   }
-  // Keep every key > prefix and the first `need` keys equal to prefix in
-  // index order (k >= n keeps everything).  A kept key's output slot is the
+  // Keep every key whose masked bits exceed prefix and the first `need`
+  // keys whose masked bits equal it, in index order (k >= n keeps
+  // everything).  After all four passes the mask is the whole key; a pass
+  // that kept its whole bin stops early, and then every equal key is kept.  A kept key's output slot is the
   // number of greater keys before it plus min(equal keys before it, need);
   // both counts come from one scan of the packed per-thread counts.
   int gt_seen = 0, eq_seen = 0;
@@ -1097,8 +1102,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const bool in = j0 + r < n;
-      gt_c += in && (k >= n || x[r] > prefix);
-      eq_c += in && k < n && x[r] == prefix;
+      gt_c += in && (k >= n || (x[r] & mask) > prefix);
+      eq_c += in && k < n && (x[r] & mask) == prefix;
     }
     int tot;
     const int ex = block_excl_scan(gt_c | (eq_c << 16), s_wave, &tot);
@@ -1106,10 +1111,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const bool in = j0 + r < n;
-      if (in && (k >= n || x[r] > prefix)) {
+      if (in && (k >= n || (x[r] & mask) > prefix)) {
         out[g + min(e, need)] = j0 + r;
         ++g;
-      } else if (in && k < n && x[r] == prefix) {
+      } else if (in && k < n && (x[r] & mask) == prefix) {
         if (e < need) out[g + e] = j0 + r;
         ++e;
       }
