@@ -41,6 +41,8 @@ def test_tiny_mha_all_rows():
     ((500,), (500,), 32, 4, 128, 64, (0, 64, 1000, 1)),
     ((300,), (300,), 24, 8, 64, 32, (0, 5, 63, 64, 65, 299, 300, 600)),
     ((640,), (640,), 12, 4, 128, 16, (13, 0, 200, 640)),    # G = 3 does not divide the 128-row tile
+    ((600,), (600,), 16, 1, 128, 64, (0,)),                 # G = 16, the largest group: 16 positions per item
+    ((450,), (450,), 32, 2, 64, 64, (0, 100)),               # G = 16 with D = 64 on 64-token pages
 ])
 def test_prefill_shapes(case):
     kv, q, hq, hkv, d, p, windows = case

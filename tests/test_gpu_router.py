@@ -75,6 +75,7 @@ def check_scores(got, ref):
     ((2000,), (333,), 8, 8, 128, 32, (0, 1000, 10, 77, 0, 5, 64, 2000)),
     ((900, 17, 300), (900, 5, 300), 16, 4, 128, 64, (0, 64, 128, 33)),
     ((640,), (640,), 12, 4, 64, 32, (13, 0, 200, 640)),
+    ((600,), (600,), 16, 1, 128, 64, (0,)),  # G = 16
 ])
 def test_scores_match_oracle(case):
     kv, q, hq, hkv, d, p, windows = case
