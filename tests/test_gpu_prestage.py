@@ -117,3 +117,24 @@ def test_tables_staged_for_another_layer_are_not_used():
         ctx.set_timing(False)
     finally:
         ctx.close()
+
+
+def test_relocation_set_after_the_append_is_not_missed():
+    # offsets set between the append and the prefill change the segment
+    # tables: the staged ones no longer match and the prefill uploads its own
+    import torch
+    w = wl.small_workload("prestage_rope", (900, 400), (300, 400), 8, 2, 128, 64, (0, 256), seed=54)
+    x = wl.make_inputs(w)
+    rope = dict(deltas=[[0, 4096], [0, 77]])
+    say(f"prefill {w.name} kv={w.kv_lens} q={w.q_lens} rope={rope}")
+    run = R.WorkloadRun(w, R.to_device(w, x), deltas=rope["deltas"])
+    try:
+        run.ctx.set_timing(True, [S.KERNEL_UPLOAD])
+        run.load()  # appends, then sets the offsets
+        o, l = run.prefill()
+        torch.cuda.synchronize()
+        assert uploads(run.ctx) == 1
+        compare(w, x, S.bf16_bits(o), l.cpu().numpy().astype(np.float64), rope=rope)
+        run.ctx.set_timing(False)
+    finally:
+        run.close()
