@@ -145,6 +145,20 @@ def test_topk_matches_oracle_exactly(counts, ks):
         at += n
 
 
+def test_topk_of_equal_and_nearly_equal_scores():
+    # all keys equal (the lowest indices win), and keys equal but for their
+    # lowest mantissa bits
+    counts, ks = (5000, 3000, 7), (1234, 2999, 3)
+    s = np.concatenate([np.full(5000, 0.75, np.float32),
+                        (np.float32(3.0).view(np.uint32) + np.arange(3000, dtype=np.uint32) % 5).view(np.float32),
+                        np.full(7, 2.0, np.float32)])
+    got = split_out(run_topk(counts, s, ks), ks)
+    at = 0
+    for n, k, g in zip(counts, ks, got):
+        assert np.array_equal(g, RT.top_k(s[at:at + n].astype(np.float64), k)), (n, k)
+        at += n
+
+
 def test_topk_of_gpu_scores_is_a_valid_selection():
     import torch
     w = wl.small_workload("route", (2000, 700), (2000, 700), 16, 4, 128, 64, (0, 64, 128, 33), seed=8)
