@@ -169,21 +169,32 @@ def merge_partials(o_parts: np.ndarray, lse_parts: np.ndarray):
     return o, lse
 
 
-def paged_round_trip(k: np.ndarray, page_size: int, seed: int):
+def paged_store(rows: np.ndarray, page_size: int, seed: int):
     """Store logical rows [n, ...] in pages placed at a seeded random
-    physical order, then read them back through the page table.
-
-    Returns (gathered rows, page_table).  Used to show the oracle's result
-    does not depend on physical page placement.
-    """
-    n = k.shape[0]
+    physical order.  Returns (pool [n_pages, page_size, ...], page_table):
+    logical page i sits at pool[page_table[i]]; unused slots are zero."""
+    n = rows.shape[0]
     n_pages = -(-n // page_size)
-    perm = np.random.default_rng(seed).permutation(n_pages)
-    pool = np.zeros((n_pages, page_size) + k.shape[1:], dtype=k.dtype)
+    table = np.random.default_rng(seed).permutation(n_pages)
+    pool = np.zeros((n_pages, page_size) + rows.shape[1:], dtype=rows.dtype)
     for i in range(n_pages):
-        chunk = k[i * page_size:(i + 1) * page_size]
-        pool[perm[i], :len(chunk)] = chunk
-    out = np.empty_like(k)
+        chunk = rows[i * page_size:(i + 1) * page_size]
+        pool[table[i], :len(chunk)] = chunk
+    return pool, table
+
+
+def paged_gather(pool: np.ndarray, table, n: int) -> np.ndarray:
+    """Read logical rows 0 .. n-1 back through a page table: row t is slot
+    t % page_size of physical page table[t // page_size]."""
+    page_size = pool.shape[1]
+    out = np.empty((n,) + pool.shape[2:], dtype=pool.dtype)
     for t in range(n):
-        out[t] = pool[perm[t // page_size], t % page_size]
-    return out, perm
+        out[t] = pool[table[t // page_size], t % page_size]
+    return out
+
+
+def paged_round_trip(k: np.ndarray, page_size: int, seed: int):
+    """``paged_store`` then ``paged_gather``: returns (gathered rows, page_table).
+    Used to show the oracle's result does not depend on physical page placement."""
+    pool, table = paged_store(k, page_size, seed)
+    return paged_gather(pool, table, k.shape[0]), table

@@ -28,31 +28,11 @@ import numpy as np
 from . import attention as A
 
 
-def probabilities(q, k, windows, scale):
-    """Normalised probabilities P[t, h, j] (fp64) of one sequence whose
-    queries are its last q_len tokens; zero where j is not visible."""
-    q = np.asarray(q, np.float64)
-    k = np.asarray(k, np.float64)
-    q_len, hq, _ = q.shape
-    kv_len, hkv, _ = k.shape
-    group = hq // hkv
-    pos = A.query_positions(kv_len, q_len)
-    probs = np.zeros((q_len, hq, kv_len))
-    for h in range(hq):
-        g = h // group
-        mask = A.visibility_mask(pos, kv_len, windows[g])
-        s = scale * (q[:, h, :] @ k[:, g, :].T)
-        s = np.where(mask, s, -np.inf)
-        mx = s.max(axis=1, keepdims=True)
-        e = np.where(mask, np.exp(s - mx), 0.0)
-        probs[:, h, :] = e / e.sum(axis=1, keepdims=True)
-    return probs
-
-
 def token_scores(q, k, windows, scale, all_keys=False):
     """Attention mass received by each key of the query chunk (or by every
-    key when all_keys is set).  The same probabilities as ``probabilities``,
-    added up one query head at a time so that large inputs fit in memory."""
+    key when all_keys is set): the normalised probabilities P[t, h, j]
+    (zero where j is not visible to row t of head h), added up over rows
+    one query head at a time so that large inputs fit in memory."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     q_len, hq, _ = q.shape

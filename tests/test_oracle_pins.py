@@ -29,35 +29,13 @@ from oracle import attention as A
 from oracle import ledger as LG
 from oracle import segments as SG
 
+from brute import brute_attention as _brute
+
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
 def _rand_bf16(rng, shape, scale=1.0):
     return wl.to_bf16_bits(rng.standard_normal(shape).astype(np.float32) * np.float32(scale))
-
-
-def _brute(q, k, v, kv_len, windows, scale):
-    """Pure-Python reference written from the visibility reading:
-    key j is visible to a query at p iff j <= p and (W == 0 or j > p - W)."""
-    q_len, hq, d = q.shape
-    hkv = k.shape[1]
-    grp = hq // hkv
-    o = np.zeros((q_len, hq, d))
-    lse = np.zeros((q_len, hq))
-    for t in range(q_len):
-        p = kv_len - q_len + t
-        for h in range(hq):
-            g = h // grp
-            w = windows[g]
-            js = [j for j in range(kv_len) if j <= p and (w == 0 or j > p - w)]
-            s = [scale * sum(q[t, h, c] * k[j, g, c] for c in range(d)) for j in js]
-            mx = max(s)
-            ex = [math.exp(x - mx) for x in s]
-            tot = sum(ex)
-            lse[t, h] = mx + math.log(tot)
-            for c in range(d):
-                o[t, h, c] = sum(e * v[j, g, c] for e, j in zip(ex, js)) / tot
-    return o, lse
 
 
 @pytest.mark.parametrize("case", [
