@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdlib>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -148,6 +149,12 @@ struct segkv_ctx {
   // Pages are shared between forked sequences; a page returns to the free
   // list when its last holder drops it.
   int32_t take_page() {
+    // The caller has checked that the batch fits; an empty list here is a
+    // bug in that check, never a state to continue from.
+    if (free_list.empty()) {
+      std::fprintf(stderr, "segkv: internal error: page allocation from an empty free list\n");
+      std::abort();
+    }
     const int32_t id = free_list.back();
     free_list.pop_back();
     refcnt[static_cast<size_t>(id)] = 1;
@@ -846,10 +853,23 @@ int segkv_append_pages(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_
     }
   }
 
-  // Commit: trim, then copy shared tails and allocate, then record scatter
-  // work.  A copied page's reference is dropped only after every allocation
-  // of the call, so a page that this launch reads as a copy source is never
-  // handed out (and written) by the same launch.
+  // Commit in two phases.  First every trim of the batch returns its pages,
+  // so that the check above (which counted them as available) holds for
+  // each allocation that follows, whatever the order of growing and
+  // trimming heads and sequences.  Then shared tails are copied, pages are
+  // allocated and scatter work is recorded.  A copied page's reference is
+  // dropped only after every allocation of the call, so a page that this
+  // launch reads as a copy source is never handed out (and written) by the
+  // same launch.
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    for (int32_t g = 0; g < c->Hkv; ++g) {
+      Segment &sg = c->seg(layer, seq_ids[b], g);
+      const int32_t *pl = &plan[(static_cast<size_t>(b) * c->Hkv + g) * kPlan];
+      for (int32_t i = 0; i < pl[1]; ++i) c->drop_page(sg.live()[i]);
+      sg.drop_front(pl[1]);
+      sg.first_token = pl[0];
+    }
+  }
   ScatterItem *items = reinterpret_cast<ScatterItem *>(stage);
   int64_t it = 0;
   std::vector<int32_t> &cow_src = c->scratch_release;
@@ -861,9 +881,6 @@ int segkv_append_pages(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_
     for (int32_t g = 0; g < c->Hkv; ++g) {
       Segment &sg = c->seg(layer, seq_ids[b], g);
       const int32_t *pl = &plan[(static_cast<size_t>(b) * c->Hkv + g) * kPlan];
-      for (int32_t i = 0; i < pl[1]; ++i) c->drop_page(sg.live()[i]);
-      sg.drop_front(pl[1]);
-      sg.first_token = pl[0];
       int32_t cow_from = -1;
       if (pl[4]) {
         int32_t &tail = sg.pages[sg.head + static_cast<size_t>(pl[2] - 1)];

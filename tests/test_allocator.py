@@ -182,3 +182,32 @@ def test_empty_batches_are_no_ops():
     kv.append_pages(0, [], [], [])
     kv.append_pages(0, [0], [0], [0])
     assert kv.free_pages() == 10
+
+
+def test_growing_head_before_trimming_head_in_one_append():
+    """A global head that grows is planned before a local head that trims in
+    the same append; the pool only fits once the trim has returned its
+    pages, so every trim of the call must land before any allocation."""
+    kv = ctx([0, 16], page=16, pages=9, seqs=1)
+    kv.append_pages(0, [0], [64], [64])          # 4 + 4 pages of 9
+    assert kv.free_pages() == 1
+    kv.append_pages(0, [0], [32], [1])           # global +2, local -4 +1
+    check_pool(kv, 1, 1, 2)
+    assert [len(kv.page_table(0, 0, g)[2]) for g in range(2)] == [6, 1]
+    assert kv.page_table(0, 0, 1)[0] == 80
+    assert kv.free_pages() == 2
+
+
+def test_growing_sequence_before_trimming_sequence_in_one_batch():
+    """Sequence 0 grows and sequence 1 trims in one batched append: the
+    allocation for sequence 0 needs the pages sequence 1 gives back."""
+    kv = ctx([16], page=16, pages=6, seqs=2)
+    kv.append_pages(0, [1], [64], [64])          # 4 pages
+    kv.append_pages(0, [0], [16], [16])          # 1 page
+    assert kv.free_pages() == 1
+    kv.append_pages(0, [0, 1], [32, 1], [32, 1])  # seq 0: +2; seq 1: -3 +1
+    check_pool(kv, 1, 2, 1)
+    assert len(kv.page_table(0, 0, 0)[2]) == 3
+    ft, kl, ids = kv.page_table(0, 1, 0)
+    assert (ft, kl, len(ids)) == (48, 65, 2)
+    assert kv.free_pages() == 1
