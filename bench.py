@@ -4,41 +4,49 @@
 One step = one pass of the attention hot path over one batch of the
 workload: release the batch's sequences, append their cache fill (no
 queries) and their query tokens (page allocation, table upload, KV
-scatter), then run varlen prefill.  Inputs are resident in HBM before the
-timed region.
+scatter), then run varlen prefill (and the combine of split rows).  Inputs
+are resident in HBM before the timed region.
 
-Headline: the Mistral-7B-shaped layer prefill (1 sequence, L = 8192, 32
-query / 8 KV heads, D = 128, 1 global + 7 local KV heads with W = 1024,
-page 64, random page order).  value = visible-token TFLOP/s = 4 * D *
-(visible (query head, query, key) pairs) per step / step time.
+Headline: the Llama-3.3-70B-shaped varlen layer prefill, the largest
+workload that fits one GPU (4 sequences of [29127, 12589, 8841, 23919]
+tokens, 64 query / 8 KV heads, D = 128, 1 global + 7 local KV heads with
+W = 2048, page 64, random page order).  value = visible-token TFLOP/s = 4 *
+D * (visible (query head, query, key) pairs) per step / step time.
 
 In the same JSON line:
-  roofline      the prefill kernel's rate from HIP events recorded around
-                each launch on the library's stream, against the 2.5 PFLOP/s
-                dense bf16 MFMA peak (traffic: rocprofv3 counter bytes when
-                they were taken on the current kernel source, else null);
+  roofline      the prefill's kernel rate: visible FLOPs over the prefill
+                launch plus its combine launch, both timed by HIP events that
+                the library records around each launch on its stream, against
+                the 2.5 PFLOP/s dense bf16 MFMA peak (traffic: rocprofv3
+                counter bytes when they were taken on the current kernel
+                source, else null);
   all_global    the same steps with every head forced global;
-  relocation    query-side RoPE relocation: the same prefill and decode with
-                every local head's queries relocated by a document offset
-                (the global head at offset 0), and the cost over the plain
-                kernels;
   protocol      3 unmeasured + 10 measured (segmented, all-global) pairs,
-                p50 / p95 of the prefill kernel time;
+                p50 / p95 of prefill + combine kernel time;
+  workloads     the 128K chunked prefill (122880 cached + 8192 queries) and
+                the Mistral-7B-shaped L = 8192 prefill, each with the same
+                fields;
+  relocation    query-side RoPE relocation: the headline prefill and the
+                decode with every local head's queries relocated by a
+                document offset (global heads at offset 0), and the cost over
+                the plain kernels;
   decode        visible-KV GB/s of split-KV decode + combine at 32K x 31
-                sequences against 8 TB/s, and its all-global arm;
-  router        attention-mass token scores of the headline prefill (a second
-                MFMA pass over the visible pairs, QK only: 2 D FLOPs per pair)
-                and the top-k (k = L/4) that routes tokens to the dense FFN;
-  merge         the head-decomposition merge of a reused 128K-token document
-                (offline Local-head partials, online Global heads and
-                protected rows, LSE merge on the window's boundary rows):
+                sequences against 8 TB/s, its all-global arm and the oracle's
+                rate on the host;
+  router        attention-mass token scores of the Mistral-7B-shaped prefill
+                (a second MFMA pass over the visible pairs, QK only: 2 D FLOPs
+                per pair) and the top-k (k = L/4) that routes tokens to the
+                dense FFN;
+  merge         the head-decomposition merge of a reused 128K-token document:
                 algorithmic GB/s against 8 TB/s;
   fork          copy-on-write forks: the 32K x 31 decode with the 31 sequences
-                forked from one 32767-token parent (each appends its own query
-                token): pages in use against 31 unshared copies, forks that fit
-                in the unshared pool, and the decode kernel over the forks;
-  workloads     the varlen Llama-3.3-70B-shaped and the 128K chunked prefill;
+                forked from one 32767-token parent: pages in use against 31
+                unshared copies, and the decode kernel over the forks;
   cpu_baseline  the fp64 oracle on a bounded sample of the headline workload.
+
+Warm-up: each arm first runs its own step until 0.25 s of wall time has
+passed (the GPU's clock settles under sustained load and drops back when it
+idles), then the W warm-up steps, then the K timed steps.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -105,6 +113,19 @@ def kernel_avg(ctx, kernel):
 
 # --------------------------------------------------------------- prefill
 
+WARM_CLOCK_S = 0.25
+
+
+def warm_clock(step):
+    """Run ``step`` until WARM_CLOCK_S of wall time has passed (untimed)."""
+    t0 = time.perf_counter()
+    while True:
+        step()
+        sync()
+        if time.perf_counter() - t0 >= WARM_CLOCK_S:
+            return
+
+
 def prefill_arm(w, dev, steps, warmup, windows=None, split_tiles=None, deltas=None):
     import torch
     from long_context_serving_amd import runner as R
@@ -120,6 +141,7 @@ def prefill_arm(w, dev, steps, warmup, windows=None, split_tiles=None, deltas=No
         run.load()
         run.prefill(o, lse)
 
+    warm_clock(step)
     for _ in range(warmup):
         step()
     sync()
@@ -137,21 +159,25 @@ def prefill_arm(w, dev, steps, warmup, windows=None, split_tiles=None, deltas=No
         step()
     sync()
     k_ms, k_n = kernel_avg(run.ctx, S.KERNEL_PREFILL)
-    c_ms, _ = kernel_avg(run.ctx, S.KERNEL_COMBINE)
+    c_ms, c_n = kernel_avg(run.ctx, S.KERNEL_COMBINE)
     run.ctx.set_timing(True, [S.KERNEL_SCATTER])
-    for _ in range(max(2, steps // 4)):
+    n_sc = max(2, steps // 4)
+    for _ in range(n_sc):
         step()
     sync()
     s_ms, s_n = kernel_avg(run.ctx, S.KERNEL_SCATTER)
     run.ctx.set_timing(False)
+    # combine time per step (a step has a combine launch only when rows are split)
+    c_step = c_ms * c_n / max(k_n, 1)
     return run, {"ms_per_step": dt * 1e3, "prefill_kernel_ms": k_ms, "prefill_launches": k_n,
-                 "combine_kernel_ms": c_ms, "scatter_kernel_ms_per_launch": s_ms,
-                 "scatter_launches_per_step": s_n / max(max(2, steps // 4), 1)}
+                 "combine_kernel_ms": c_step, "scatter_kernel_ms_per_launch": s_ms,
+                 "scatter_launches_per_step": s_n / n_sc}
 
 
 def paired_protocol(run_a, run_b, warm=3, measured=10):
     """The pages' timing protocol at kernel level: unmeasured warm pairs, then
-    measured (segmented, all-global) pairs; returns per-arm kernel times."""
+    measured (segmented, all-global) pairs; returns per-arm prefill +
+    combine kernel times."""
     from long_context_serving_amd import segkv as S
     times = {"segmented": [], "all_global": []}
     for i in range(warm + measured):
@@ -168,6 +194,47 @@ def paired_protocol(run_a, run_b, warm=3, measured=10):
     return {k: {"p50_ms": pct(v, 50), "p95_ms": pct(v, 95)} for k, v in times.items()}
 
 
+def prefill_report(w, dev, steps, warmup, with_global=True, with_protocol=True):
+    """Segmented arm (kept open for later arms) and its report: step rate,
+    kernel roofline over prefill + combine, the all-global arm and the
+    paired protocol."""
+    from long_context_serving_amd import metrics as M
+    flops = M.prefill_flops(w)
+    g = (0,) * w.num_kv_heads
+    flops_g = M.prefill_flops(w, windows=g)
+    log(f"prefill {w.name} segmented")
+    run, seg = prefill_arm(w, dev, steps, warmup)
+    log(f"  {seg}")
+    kern = seg["prefill_kernel_ms"] + seg["combine_kernel_ms"]
+    achieved = flops / (kern * 1e-3) / 1e12
+    rep = {
+        "workload": w.name, "value": flops / (seg["ms_per_step"] * 1e-3) / 1e12, "unit": "TFLOP/s",
+        "visible_flops": flops, "ms_per_step": seg["ms_per_step"],
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic("prefill_" + w.name),
+                     "kernel": f"prefill_kernel<{w.head_dim},{w.page_size}> + combine_kernel<{w.head_dim}>",
+                     "avg_launch_ms": seg["prefill_kernel_ms"], "combine_ms_per_step": seg["combine_kernel_ms"],
+                     "prefill_launch_only_tflops": flops / (seg["prefill_kernel_ms"] * 1e-3) / 1e12},
+        "step_breakdown": seg,
+    }
+    if with_global:
+        log(f"prefill {w.name} all-global")
+        run_g, glob = prefill_arm(w, dev, steps, warmup, windows=g)
+        log(f"  {glob}")
+        kern_g = glob["prefill_kernel_ms"] + glob["combine_kernel_ms"]
+        rep["all_global"] = {
+            "value": flops_g / (glob["ms_per_step"] * 1e-3) / 1e12, "unit": "TFLOP/s", "visible_flops": flops_g,
+            "ms_per_step": glob["ms_per_step"], "prefill_kernel_ms": glob["prefill_kernel_ms"],
+            "combine_kernel_ms": glob["combine_kernel_ms"], "kernel_tflops": flops_g / (kern_g * 1e-3) / 1e12,
+            "kernel_frac": flops_g / (kern_g * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "segmented_speedup_step": glob["ms_per_step"] / seg["ms_per_step"],
+            "segmented_speedup_kernel": kern_g / kern}
+        if with_protocol:
+            rep["protocol"] = paired_protocol(run, run_g)
+        run_g.close()
+    return run, rep
+
+
 # ---------------------------------------------------------------- decode
 
 def decode_arm(w, dev, steps, warmup, windows=None, deltas=None):
@@ -177,6 +244,7 @@ def decode_arm(w, dev, steps, warmup, windows=None, deltas=None):
     run = R.WorkloadRun(w, dev, windows=windows, deltas=deltas).load()
     o = torch.empty_like(dev.q)
     lse = torch.empty(dev.q.shape[:2], dtype=torch.float32, device=dev.q.device)
+    warm_clock(lambda: run.decode(o, lse))
     for _ in range(warmup):
         run.decode(o, lse)
     sync()
@@ -210,9 +278,14 @@ def router_arm(w, dev, steps, warmup, flops_qk):
     scores = torch.empty(dev.q.shape[0], dtype=torch.float32, device=dev.q.device)
     k = [n // 4 for n in w.q_lens]
     idx = torch.empty(sum(k), dtype=torch.int32, device=dev.q.device)
-    for _ in range(warmup):
+
+    def call():
         run.ctx.token_scores(0, run.seq_ids, w.q_lens, dev.q, lse, scores)
         run.ctx.topk(w.q_lens, scores, k, idx)
+
+    warm_clock(call)
+    for _ in range(warmup):
+        call()
     sync()
     # Call time without timing events, then kernel times over as many calls.
     t0 = time.perf_counter()
@@ -253,6 +326,7 @@ def merge_arm(mw, steps, warmup):
     del mi
     o = torch.empty_like(args[0])
     lse = torch.empty_like(args[1])
+    warm_clock(lambda: ctx.merge(*args, o=o, lse=lse))
     for _ in range(warmup):
         ctx.merge(*args, o=o, lse=lse)
     sync()
@@ -306,6 +380,7 @@ def fork_arm(dw, steps, warmup, pages_unshared):
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
     ids = list(range(n))
+    warm_clock(lambda: ctx.decode(0, ids, q, o, lse))
     for _ in range(warmup):
         ctx.decode(0, ids, q, o, lse)
     sync()
@@ -333,30 +408,38 @@ def local_head_deltas(w, offset):
     return [[offset if win > 0 else 0 for win in w.windows] for _ in range(w.n_seqs)]
 
 
-def cpu_baseline(w, x, budget_s=15.0):
-    """The fp64 oracle, as it stands, on a seeded sample of query rows of the
-    workload (all heads), timed on the host cores."""
-    from oracle import attention as A
-    from long_context_serving_amd import metrics as M
-    threads = None
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads") or 0) for i in threadpool_info()) or None
+        return max((i.get("num_threads") or 0) for i in threadpool_info()) or None
     except Exception:
-        pass
+        return None
+
+
+def cpu_baseline(w, x, budget_s=15.0):
+    """The fp64 oracle, as it stands, on a seeded sample of query rows of the
+    workload (all heads; rows spread over the sequences in proportion to
+    their query counts), timed on the host cores."""
+    from oracle import attention as A
+    from long_context_serving_amd import metrics as M
+    threads = _blas_threads()
     rng = np.random.default_rng(2024)
-    q_len = w.q_lens[0]
+    q_tot = sum(w.q_lens)
 
     def run(n):
-        rows = np.sort(rng.choice(q_len, size=min(n, q_len), replace=False))
+        rows = []
+        for b, ql in enumerate(w.q_lens):
+            nb = max(1, int(round(n * ql / q_tot))) if ql else 0
+            rows.append(np.sort(rng.choice(ql, size=min(nb, ql), replace=False)) if nb else np.zeros(0, np.int64))
         t0 = time.perf_counter()
-        A.attend_batch(x.q, x.k, x.v, x.cu_q, x.cu_kv, w.windows, w.scale, rows_per_seq=[rows])
-        return time.perf_counter() - t0, M.prefill_flops_rows(w, 0, rows), len(rows)
+        A.attend_batch(x.q, x.k, x.v, x.cu_q, x.cu_kv, w.windows, w.scale, rows_per_seq=rows)
+        dt = time.perf_counter() - t0
+        return dt, sum(M.prefill_flops_rows(w, b, r) for b, r in enumerate(rows)), sum(len(r) for r in rows)
 
     n = 64
     t, flops, n = run(n)
-    while t < budget_s / 3 and n < q_len:   # grow the sample until it is ~budget_s of work
-        n = int(min(q_len, n * max(2.0, min(8.0, budget_s / max(t, 1e-3)))))
+    while t < budget_s / 3 and n < q_tot:   # grow the sample until it is ~budget_s/3 of work
+        n = int(min(q_tot, n * max(2.0, min(8.0, budget_s / 3 / max(t, 1e-3)))))
         t, flops, n = run(n)
     reps = 1
     if t < budget_s / 3:                     # the whole workload is cheap: repeat it
@@ -367,22 +450,48 @@ def cpu_baseline(w, x, budget_s=15.0):
         t = (time.perf_counter() - t0) / reps
     out = {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads or os.cpu_count(),
            "kind": "oracle",
-           "sample": f"{n} of {q_len} query rows (seeded), all {w.num_q_heads} query heads, of "
-                     f"{w.name}; {t:.1f} s per pass, {reps} pass(es); fp64 numpy, BLAS threads={threads}, host cpus={os.cpu_count()}"}
-    # The same oracle on one thread, on a smaller sample (about a third of the budget).
+           "sample": f"{n} of {q_tot} query rows (seeded, spread over the {w.n_seqs} sequences), all "
+                     f"{w.num_q_heads} query heads, of {w.name}; {t:.1f} s per pass, {reps} pass(es); fp64 "
+                     f"numpy, BLAS threads={threads}, host cpus={os.cpu_count()}"}
     try:
         from threadpoolctl import threadpool_limits
     except ImportError:
         return out
     with threadpool_limits(limits=1):
-        n1 = 16
+        n1 = 8
         t1, f1, n1 = run(n1)
-        while t1 < budget_s / 9 and n1 < q_len:
-            n1 = int(min(q_len, n1 * max(2.0, min(8.0, budget_s / 3 / max(t1, 1e-3)))))
+        while t1 < budget_s / 9 and n1 < q_tot:
+            n1 = int(min(q_tot, n1 * max(2.0, min(8.0, budget_s / 9 / max(t1, 1e-3)))))
             t1, f1, n1 = run(n1)
     out["single_thread"] = {"value": f1 / t1 / 1e12, "unit": "TFLOP/s", "cores": 1,
-                            "sample": f"{n1} of {q_len} query rows (seeded), {t1:.1f} s"}
+                            "sample": f"{n1} of {q_tot} query rows (seeded), {t1:.1f} s"}
     return out
+
+
+def cpu_baseline_decode(w, x, budget_s=8.0):
+    """The fp64 oracle on the decode workload's sequences (one query row each,
+    all heads), as visible-KV GB/s: the same algorithmic bytes as the GPU
+    figure, over the oracle's wall time, on a growing prefix of the batch."""
+    from oracle import attention as A
+    from long_context_serving_amd import metrics as M
+    threads = _blas_threads()
+    by = M.decode_bytes(w)["total"] / w.n_seqs
+
+    def run(n):
+        t0 = time.perf_counter()
+        cu_q = x.cu_q[:n + 1]
+        cu_kv = x.cu_kv[:n + 1]
+        A.attend_batch(x.q, x.k, x.v, cu_q, cu_kv, w.windows, w.scale)
+        return time.perf_counter() - t0
+
+    n = 1
+    t = run(n)
+    while t < budget_s / 2 and n < w.n_seqs:
+        n = min(w.n_seqs, n * 2)
+        t = run(n)
+    return {"value": by * n / t / 1e9, "unit": "GB/s", "cores": threads or os.cpu_count(), "kind": "oracle",
+            "sample": f"{n} of {w.n_seqs} sequences of {w.name} (one query row, all {w.num_q_heads} heads), "
+                      f"{t:.1f} s; fp64 numpy, BLAS threads={threads}, host cpus={os.cpu_count()}"}
 
 
 # ------------------------------------------------------------------ main
@@ -390,15 +499,13 @@ def cpu_baseline(w, x, budget_s=15.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # The GPU reaches its steady clock after ~100 headline steps (~40 ms of
-    # work) and drops back within a second of idling, so every arm warms up
-    # with its own W untimed steps.
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "merge", "router"], default="all",
-                    help="profiling runs: only the segmented headline prefill, or only segmented decode")
+    ap.add_argument("--only", choices=["all", "prefill", "chunk", "mistral", "decode", "merge", "router"],
+                    default="all",
+                    help="profiling runs: only the segmented headline prefill, the 128K chunk, the Mistral-7B-shaped "
+                         "prefill, segmented decode, the merge or the router")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-secondary", action="store_true", help="skip the varlen and 128K prefill workloads")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -426,88 +533,97 @@ def main():
 
     from long_context_serving_amd import metrics as M
     from long_context_serving_amd import runner as R
-    from long_context_serving_amd import segkv as S
     from long_context_serving_amd import workloads as wl
+    from long_context_serving_amd import segkv as S
     S.load_library()
     K, Wm = args.steps, args.warmup
-    out = {}
+    full = args.only == "all"
+    out = {"metric": METRIC, "n_gpus": 1, "steps": K, "warmup": Wm, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded N(0,1) bf16 Q/K/V; no weights or datasets)"}
 
-    headline = wl.MISTRAL7B_PREFILL
-    flops = M.prefill_flops(headline)
-    flops_g = M.prefill_flops(headline, windows=(0,) * headline.num_kv_heads)
+    def line(rep, config):
+        out.update({"value": rep["value"], "unit": rep["unit"], "ms_per_step": rep["ms_per_step"],
+                    "config": config, "roofline": rep["roofline"]})
+
+    headline = wl.LLAMA70B_VARLEN_PREFILL
     if args.only in ("all", "prefill"):
-        log(f"inputs {headline.name}")
-        x2 = wl.make_inputs(headline)
-        dev2 = R.to_device(headline, x2)
-        log("prefill segmented")
-        run_seg, seg = prefill_arm(headline, dev2, K, Wm)
-        log(f"  {seg}")
-        if args.only == "all":
-            log("prefill all-global")
-            run_glob, glob = prefill_arm(headline, dev2, K, Wm, windows=(0,) * headline.num_kv_heads)
-            log(f"  {glob}")
-            proto = paired_protocol(run_seg, run_glob)
-            run_glob.close()
-            log("router (token scores + top-k)")
-            out["router"] = router_arm(headline, dev2, K, Wm, flops // 2)
-            log(f"  {out['router']}")
-            log("prefill relocated")
-            run_rel, rel = prefill_arm(headline, dev2, K, Wm, deltas=local_head_deltas(headline, RELOCATION_OFFSET))
-            run_rel.close()
+        log(f"inputs {headline.name} lengths {list(headline.kv_lens)}")
+        x3 = wl.make_inputs(headline)
+        dev3 = R.to_device(headline, x3)
+        run3, rep3 = prefill_report(headline, dev3, K, Wm, with_global=full, with_protocol=full)
+        run3.close()
+        line(rep3, {"workload": headline.name, "global_batch": headline.n_seqs,
+                    "seq_lens": list(headline.kv_lens), "num_q_heads": headline.num_q_heads,
+                    "num_kv_heads": headline.num_kv_heads, "head_dim": headline.head_dim,
+                    "page_size": headline.page_size, "head_windows": "1 global + 7 local W=2048",
+                    "visible_flops": rep3["visible_flops"], "parallelism": "none (1 GPU)"})
+        out["step_breakdown"] = rep3["step_breakdown"]
+        for k in ("all_global", "protocol"):
+            if k in rep3:
+                out[k] = rep3[k]
+        if full:
+            log("prefill relocated (headline)")
+            run_r, rel = prefill_arm(headline, dev3, K, Wm, deltas=local_head_deltas(headline, RELOCATION_OFFSET))
+            run_r.close()
             log(f"  {rel}")
-        run_seg.close()
-        achieved = flops / (seg["prefill_kernel_ms"] * 1e-3) / 1e12
-        traffic = measured_traffic("prefill_" + headline.name)
-        out.update({
-            "metric": METRIC, "value": flops / (seg["ms_per_step"] * 1e-3) / 1e12, "unit": "TFLOP/s",
-            "n_gpus": 1, "steps": K, "warmup": Wm, "ms_per_step": seg["ms_per_step"],
-            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-            "data": "synthetic (seeded N(0,1) bf16 Q/K/V; no weights or datasets)",
-            "config": {"workload": headline.name, "global_batch": 1, "seq_len": 8192, "num_q_heads": 32,
-                       "num_kv_heads": 8, "head_dim": 128, "page_size": 64,
-                       "head_windows": "1 global + 7 local W=1024", "visible_flops": flops,
-                       "parallelism": "none (1 GPU)"},
-            "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
-                         "kernel": "prefill_kernel<128,64>", "avg_launch_ms": seg["prefill_kernel_ms"]},
-            "step_breakdown": seg,
-        })
-        if args.only == "all":
-            out.update({
-            "all_global": {"value": flops_g / (glob["ms_per_step"] * 1e-3) / 1e12, "unit": "TFLOP/s",
-                           "visible_flops": flops_g, "ms_per_step": glob["ms_per_step"],
-                           "prefill_kernel_ms": glob["prefill_kernel_ms"],
-                           "kernel_tflops": flops_g / (glob["prefill_kernel_ms"] * 1e-3) / 1e12,
-                           "segmented_speedup_step": glob["ms_per_step"] / seg["ms_per_step"],
-                           "segmented_speedup_kernel": glob["prefill_kernel_ms"] / seg["prefill_kernel_ms"]},
-            "protocol": proto,
-            "relocation": {"offset": RELOCATION_OFFSET, "prefill": {
-                "kernel_tflops": flops / (rel["prefill_kernel_ms"] * 1e-3) / 1e12,
-                "step_tflops": flops / (rel["ms_per_step"] * 1e-3) / 1e12,
-                "prefill_kernel_ms": rel["prefill_kernel_ms"],
-                "kernel_time_over_plain": rel["prefill_kernel_ms"] / seg["prefill_kernel_ms"]}},
-        })
-        del dev2
+            kr = rel["prefill_kernel_ms"] + rel["combine_kernel_ms"]
+            kp = rep3["step_breakdown"]["prefill_kernel_ms"] + rep3["step_breakdown"]["combine_kernel_ms"]
+            out["relocation"] = {"offset": RELOCATION_OFFSET, "prefill": {
+                "workload": headline.name, "kernel_tflops": rep3["visible_flops"] / (kr * 1e-3) / 1e12,
+                "step_tflops": rep3["visible_flops"] / (rel["ms_per_step"] * 1e-3) / 1e12,
+                "prefill_kernel_ms": rel["prefill_kernel_ms"], "combine_kernel_ms": rel["combine_kernel_ms"],
+                "kernel_time_over_plain": kr / kp}}
+        if not args.no_cpu_baseline:
+            log("cpu baseline (oracle, headline)")
+            out["cpu_baseline"] = cpu_baseline(headline, x3)
+        del dev3, x3
+
+    secondary = {}
+    for w, key in ((wl.CHUNKED_PREFILL_128K, "chunk"), (wl.MISTRAL7B_PREFILL, "mistral")):
+        if not (full or args.only == key):
+            continue
+        log(f"inputs {w.name}")
+        x = wl.make_inputs(w)
+        dev = R.to_device(w, x)
+        del x
+        run, rep = prefill_report(w, dev, K, Wm, with_global=full, with_protocol=full)
+        if full and w is wl.MISTRAL7B_PREFILL:
+            run.close()
+            log("router (token scores + top-k)")
+            out["router"] = router_arm(w, dev, K, Wm, M.prefill_flops(w) // 2)
+            log(f"  {out['router']}")
+        else:
+            run.close()
+        secondary[w.name] = rep
+        if args.only == key:
+            line(rep, {"workload": w.name, "global_batch": w.n_seqs, "seq_lens": list(w.kv_lens),
+                       "q_lens": list(w.q_lens)})
+        del dev
+    if secondary:
+        out["workloads"] = secondary
 
     if args.only == "router":
-        log(f"inputs {headline.name}")
-        dev2 = R.to_device(headline, wl.make_inputs(headline))
-        out["router"] = router_arm(headline, dev2, K, Wm, flops // 2)
-        del dev2
+        w = wl.MISTRAL7B_PREFILL
+        dev = R.to_device(w, wl.make_inputs(w))
+        m = router_arm(w, dev, K, Wm, M.prefill_flops(w) // 2)
+        out["router"] = m
+        out.update({"value": m["roofline"]["achieved"], "unit": "TFLOP/s", "ms_per_step": m["ms_per_call"],
+                    "config": {"workload": m["workload"]}, "roofline": m["roofline"]})
+        del dev
 
     if args.only in ("all", "decode"):
         dw = wl.DECODE_32K
         log(f"inputs {dw.name}")
         x4 = wl.make_inputs(dw)
         dev4 = R.to_device(dw, x4)
-        del x4
         by = M.decode_bytes(dw)
         by_g = M.decode_bytes(dw, windows=(0,) * dw.num_kv_heads)
         log("decode segmented")
         d = decode_arm(dw, dev4, K, Wm)
         log(f"  {d}")
         dg = dr = None
-        if args.only == "all":
+        if full:
             log("decode all-global")
             dg = decode_arm(dw, dev4, K, Wm, windows=(0,) * dw.num_kv_heads)
             log(f"  {dg}")
@@ -520,11 +636,13 @@ def main():
             "value": by["total"] / (kern * 1e-3) / 1e9,
             "value_step": by["total"] / (d["ms_per_step"] * 1e-3) / 1e9,
             "visible_bytes": by,
-            "roofline": {"bound": "hbm", "achieved": by["total"] / (d["split_kernel_ms"] * 1e-3) / 1e9,
+            "roofline": {"bound": "hbm", "achieved": by["total"] / (kern * 1e-3) / 1e9,
                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": by["total"] / (d["split_kernel_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         "frac": by["total"] / (kern * 1e-3) / 1e9 / PEAK_HBM_GBS,
                          "traffic": measured_traffic("decode_" + dw.name),
-                         "kernel": "decode_kernel<128,64>", "avg_launch_ms": d["split_kernel_ms"]},
+                         "kernel": "decode_kernel<128,64> + combine_kernel<128>",
+                         "avg_launch_ms": d["split_kernel_ms"], "combine_ms": d["combine_kernel_ms"]},
+            "frac_split_only": by["total"] / (d["split_kernel_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "frac_split_plus_combine": by["total"] / (kern * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "detail": d,
         }
@@ -537,62 +655,29 @@ def main():
             out.setdefault("relocation", {"offset": RELOCATION_OFFSET})["decode"] = {
                 "value": by["total"] / (kern_r * 1e-3) / 1e9, "unit": "GB/s", "detail": dr,
                 "kernel_time_over_plain": kern_r / kern}
+        if not args.no_cpu_baseline:
+            log("cpu baseline (oracle, decode)")
+            dec["cpu_baseline"] = cpu_baseline_decode(dw, x4)
         out["decode"] = dec
-        del dev4
-        if args.only == "all":
+        del dev4, x4
+        if full:
             log("decode over forks")
             out["fork"] = fork_arm(dw, K, Wm, d["pages_in_use"])
             log(f"  {out['fork']}")
+        if args.only == "decode":
+            out.update({"value": dec["value"], "unit": "GB/s", "ms_per_step": d["ms_per_step"],
+                        "config": {"workload": dw.name}, "roofline": dec["roofline"]})
 
     if args.only in ("all", "merge"):
         log(f"merge {wl.MERGE_128K.name}")
-        out["merge"] = merge_arm(wl.MERGE_128K, K, Wm)
-        log(f"  {out['merge']['value']:.1f} GB/s, kernel {out['merge']['kernel_ms']:.4f} ms")
+        m = merge_arm(wl.MERGE_128K, K, Wm)
+        out["merge"] = m
+        log(f"  {m['value']:.1f} GB/s, kernel {m['kernel_ms']:.4f} ms")
+        if args.only == "merge":
+            out.update({"value": m["value"], "unit": "GB/s", "ms_per_step": m["ms_per_call"],
+                        "config": {"workload": m["workload"]}, "roofline": m["roofline"]})
 
-    if args.only == "all" and not args.no_secondary:
-        sec = {}
-        for w, split in ((wl.LLAMA70B_VARLEN_PREFILL, None), (wl.CHUNKED_PREFILL_128K, None)):
-            log(f"inputs {w.name}")
-            x = wl.make_inputs(w)
-            dev = R.to_device(w, x)
-            del x
-            f = M.prefill_flops(w)
-            steps = max(2, K // 8)
-            run, r = prefill_arm(w, dev, steps, max(1, Wm // 8), split_tiles=split)
-            run.close()
-            sec[w.name] = {"visible_flops": f, "steps": steps, "step_tflops": f / (r["ms_per_step"] * 1e-3) / 1e12,
-                           "kernel_tflops": f / ((r["prefill_kernel_ms"] + r["combine_kernel_ms"]) * 1e-3) / 1e12,
-                           "frac_of_peak": f / ((r["prefill_kernel_ms"] + r["combine_kernel_ms"]) * 1e-3) / 1e12
-                           / PEAK_BF16_TFLOPS, "detail": r}
-            log(f"  {sec[w.name]}")
-            del dev
-        out["workloads"] = sec
-
-    if args.only in ("all", "prefill") and not args.no_cpu_baseline:
-        log("cpu baseline (oracle)")
-        out["cpu_baseline"] = cpu_baseline(headline, wl.make_inputs(headline))
-    elif "value" in out:
-        out["cpu_baseline"] = None
-
-    if "value" not in out and args.only == "router":  # profiling runs still print one line
-        m = out["router"]
-        out = {"metric": METRIC, "value": m["roofline"]["achieved"], "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
-               "warmup": Wm, "ms_per_step": m["ms_per_call"], "higher_is_better": True, "scaling": "weak",
-               "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": {"workload": m["workload"]},
-               "roofline": m["roofline"], "cpu_baseline": None, "router": m}
-    if "value" not in out and args.only == "merge":  # profiling runs still print one line
-        m = out["merge"]
-        out = {"metric": METRIC, "value": m["value"], "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": Wm,
-               "ms_per_step": m["ms_per_call"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-               "dtype": "bf16", "data": "synthetic", "config": {"workload": m["workload"]},
-               "roofline": m["roofline"], "cpu_baseline": None, "merge": m}
-    if "value" not in out:  # decode-only runs still print one line
-        dec = out.get("decode", {})
-        out = {"metric": METRIC, "value": dec.get("value"), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": Wm,
-               "ms_per_step": dec.get("detail", {}).get("ms_per_step"), "higher_is_better": True, "scaling": "weak",
-               "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-               "config": {"workload": wl.DECODE_32K.name}, "roofline": dec.get("roofline"), "cpu_baseline": None,
-               "decode": dec}
+    out.setdefault("cpu_baseline", None)
     print(json.dumps(out), flush=True)
 
 

@@ -93,7 +93,37 @@ typedef struct segkv_config {
                              1: interleaved (channels 2i and 2i+1 pair) */
   int32_t rope_dims;      /* rotary channels, the trailing ones of a head; 0 => head_dim; otherwise a
                              multiple of 16 in [16, head_dim].  Leading channels carry no position code. */
+  /* Device scratch of every call: its tables (sequence and segment
+     descriptors, page ids, work lists) and the split partials (o, lse) that
+     the combine merges.  Owned by the caller, 256-byte aligned, at least
+     segkv_workspace_bytes() bytes for the batches the caller will run.  NULL
+     (device contexts): segkv_create allocates workspace_bytes bytes, or
+     segkv_workspace_bytes(cfg, max_batch_q_tokens) when workspace_bytes is 0,
+     and frees them in segkv_destroy.  No call allocates device memory after
+     create.  Ignored by planning-only contexts. */
+  void *workspace;
+  uint64_t workspace_bytes;
+  int32_t max_batch_q_tokens; /* largest query-token count of one prefill or token-score batch that the
+                                 context's own workspace and host staging are sized for; 0 => 16384 */
+  int32_t pad0;
 } segkv_config;
+
+/*
+ * Device workspace that suffices for every call on batches of at most
+ * max_seqs sequences and max_batch_q_tokens query tokens (prefill and token
+ * scores; a decode batch is at most max_seqs sequences), when the segments
+ * listed in one call hold at most num_pages page ids together (always true
+ * without forks; sequences that share pages through segkv_fork list each
+ * shared page once per sequence, so a batch of forks may need more) and the
+ * prefill split knob is automatic.  The bound covers the prefill's split
+ * partials (at most two per resident workgroup), the decode's stream-K
+ * partials (one per segment piece) and the token scores' partial rows (one
+ * per visible (query tile, key tile) pair, which grows with the square of a
+ * global head's chunk).  A call that needs more than the workspace holds
+ * fails with SEGKV_E_NOMEM before it enqueues anything or changes any
+ * state.  Returns 0 for an invalid configuration or a negative token count.
+ */
+size_t segkv_workspace_bytes(const segkv_config *cfg, int32_t max_batch_q_tokens);
 
 /*
  * Create a context.  k_pool and v_pool both NULL gives a planning-only

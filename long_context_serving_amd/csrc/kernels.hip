@@ -699,6 +699,423 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
 }
 
 // ===========================================================================
+// Prefill, wide variant: 4 waves of 64 rows each (one wave per SIMD), so
+// that every K and V^T operand read from LDS feeds two products (one per
+// 32-row column block) instead of one.  The tile loop is software
+// pipelined: while the products S^T = K Q^T of tile i+1 run, the same wave
+// turns tile i's scores into probabilities (exp, row sums, bf16 packing), so
+// the softmax's vector work overlaps the matrix work of one wave instead of
+// relying on a second wave per SIMD.  Then O^T += V^T P^T for tile i.
+// Stage s of a four-stage LDS ring holds one tile's K and V^T; tile i's V^T
+// and tile i+1's K are read in iteration i, tiles i+2 and i+3 are loading.
+// Work items, the queue, the split partials and the output layout are those
+// of prefill_kernel.
+// ===========================================================================
+
+template <int D, int P>
+__global__ __launch_bounds__(kPrefillWideThreads, 1) void prefill_wide_kernel(PrefillArgs a) {
+  using L = PrefillLds<D>;
+  constexpr int NKK = D / 16;  // k-steps of the QK product
+  constexpr int NDB = D / 32;  // 32-channel blocks of O^T
+  constexpr int NW = kPrefillWideThreads / 64;
+  constexpr int K_INSTR = L::K_CHUNKS / kPrefillWideThreads;  // direct loads per lane per tile (K)
+  constexpr int V_INSTR = L::V_CHUNKS / kPrefillWideThreads;  // (V^T)
+  constexpr int NSTAGE = 4;
+  constexpr int LOADS_PER_TILE = K_INSTR + V_INSTR;
+  static_assert(kPrefillRows == 64 * NW, "two 32-row column blocks per wave");
+  static_assert(K_INSTR >= 1 && V_INSTR >= 1, "tile smaller than one load per lane");
+  __shared__ __attribute__((aligned(16))) uint4 smem4[NSTAGE * L::STAGE_BYTES / 16];
+  __shared__ int s_next[2];
+  __shared__ __attribute__((aligned(16))) float s_rope[NW][2 * D];
+  char *smem = reinterpret_cast<char *>(smem4);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int G = a.group;
+  const int rows = a.rows_per_tile;
+  const int n_items = a.n_items;
+
+  if (tid == 0) s_next[0] = atomicAdd(a.counter, 1);
+  __syncthreads();
+  int cur = __builtin_amdgcn_readfirstlane(s_next[0]);
+  if (cur >= n_items) return;
+  int nxt = -1;
+  int fslot = 1;
+
+  // Producer: K/V tile loads run ahead of the consumer along this
+  // workgroup's sequence of tiles, across item boundaries.
+  int p_item = -1, p_tile = 0, p_end = 0;
+  SegDesc psg;
+  auto p_set = [&](int idx) {
+    const PrefillItem pi_ = sload(a.items + idx);
+    p_item = idx;
+    p_tile = pi_.tile_begin;
+    p_end = pi_.tile_end;
+    psg = sload(a.segs + pi_.seq * a.num_kv_heads + pi_.kv_head);
+  };
+  p_set(cur);
+  int issued = 0;  // tiles issued so far (index in this workgroup's tile sequence)
+  int ready = 0;   // tiles known to have landed in LDS and passed a barrier
+  auto issue_tile = [&](int tile, int stage) {
+    const int k0 = tile * kTileKeys;
+    const int last_page = psg.n_pages - 1;
+    char *st = smem + stage * L::STAGE_BYTES;
+    constexpr int NP = kTileKeys / P;
+    int pid[NP];
+    const int pg0 = (k0 - psg.first_token) / P;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) pid[i] = sload(a.page_ids + psg.page_off + min(max(pg0 + i, 0), last_page));
+    auto page_of = [&](int key_in_tile, int *slot) {
+      const int rel = k0 + key_in_tile - psg.first_token;
+      *slot = rel >= 0 && rel / P <= last_page ? key_in_tile % P : 0;
+      int page = pid[0];
+#pragma unroll
+      for (int i = 1; i < NP; ++i)
+        if (key_in_tile / P == i) page = pid[i];
+      return page;
+    };
+#pragma unroll
+    for (int j = 0; j < K_INSTR; ++j) {
+      const int c = (j * NW + wave) * 64 + lane;
+      const int row = c / L::KCPR;
+      const int logical = (c % L::KCPR) ^ L::k_swz(row);
+      const uint16_t *src;
+      if constexpr (P == kTileKeys) {
+        src = a.k_pool + static_cast<size_t>(pid[0]) * (P * D) + row * D + logical * 8;
+      } else {
+        int slot;
+        const int page = page_of(row, &slot);
+        src = a.k_pool + (static_cast<size_t>(page) * P + slot) * D + logical * 8;
+      }
+      lds_dma16(src, st + (j * NW + wave) * 1024);
+    }
+#pragma unroll
+    for (int j = 0; j < V_INSTR; ++j) {
+      const int c = (j * NW + wave) * 64 + lane;
+      const int d = c / 8;
+      const int logical = (c % 8) ^ L::v_swz(d);
+      const uint16_t *src;
+      if constexpr (P == kTileKeys) {
+        src = a.v_pool + static_cast<size_t>(pid[0]) * (P * D) + d * P + logical * 8;
+      } else {
+        int slot;
+        const int page = page_of(logical * 8, &slot);
+        src = a.v_pool + static_cast<size_t>(page) * (P * D) + d * P + slot;
+      }
+      lds_dma16(src, st + L::K_CHUNKS * 16 + (j * NW + wave) * 1024);
+    }
+  };
+  auto produce = [&](int limit) {
+    while (issued < limit && p_item >= 0) {
+      issue_tile(p_tile, issued % NSTAGE);
+      ++issued;
+      if (++p_tile == p_end) {
+        if (p_item == cur && nxt >= 0 && nxt < n_items)
+          p_set(nxt);
+        else
+          p_item = -1;
+      }
+    }
+  };
+  // Barrier that leaves the newest `pending` issued tiles' loads in flight
+  // (see prefill_kernel); every older tile is then ready.
+  auto sync_tiles = [&](int pending) {
+    if (pending >= 2) {
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * LOADS_PER_TILE) : "memory");
+      ready = issued - 2;
+    } else if (pending == 1) {
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LOADS_PER_TILE) : "memory");
+      ready = issued - 1;
+    } else {
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      ready = issued;
+    }
+  };
+  // Tile g of the sequence must be ready before it is read: when the
+  // producer fell behind (short items), issue it now and wait for it.
+  auto ensure_landed = [&](int g) {
+    if (ready <= g) {
+      produce(g + 1);
+      sync_tiles(0);
+    }
+  };
+
+  produce(3);
+  sync_tiles(issued - 1);
+  int consumed = 0;  // tiles of the sequence whose PV product is done
+
+  const int key_a0 = st_row_key(col);
+  const int vrow_swz = L::v_swz(col);
+
+  while (true) {
+    const PrefillItem it = sload(a.items + cur);
+    const SeqDesc sd = sload(a.seqs + it.seq);
+    const SegDesc sg = sload(a.segs + it.seq * a.num_kv_heads + it.kv_head);
+    const int t0 = it.qtile * rows;
+    const int t_last = min(t0 + rows, sd.q_len) - 1;
+    const int base = sd.kv_len - sd.q_len;
+    const int W = sg.window;
+    const int p_wmin = base + min(t0 + (wave * 64) / G, t_last);
+    const int p_wmax = base + min(t0 + (wave * 64 + 63) / G, t_last);
+    // The two rows of this lane: column blocks c = 0, 1.
+    int hh[2], tt[2], pp[2], lo[2];
+    bool valid[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int r = wave * 64 + 32 * c + col;
+      const int po = r / G;
+      hh[c] = it.kv_head * G + (r - po * G);
+      tt[c] = t0 + po;
+      valid[c] = po < rows && tt[c] < sd.q_len;
+      pp[c] = base + min(tt[c], t_last);
+      lo[c] = W > 0 ? pp[c] - W + 1 : 0;
+    }
+
+    bf16x8 qv[2][NKK];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const uint16_t *qrow =
+          a.q + (static_cast<size_t>(sd.q_start + min(tt[c], t_last)) * a.num_q_heads + hh[c]) * D;
+      if (sg.rope_off < 0) {
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          const u32x4 x = ld16(qrow + kk * 16 + half * 8);
+          qv[c][kk] = as_bf16x8(valid[c] ? x : z);
+        }
+      } else {
+        relocate_row<D, NKK>(qv[c], qrow, 16, half * 8, valid[c], a.rope.tables + sg.rope_off, s_rope[wave], a.rope);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+v"(qv[c][kk]));
+
+    f32x16 oacc[2][NDB];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[c][db] = f32x16{};
+    float m[2] = {kNegInf, kNegInf};
+    float l[2] = {0.f, 0.f};
+    float msc[2] = {0.f, 0.f};
+
+    auto stage_of = [&](int g) { return smem + (g % NSTAGE) * L::STAGE_BYTES; };
+    auto k_frag = [&](const char *st, int kk, int kb) {
+      const int c = (2 * kk + half) ^ L::k_swz(key_a0);
+      return as_bf16x8(*reinterpret_cast<const u32x4 *>(st + ((key_a0 + 32 * kb) * L::KCPR + c) * 16));
+    };
+    auto v_frag = [&](const char *st, int ks, int db) {  // ks: 16-key step (kb = ks / 2, s = ks % 2)
+      const int c = ((ks >> 1) * 4 + (ks & 1) * 2 + half) ^ vrow_swz;
+      return as_bf16x8(*reinterpret_cast<const u32x4 *>(st + ((L::K_CHUNKS + (db * 32 + col) * 8) + c) * 16));
+    };
+    auto tile_empty = [&](int k0) { return k0 > p_wmax || (W > 0 && k0 + kTileKeys - 1 < p_wmin - W + 1); };
+    auto tile_full = [&](int k0) { return k0 + kTileKeys - 1 <= p_wmin && (W == 0 || k0 >= p_wmax - W + 1); };
+
+    // Scores of two tiles alternate between sA and sB (the tile loop is
+    // unrolled by two so that neither is copied).
+    f32x16 sA[2][2], sB[2][2];
+
+    // S^T of tile g (K from its stage) into s, all four products per k-step,
+    // K operands one k-step ahead.  `work(kk)` runs after the products of
+    // k-step kk are issued (the softmax of the previous tile, in slices).
+    auto qk = [&](f32x16 (&s)[2][2], const char *st, auto &&work) {
+      bf16x8 k0 = k_frag(st, 0, 0), k1 = k_frag(st, 0, 1);
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 n0 = k0, n1 = k1;
+        if (kk + 1 < NKK) {
+          n0 = k_frag(st, kk + 1, 0);
+          n1 = k_frag(st, kk + 1, 1);
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          s[c][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qv[c][kk], kk ? s[c][0] : f32x16{}, 0, 0, 0);
+          s[c][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qv[c][kk], kk ? s[c][1] : f32x16{}, 0, 0, 0);
+        }
+        work(kk);
+        k0 = n0;
+        k1 = n1;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Mask (edge tiles), row max and the lazy rescale of tile k0's scores.
+    auto softmax_head = [&](f32x16 (&s)[2][2], int k0, bool mask) {
+      if (mask) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const unsigned lo_rel = static_cast<unsigned>(lo[c] - k0 - 8 * half);
+          const unsigned span = static_cast<unsigned>(pp[c] - lo[c]);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int off = ((v >> 3) << 4) + (v & 7);
+            if (static_cast<unsigned>(off) - lo_rel > span) s[c][0][v] = kNegInf;
+            if (static_cast<unsigned>(off + 32) - lo_rel > span) s[c][1][v] = kNegInf;
+          }
+        }
+      }
+      bool bump[2];
+      float m_new[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        float mx = max32(s[c][0], s[c][1]);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        bump[c] = mx * a.scale_log2 > m[c] * a.scale_log2 + kRescaleLog2;
+        m_new[c] = bump[c] ? mx : m[c];
+      }
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(bump[0] || bump[1]) != 0, 0)) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const float ms = m_new[c] == kNegInf ? 0.f : m_new[c] * a.scale_log2;
+          const float alpha = bump[c] ? fast_exp2(m[c] * a.scale_log2 - ms) : 1.f;
+          l[c] *= alpha;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) oacc[c][db] *= alpha;
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        m[c] = m_new[c];
+        msc[c] = m[c] == kNegInf ? 0.f : m[c] * a.scale_log2;
+      }
+    };
+    // Probabilities of slice j (j = 4 c + 2 kb + s: 8 keys of one row block)
+    // in place, packed to bf16 for the PV product.
+    bf16x8 pk[2][2][2];
+    auto softmax_slice = [&](f32x16 (&s)[2][2], int j) {
+      const int c = j >> 2, kb = (j >> 1) & 1, sh = j & 1;
+      float e[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) e[u] = fast_exp2(fmaf(s[c][kb][8 * sh + u], a.scale_log2, -msc[c]));
+      l[c] += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+      pk[c][kb][sh] = pack8_bf16(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+    };
+    // O^T += V^T P^T for the tile in stage st, V operands one step ahead.
+    auto pv = [&](const char *st) {
+      bf16x8 vn = v_frag(st, 0, 0);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const bf16x8 va = vn;
+          const int nks = db + 1 < NDB ? ks : ks + 1, ndb = db + 1 < NDB ? db + 1 : 0;
+          if (nks < 4) vn = v_frag(st, nks, ndb);
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+            oacc[c][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk[c][ks >> 1][ks & 1], oacc[c][db], 0, 0, 0);
+        }
+      }
+    };
+
+    const int n_tiles = it.tile_end - it.tile_begin;
+    const int fetch_i = max(0, n_tiles - 4);  // iteration whose end publishes the next item's index
+    const int g0 = consumed;                   // this item's first tile in the sequence
+    auto no_work = [](int) {};
+
+    // One iteration: softmax + PV of tile i (scores in s_cur), with the QK of
+    // tile i + 1 (into s_nxt) under the softmax.
+    auto iteration = [&](int i, f32x16 (&s_cur)[2][2], f32x16 (&s_nxt)[2][2]) {
+      const int k0 = (it.tile_begin + i) * kTileKeys;
+      if (i == fetch_i && tid == 0) s_next[fslot] = atomicAdd(a.counter, 1);
+      produce(g0 + i + 4);
+      const bool has_next = i + 1 < n_tiles;
+      const bool next_live = has_next && !tile_empty(k0 + kTileKeys);
+      const bool live = !tile_empty(k0);
+      if (live) softmax_head(s_cur, k0, !tile_full(k0));
+      if (next_live) {
+        ensure_landed(g0 + i + 1);
+        const char *stk = stage_of(g0 + i + 1);
+        if (live)
+          qk(s_nxt, stk, [&](int kk) {
+#pragma unroll
+            for (int j = kk * 8 / NKK; j < (kk + 1) * 8 / NKK; ++j) softmax_slice(s_cur, j);
+          });
+        else
+          qk(s_nxt, stk, no_work);
+      } else if (live) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) softmax_slice(s_cur, j);
+      }
+      if (live) pv(stage_of(g0 + i));
+      sync_tiles(issued - (g0 + i) - 3);
+      if (i == fetch_i) {
+        nxt = __builtin_amdgcn_readfirstlane(s_next[fslot]);
+        fslot ^= 1;
+        if (p_item < 0 && nxt < n_items) p_set(nxt);
+      }
+    };
+
+    // Prologue: QK of the first tile.
+    ensure_landed(g0);
+    if (!tile_empty(it.tile_begin * kTileKeys)) qk(sA, stage_of(g0), no_work);
+    for (int i = 0; i < n_tiles; i += 2) {
+      iteration(i, sA, sB);
+      if (i + 1 < n_tiles) iteration(i + 1, sB, sA);
+    }
+    consumed = g0 + n_tiles;
+
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const float l_tot = l[c] + __shfl_xor(l[c], 32);
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      const float lse_val = l_tot > 0.f ? m[c] * a.scale + logf(l_tot) : kNegInf;
+      const int r = wave * 64 + 32 * c + col;
+      if (it.part < 0) {
+        u32x4 w[NDB][2];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+          for (int ip = 0; ip < 2; ++ip) {
+            const f32x16 &ac = oacc[c][db];
+            const u32x2 p0 =
+                pack4_bf16(ac[8 * ip] * inv, ac[8 * ip + 1] * inv, ac[8 * ip + 2] * inv, ac[8 * ip + 3] * inv);
+            const u32x2 p1 =
+                pack4_bf16(ac[8 * ip + 4] * inv, ac[8 * ip + 5] * inv, ac[8 * ip + 6] * inv, ac[8 * ip + 7] * inv);
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+              const auto sw = __builtin_amdgcn_permlane32_swap(p0[k], p1[k], false, false);
+              w[db][ip][k] = sw[0];
+              w[db][ip][2 + k] = sw[1];
+            }
+          }
+        }
+        if (valid[c]) {
+          uint16_t *orow = a.o + (static_cast<size_t>(sd.q_start + tt[c]) * a.num_q_heads + hh[c]) * D;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int ip = 0; ip < 2; ++ip)
+              *reinterpret_cast<u32x4 *>(orow + db * 32 + ip * 16 + half * 8) = w[db][ip];
+          if (half == 0 && a.lse) a.lse[static_cast<size_t>(sd.q_start + tt[c]) * a.num_q_heads + hh[c]] = lse_val;
+        }
+      } else {
+        float *prow = a.part_o + (static_cast<size_t>(it.part) * kPrefillRows + r) * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int d0 = db * 32 + i * 8 + half * 4;
+            f32x4 x = {oacc[c][db][4 * i] * inv, oacc[c][db][4 * i + 1] * inv, oacc[c][db][4 * i + 2] * inv,
+                       oacc[c][db][4 * i + 3] * inv};
+            *reinterpret_cast<f32x4 *>(prow + d0) = x;
+          }
+        }
+        if (half == 0) a.part_lse[static_cast<size_t>(it.part) * kPrefillRows + r] = lse_val;
+      }
+    }
+
+    if (nxt >= n_items) break;
+    cur = nxt;
+    nxt = -1;
+  }
+}
+
+// ===========================================================================
 // Attention-mass token scores ("attention as a router" for the sparse FFN:
 // "Xiaohongshu Open-Sources RedKnot" page, "What Happened" item 2; "RedKnot:
 // Head-Aware KV Reuse and SegPagedAttention" page, "The Three Core
@@ -1532,6 +1949,12 @@ hipError_t launch_scatter(const ScatterArgs &a, int n_items, int head_dim, int p
 hipError_t launch_prefill(const PrefillArgs &a, int n_items, int head_dim, int page_size, hipStream_t s) {
   if (n_items <= 0) return hipSuccess;
   SEGKV_DISPATCH_DP(prefill_kernel, head_dim, page_size, dim3(n_items), dim3(kPrefillThreads), s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_wide(const PrefillArgs &a, int n_items, int head_dim, int page_size, hipStream_t s) {
+  if (n_items <= 0) return hipSuccess;
+  SEGKV_DISPATCH_DP(prefill_wide_kernel, head_dim, page_size, dim3(n_items), dim3(kPrefillWideThreads), s, a);
   return hipGetLastError();
 }
 

@@ -94,19 +94,23 @@ struct segkv_ctx {
   std::vector<Segment> segs;       // [L][S][Hkv]
   std::vector<SeqLayer> seq_layer; // [L][S]
 
-  // device metadata and staging
-  char *d_meta = nullptr;
-  size_t d_meta_cap = 0;
+  // Device workspace: each call puts its tables at the start and its split
+  // partials after them (at a 256-byte boundary).  Caller-owned unless the
+  // config left it NULL.
+  char *ws = nullptr;
+  size_t ws_bytes = 0;
+  bool ws_owned = false;
+  int32_t max_q = 0;  // query tokens the staging was sized for
+  // host staging
   char *h_stage[kStages] = {};
   char *h_stage_dev[kStages] = {};  // the same pinned memory as seen by kernels
   size_t h_stage_cap[kStages] = {};
   hipEvent_t stage_ev[kStages / kStageGroup] = {};  // recorded when the ring leaves the group
   bool stage_used[kStages / kStageGroup] = {};
   int stage_next = 0;
-  float *d_part = nullptr;
-  size_t d_part_cap = 0;  // bytes
   // Prefill tables put on the device by an append's scatter launch: valid
-  // while nothing else has written d_meta since (pre_buf = their bytes).
+  // while nothing else has written the workspace's tables since (pre_buf =
+  // their bytes).
   std::vector<char> pre_buf, plan_buf;
   bool pre_valid = false;
   size_t pre_room = kPrestageRoom;  // staging room an append keeps for them
@@ -190,6 +194,27 @@ int32_t local_segment_start(int32_t kv_len, int32_t n_query, int32_t window, int
 
 // ---- staging / upload --------------------------------------------------
 
+// Pinned staging buffer `slot` holds at least `bytes` (the caller has made
+// sure no enqueued work still reads it).  Slots are sized at create for the
+// largest tables of the context's batch range; only a larger call (a huge
+// cache-fill append, a token-score call past that range) grows one.
+int ensure_stage(segkv_ctx *c, int slot, size_t bytes) {
+  if (c->h_stage_cap[slot] >= bytes) return SEGKV_OK;
+  if (c->h_stage[slot]) {
+    hipError_t e = hipHostFree(c->h_stage[slot]);
+    if (e != hipSuccess) return c->device_fail(e, "hipHostFree");
+    c->h_stage[slot] = nullptr;
+    c->h_stage_cap[slot] = 0;
+  }
+  size_t cap = std::max<size_t>(align_up(bytes, 1 << 16), 1 << 16);
+  hipError_t e = hipHostMalloc(reinterpret_cast<void **>(&c->h_stage[slot]), cap, hipHostMallocDefault);
+  if (e != hipSuccess) return c->device_fail(e, "hipHostMalloc(stage)");
+  e = hipHostGetDevicePointer(reinterpret_cast<void **>(&c->h_stage_dev[slot]), c->h_stage[slot], 0);
+  if (e != hipSuccess) return c->device_fail(e, "hipHostGetDevicePointer(stage)");
+  c->h_stage_cap[slot] = cap;
+  return SEGKV_OK;
+}
+
 // Every call that stages tables takes the next pinned buffer of a ring of
 // kStages; its kernels read the buffer in place or through the upload
 // kernel.  One completion event covers a group of kStageGroup buffers, so
@@ -213,41 +238,24 @@ int acquire_stage(segkv_ctx *c, size_t bytes, char **out, int *slot_out) {
       if (e != hipSuccess) return c->device_fail(e, "hipEventSynchronize(stage)");
     }
   }
-  if (c->h_stage_cap[slot] < bytes) {
-    if (c->h_stage[slot]) {
-      hipError_t e = hipHostFree(c->h_stage[slot]);
-      if (e != hipSuccess) return c->device_fail(e, "hipHostFree");
-      c->h_stage[slot] = nullptr;
-      c->h_stage_cap[slot] = 0;
-    }
-    size_t cap = std::max<size_t>(align_up(bytes, 1 << 16), 1 << 16);
-    hipError_t e = hipHostMalloc(reinterpret_cast<void **>(&c->h_stage[slot]), cap, hipHostMallocDefault);
-    if (e != hipSuccess) return c->device_fail(e, "hipHostMalloc(stage)");
-    e = hipHostGetDevicePointer(reinterpret_cast<void **>(&c->h_stage_dev[slot]), c->h_stage[slot], 0);
-    if (e != hipSuccess) return c->device_fail(e, "hipHostGetDevicePointer(stage)");
-    c->h_stage_cap[slot] = cap;
-  }
+  const int rc = ensure_stage(c, slot, bytes);
+  if (rc) return rc;
   *out = c->h_stage[slot];
   *slot_out = slot;
   return SEGKV_OK;
 }
 
-int ensure_device_buffer(segkv_ctx *c, char **buf, size_t *cap, size_t bytes, const char *what) {
-  if (*cap >= bytes) return SEGKV_OK;
-  if (buf == &c->d_meta) c->pre_valid = false;
-  hipError_t e;
-  if (*buf) {
-    e = hipStreamSynchronize(c->stream);  // the old buffer may still be read
-    if (e != hipSuccess) return c->device_fail(e, "hipStreamSynchronize");
-    e = hipFree(*buf);
-    if (e != hipSuccess) return c->device_fail(e, "hipFree");
-    *buf = nullptr;
-    *cap = 0;
-  }
-  size_t ncap = std::max<size_t>(align_up(bytes + bytes / 2, 1 << 16), 1 << 16);
-  e = hipMalloc(reinterpret_cast<void **>(buf), ncap);
-  if (e != hipSuccess) return c->device_fail(e, what);
-  *cap = ncap;
+// Where a call's tables and partials go: tables at base, partials at the
+// next 256-byte boundary.  Fails (before anything is enqueued) when they do
+// not fit in cap bytes.
+int carve(segkv_ctx *c, char *base, size_t cap, size_t table_bytes, size_t part_bytes, float **parts) {
+  const size_t off = align_up(table_bytes, 256);
+  if (off + part_bytes > cap)
+    return c->fail(SEGKV_E_NOMEM,
+                   "workspace too small: this call needs %zu bytes of tables and %zu of partials, the workspace "
+                   "holds %zu (size it with segkv_workspace_bytes)",
+                   table_bytes, part_bytes, cap);
+  *parts = part_bytes ? reinterpret_cast<float *>(base + off) : nullptr;
   return SEGKV_OK;
 }
 
@@ -257,12 +265,12 @@ int timed_end(segkv_ctx *c, TimedLaunch *t);
 // Tables go to device memory through a small copy kernel on the context's
 // stream (it reads the pinned staging buffer directly): a DMA-engine copy
 // between kernels costs a queue hand-off that is several times the copy.
-int upload(segkv_ctx *c, int slot, size_t bytes) {
-  c->pre_valid = false;
+int upload(segkv_ctx *c, int slot, size_t bytes, char *dst) {
+  if (dst == c->ws) c->pre_valid = false;
   TimedLaunch t{};
   int rc = timed_begin(c, &t, SEGKV_KERNEL_UPLOAD);
   if (rc) return rc;
-  hipError_t e = launch_upload(c->d_meta, c->h_stage_dev[slot], bytes, c->stream);
+  hipError_t e = launch_upload(dst, c->h_stage_dev[slot], bytes, c->stream);
   if (e != hipSuccess) return c->device_fail(e, "upload launch");
   return timed_end(c, &t);
 }
@@ -533,15 +541,95 @@ void build_prefill_plan(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32
     std::memcpy(out->data() + pp->tbytes + pp->ibytes, citems.data(), sizeof(CombineItem) * citems.size());
 }
 
-RopeArgs rope_args(const segkv_ctx *c, const SeqTables &t) {
+RopeArgs rope_args(const segkv_ctx *c, const SeqTables &t, const char *tables) {
   RopeArgs r;
-  r.tables = reinterpret_cast<const float *>(c->d_meta + t.rope_off);
+  r.tables = reinterpret_cast<const float *>(tables + t.rope_off);
   r.lo = c->D - c->rope_dims;
   r.half = c->rope_dims / 2;
   r.style = c->rope_style;
   r.pad = 0;
   return r;
 }
+
+// Upper bounds of one call's tables and partials (bytes), for batches of at
+// most max_seqs sequences and Q query tokens, with at most num_pages page ids
+// listed and the automatic prefill split.  The counts follow the planners:
+//   prefill  items per (sequence, KV head) = ceil(q_b / rows), so at most
+//            Hkv (ceil(Q / rows) + S) unsplit items; an item is split only
+//            when it exceeds total / slots tiles, so at most slots items are
+//            split, into at most 2 slots parts;
+//   decode   one piece per segment plus one per share boundary (slots shares);
+//   scores   one partial row per visible (query tile, key tile) pair of an
+//            item: tile counts grow with the query tile's index for a global
+//            head and stop at the window for a local one.  The elementwise
+//            largest tile counts are those of one sequence of all the
+//            batch's query tiles.
+struct WsBound {
+  size_t tables = 0;  // largest tables of a prefill, decode or top-k call (staging room)
+  size_t total = 0;   // largest tables + partials of any call
+};
+
+WsBound workspace_bound(const segkv_config *cfg, int64_t Q, int64_t slots) {
+  const int64_t S = cfg->max_seqs, Hkv = cfg->num_kv_heads, D = cfg->head_dim;
+  const int64_t G = cfg->num_q_heads / cfg->num_kv_heads;
+  const int64_t rows = std::max<int64_t>(1, kPrefillRows / G);
+  const int64_t nseg = S * Hkv;
+  const size_t seq_tables = align_up(sizeof(SeqDesc) * S, 16) + align_up(sizeof(SegDesc) * nseg, 16) +
+                            align_up(sizeof(int32_t) * static_cast<size_t>(cfg->num_pages), 16) +
+                            sizeof(float) * 2 * D * nseg;
+  auto with_parts = [](size_t t, size_t p) { return align_up(align_up(t, 16), 256) + p; };
+  WsBound b;
+  // prefill
+  const int64_t nq_tiles = ceil_div(Q, rows) + S;
+  const int64_t base_items = Hkv * nq_tiles;
+  const int64_t p_parts = 2 * slots;
+  const size_t p_tables = align_up(seq_tables, 16) + align_up(sizeof(PrefillItem) * (base_items + p_parts), 16) +
+                          align_up(sizeof(CombineItem) * std::min(base_items, slots), 16) + 16;
+  const size_t p_part = static_cast<size_t>(p_parts) * kPrefillRows * (D + 1) * sizeof(float);
+  // decode
+  const int64_t pieces = nseg + slots;
+  const size_t d_tables = align_up(seq_tables, 16) + align_up(sizeof(DecodeItem) * pieces, 16) +
+                          align_up(sizeof(int32_t) * (slots + 1), 16) + sizeof(CombineItem) * nseg;
+  const size_t d_part = static_cast<size_t>(pieces) * kDecodeCols * (D + 1) * sizeof(float);
+  // top-k (the tables of max_seqs sequences)
+  const size_t k_tables = align_up(sizeof(int32_t) * (S + 1), 16) + 2 * align_up(sizeof(int32_t) * S, 16);
+  // token scores: worst layer
+  int64_t part_rows = 0;
+  for (int32_t layer = 0; layer < cfg->num_layers; ++layer) {
+    int64_t r = 0;
+    for (int64_t g = 0; g < Hkv; ++g) {
+      const int64_t w = cfg->head_window[layer * Hkv + g];
+      for (int64_t qt = 0; qt < nq_tiles; ++qt) {
+        int64_t t = ((qt + 1) * rows - 1) / kTileKeys + 2;
+        if (w > 0) t = std::min<int64_t>(t, (rows + w - 2) / kTileKeys + 2);
+        r += t;
+      }
+    }
+    part_rows = std::max(part_rows, r);
+  }
+  const int64_t srows = ceil_div(Q, kTileKeys) + 2 * S;
+  // items are cut into pieces of at least kMinSplitTiles tiles
+  const int64_t cut_items = base_items + ceil_div(part_rows, kMinSplitTiles);
+  const size_t s_tables = align_up(seq_tables, 16) + align_up(sizeof(PrefillItem) * cut_items, 16) +
+                          align_up(sizeof(ScoreRow) * srows, 16) + sizeof(int32_t) * part_rows;
+  const size_t s_part = static_cast<size_t>(std::max<int64_t>(part_rows, 1)) * kTileKeys * sizeof(float);
+  b.tables = std::max({p_tables, d_tables, k_tables});
+  b.total = std::max({with_parts(p_tables, p_part), with_parts(d_tables, d_part), with_parts(s_tables, s_part),
+                      align_up(k_tables, 256)});
+  return b;
+}
+
+// Resident workgroup slots of the current device (one prefill or decode
+// workgroup per CU); the bound assumes 256 when no device answers.
+int64_t device_slots() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                             hipSuccess || cus <= 0)
+    return 256;
+  return std::max<int64_t>(cus, 1) * std::max(kPrefillWgPerCu, kDecodeWgPerCu);
+}
+
+constexpr int32_t kDefaultMaxBatchQ = 16384;
 
 }  // namespace
 
@@ -586,6 +674,10 @@ int segkv_create(const segkv_config *cfg, segkv_ctx **out) {
   size_t nwin = static_cast<size_t>(cfg->num_layers) * cfg->num_kv_heads;
   for (size_t i = 0; i < nwin; ++i)
     if (cfg->head_window[i] < 0) return bad(SEGKV_E_INVAL, "head_window entries must be >= 0");
+  if (cfg->max_batch_q_tokens < 0) return bad(SEGKV_E_INVAL, "max_batch_q_tokens must be >= 0");
+  if (cfg->workspace && reinterpret_cast<uintptr_t>(cfg->workspace) % 256)
+    return bad(SEGKV_E_INVAL, "workspace must be 256-byte aligned");
+  if (cfg->workspace && cfg->workspace_bytes == 0) return bad(SEGKV_E_INVAL, "workspace given with 0 bytes");
 
   segkv_ctx *c = new (std::nothrow) segkv_ctx();
   if (!c) return bad(SEGKV_E_NOMEM, "out of host memory");
@@ -606,6 +698,7 @@ int segkv_create(const segkv_config *cfg, segkv_ctx **out) {
   c->v_pool = static_cast<uint16_t *>(cfg->v_pool);
   c->stream = static_cast<hipStream_t>(cfg->stream);
   c->planning = cfg->k_pool == nullptr;
+  c->max_q = cfg->max_batch_q_tokens ? cfg->max_batch_q_tokens : kDefaultMaxBatchQ;
   try {
     c->segs.resize(static_cast<size_t>(c->L) * c->S * c->Hkv);
     c->seq_layer.resize(static_cast<size_t>(c->L) * c->S);
@@ -641,6 +734,33 @@ int segkv_create(const segkv_config *cfg, segkv_ctx **out) {
         return SEGKV_E_DEVICE;
       }
     }
+    // Workspace: the caller's, else allocated here once.  Staging buffers are
+    // sized here for the largest prefill, decode or top-k tables of
+    // max_batch_q_tokens, so calls in that range allocate nothing.
+    const WsBound wb = workspace_bound(cfg, c->max_q, static_cast<int64_t>(c->num_cus) * kPrefillWgPerCu);
+    if (cfg->workspace) {
+      c->ws = static_cast<char *>(cfg->workspace);
+      c->ws_bytes = cfg->workspace_bytes;
+    } else {
+      c->ws_bytes = cfg->workspace_bytes ? cfg->workspace_bytes : wb.total;
+      hipError_t e = hipMalloc(reinterpret_cast<void **>(&c->ws), c->ws_bytes);
+      if (e != hipSuccess) {
+        g_create_error = std::string("hipMalloc(workspace): ") + hipGetErrorString(e);
+        c->ws = nullptr;
+        segkv_destroy(c);
+        return SEGKV_E_NOMEM;
+      }
+      c->ws_owned = true;
+    }
+    c->pre_room = std::max(c->pre_room, std::min(wb.tables, c->ws_bytes));
+    for (int i = 0; i < kStages; ++i) {
+      const int rc = ensure_stage(c, i, align_up(wb.tables, 16) + c->pre_room);
+      if (rc) {
+        g_create_error = c->err;
+        segkv_destroy(c);
+        return rc;
+      }
+    }
   }
   *out = c;
   return SEGKV_OK;
@@ -659,13 +779,20 @@ void segkv_destroy(segkv_ctx *c) {
       if (c->stage_ev[i]) (void)hipEventDestroy(c->stage_ev[i]);
     for (int i = 0; i < kStages; ++i)
       if (c->h_stage[i]) (void)hipHostFree(c->h_stage[i]);
-    if (c->d_meta) (void)hipFree(c->d_meta);
-    if (c->d_part) (void)hipFree(c->d_part);
+    if (c->ws_owned && c->ws) (void)hipFree(c->ws);
   }
   delete c;
 }
 
 const char *segkv_last_error(const segkv_ctx *c) { return c ? c->err.c_str() : g_create_error.c_str(); }
+
+size_t segkv_workspace_bytes(const segkv_config *cfg, int32_t max_batch_q_tokens) {
+  if (!cfg || max_batch_q_tokens < 0 || cfg->num_layers <= 0 || cfg->num_q_heads <= 0 || cfg->num_kv_heads <= 0 ||
+      cfg->num_q_heads % cfg->num_kv_heads || (cfg->head_dim != 64 && cfg->head_dim != 128) || cfg->max_seqs <= 0 ||
+      cfg->num_pages <= 0 || cfg->num_pages > std::numeric_limits<int32_t>::max() || !cfg->head_window)
+    return 0;
+  return workspace_bound(cfg, max_batch_q_tokens, device_slots()).total;
+}
 
 int64_t segkv_free_pages(const segkv_ctx *c) {
   if (!c) return SEGKV_E_INVAL;
@@ -847,10 +974,6 @@ int segkv_append_pages(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_
   if (!c->planning && n_items > 0) {
     rc = acquire_stage(c, bytes + (prestage ? c->pre_room : 0), &stage, &slot);
     if (rc) return rc;
-    if (prestage) {
-      rc = ensure_device_buffer(c, &c->d_meta, &c->d_meta_cap, c->pre_room, "hipMalloc(tables)");
-      if (rc) return rc;
-    }
   }
 
   // Commit in two phases.  First every trim of the batch returns its pages,
@@ -935,16 +1058,16 @@ int segkv_append_pages(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_
     for (int32_t b = 0; b < n_seqs; ++b) cu_q[b + 1] = cu_q[b] + n_query[b];
     PrefillPlan pp;
     build_prefill_plan(c, layer, n_seqs, seq_ids, cu_q.data(), &pp, &c->plan_buf);
-    if (bytes + pp.bytes <= c->h_stage_cap[slot] && pp.bytes <= c->d_meta_cap) {
+    if (bytes + pp.bytes <= c->h_stage_cap[slot] && pp.bytes <= c->ws_bytes) {
       std::memcpy(stage + bytes, c->plan_buf.data(), pp.bytes);
       c->pre_buf.swap(c->plan_buf);
       a.copy_src = reinterpret_cast<const uint4 *>(c->h_stage_dev[slot] + bytes);
-      a.copy_dst = reinterpret_cast<uint4 *>(c->d_meta);
+      a.copy_dst = reinterpret_cast<uint4 *>(c->ws);
       a.copy_n16 = static_cast<int32_t>(pp.bytes / 16);
       a.copy_wgs = static_cast<int32_t>(std::min<size_t>(kScatterCopyWgs, ceil_div(pp.bytes / 16, kScatterThreads)));
       staged = true;
     }
-    c->pre_room = std::max(c->pre_room, pp.bytes);  // the next append keeps room enough
+    c->pre_room = std::max(c->pre_room, std::min(pp.bytes, c->ws_bytes));  // the next append keeps room enough
   }
   c->pre_valid = false;
   TimedLaunch t{};
@@ -982,29 +1105,25 @@ int segkv_prefill(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *se
   PrefillPlan pp;
   std::vector<char> &tables = c->plan_buf;
   build_prefill_plan(c, layer, n_seqs, seq_ids, cu_q, &pp, &tables);
+  const int32_t n_parts = pp.n_parts;
+  const size_t part_bytes = static_cast<size_t>(n_parts) * kPrefillRows * (c->D + 1) * sizeof(float);
+  float *parts = nullptr;
+  rc = carve(c, c->ws, c->ws_bytes, pp.bytes, part_bytes, &parts);
+  if (rc) return rc;
   // The append that declared these queries may have put the same tables on
   // the device already (its scatter launch copies them).
   const bool staged = c->pre_valid && c->pre_buf.size() == pp.bytes &&
                       std::memcmp(c->pre_buf.data(), tables.data(), pp.bytes) == 0;
-  c->pre_valid = false;  // this launch consumes the counters
   if (!staged) {
     char *stage = nullptr;
     int slot = 0;
     rc = acquire_stage(c, pp.bytes, &stage, &slot);
     if (rc) return rc;
-    rc = ensure_device_buffer(c, &c->d_meta, &c->d_meta_cap, pp.bytes, "hipMalloc(tables)");
-    if (rc) return rc;
     std::memcpy(stage, tables.data(), pp.bytes);
-    rc = upload(c, slot, pp.bytes);
+    rc = upload(c, slot, pp.bytes, c->ws);
     if (rc) return rc;
   }
-  const int32_t n_parts = pp.n_parts;
-  const size_t part_bytes = static_cast<size_t>(n_parts) * kPrefillRows * (c->D + 1) * sizeof(float);
-  if (n_parts > 0) {
-    rc = ensure_device_buffer(c, reinterpret_cast<char **>(&c->d_part), &c->d_part_cap, part_bytes,
-                              "hipMalloc(partials)");
-    if (rc) return rc;
-  }
+  c->pre_valid = false;  // this launch consumes the counters
   const SeqTables &tl = pp.tl;
   const size_t tbytes = pp.tbytes, ibytes = pp.ibytes, cbytes = pp.cbytes;
   const std::vector<CombineItem> &citems = c->scratch_citems;
@@ -1017,13 +1136,13 @@ int segkv_prefill(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *se
   a.lse = lse;
   a.k_pool = c->k_pool;
   a.v_pool = c->v_pool;
-  a.seqs = reinterpret_cast<const SeqDesc *>(c->d_meta);
-  a.segs = reinterpret_cast<const SegDesc *>(c->d_meta + tl.seg_off);
-  a.page_ids = reinterpret_cast<const int32_t *>(c->d_meta + tl.pid_off);
-  a.rope = rope_args(c, tl);
-  a.items = reinterpret_cast<const PrefillItem *>(c->d_meta + tbytes);
-  a.part_o = c->d_part;
-  a.part_lse = c->d_part ? c->d_part + static_cast<size_t>(n_parts) * kPrefillRows * c->D : nullptr;
+  a.seqs = reinterpret_cast<const SeqDesc *>(c->ws);
+  a.segs = reinterpret_cast<const SegDesc *>(c->ws + tl.seg_off);
+  a.page_ids = reinterpret_cast<const int32_t *>(c->ws + tl.pid_off);
+  a.rope = rope_args(c, tl, c->ws);
+  a.items = reinterpret_cast<const PrefillItem *>(c->ws + tbytes);
+  a.part_o = parts;
+  a.part_lse = parts ? parts + static_cast<size_t>(n_parts) * kPrefillRows * c->D : nullptr;
   a.num_q_heads = c->Hq;
   a.num_kv_heads = c->Hkv;
   a.group = G;
@@ -1031,7 +1150,7 @@ int segkv_prefill(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *se
   a.scale = c->scale;
   a.scale_log2 = c->scale * 1.4426950408889634f;
   a.n_items = pp.n_items;
-  a.counter = reinterpret_cast<int32_t *>(c->d_meta + tbytes + ibytes + cbytes);
+  a.counter = reinterpret_cast<int32_t *>(c->ws + tbytes + ibytes + cbytes);
   const int64_t n_wgs = std::min<int64_t>(static_cast<int64_t>(pp.n_items),
                                           std::max<int64_t>(1, static_cast<int64_t>(c->num_cus) * kPrefillWgPerCu));
   TimedLaunch t{};
@@ -1045,7 +1164,7 @@ int segkv_prefill(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *se
     CombineArgs ca;
     ca.part_o = a.part_o;
     ca.part_lse = a.part_lse;
-    ca.items = reinterpret_cast<const CombineItem *>(c->d_meta + tbytes + ibytes);
+    ca.items = reinterpret_cast<const CombineItem *>(c->ws + tbytes + ibytes);
     ca.o = static_cast<uint16_t *>(o);
     ca.lse = lse;
     ca.num_q_heads = c->Hq;
@@ -1061,8 +1180,14 @@ int segkv_prefill(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *se
   return SEGKV_OK;
 }
 
-int segkv_decode(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_ids, const void *q, void *o,
-                 float *lse) {
+}  // extern "C"
+
+namespace {
+
+// One-token decode with its tables at `base` and its partials after them,
+// within cap bytes of device memory.
+int decode_impl(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_ids, const void *q, void *o,
+                float *lse, char *base, size_t cap) {
   if (!c) return SEGKV_E_INVAL;
   if (c->planning) return c->fail(SEGKV_E_STATE, "decode needs device pools (planning-only context)");
   int rc = check_layer_seqs(c, layer, n_seqs, seq_ids);
@@ -1162,35 +1287,33 @@ int segkv_decode(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq
   const size_t obytes = align_up(sizeof(int32_t) * wg_off.size(), 16);
   const size_t cbytes = sizeof(CombineItem) * citems.size();
   const size_t bytes = tbytes + ibytes + obytes + cbytes;
+  const size_t part_bytes = static_cast<size_t>(n_parts) * kDecodeCols * (c->D + 1) * sizeof(float);
+  float *parts = nullptr;
+  rc = carve(c, base, cap, bytes, part_bytes, &parts);
+  if (rc) return rc;
   char *stage = nullptr;
   int slot = 0;
   rc = acquire_stage(c, bytes, &stage, &slot);
-  if (rc) return rc;
-  rc = ensure_device_buffer(c, &c->d_meta, &c->d_meta_cap, bytes, "hipMalloc(tables)");
-  if (rc) return rc;
-  const size_t part_bytes = static_cast<size_t>(n_parts) * kDecodeCols * (c->D + 1) * sizeof(float);
-  rc = ensure_device_buffer(c, reinterpret_cast<char **>(&c->d_part), &c->d_part_cap, part_bytes,
-                            "hipMalloc(partials)");
   if (rc) return rc;
   write_seq_tables(c, layer, n_seqs, seq_ids, nullptr, nullptr, tl, stage);
   std::memcpy(stage + tbytes, ditems.data(), sizeof(DecodeItem) * ditems.size());
   std::memcpy(stage + tbytes + ibytes, wg_off.data(), sizeof(int32_t) * wg_off.size());
   if (cbytes) std::memcpy(stage + tbytes + ibytes + obytes, citems.data(), cbytes);
-  rc = upload(c, slot, bytes);
+  rc = upload(c, slot, bytes, base);
   if (rc) return rc;
 
   DecodeArgs a;
   a.q = static_cast<const uint16_t *>(q);
   a.k_pool = c->k_pool;
   a.v_pool = c->v_pool;
-  a.seqs = reinterpret_cast<const SeqDesc *>(c->d_meta);
-  a.segs = reinterpret_cast<const SegDesc *>(c->d_meta + tl.seg_off);
-  a.page_ids = reinterpret_cast<const int32_t *>(c->d_meta + tl.pid_off);
-  a.rope = rope_args(c, tl);
-  a.items = reinterpret_cast<const DecodeItem *>(c->d_meta + tbytes);
-  a.wg_piece_off = reinterpret_cast<const int32_t *>(c->d_meta + tbytes + ibytes);
-  a.part_o = c->d_part;
-  a.part_lse = c->d_part + static_cast<size_t>(n_parts) * kDecodeCols * c->D;
+  a.seqs = reinterpret_cast<const SeqDesc *>(base);
+  a.segs = reinterpret_cast<const SegDesc *>(base + tl.seg_off);
+  a.page_ids = reinterpret_cast<const int32_t *>(base + tl.pid_off);
+  a.rope = rope_args(c, tl, base);
+  a.items = reinterpret_cast<const DecodeItem *>(base + tbytes);
+  a.wg_piece_off = reinterpret_cast<const int32_t *>(base + tbytes + ibytes);
+  a.part_o = parts;
+  a.part_lse = parts ? parts + static_cast<size_t>(n_parts) * kDecodeCols * c->D : nullptr;
   a.o = static_cast<uint16_t *>(o);
   a.lse = lse;
   a.num_q_heads = c->Hq;
@@ -1208,7 +1331,7 @@ int segkv_decode(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq
   CombineArgs ca;
   ca.part_o = a.part_o;
   ca.part_lse = a.part_lse;
-  ca.items = reinterpret_cast<const CombineItem *>(c->d_meta + tbytes + ibytes + obytes);
+  ca.items = reinterpret_cast<const CombineItem *>(base + tbytes + ibytes + obytes);
   ca.o = static_cast<uint16_t *>(o);
   ca.lse = lse;
   ca.num_q_heads = c->Hq;
@@ -1219,6 +1342,16 @@ int segkv_decode(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq
   e = launch_combine(ca, static_cast<int>(citems.size()), c->G, c->D, c->stream);
   if (e != hipSuccess) return c->device_fail(e, "combine launch");
   return timed_end(c, &t2);
+}
+
+}  // namespace
+
+extern "C" {
+
+int segkv_decode(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_ids, const void *q, void *o,
+                 float *lse) {
+  if (!c) return SEGKV_E_INVAL;
+  return decode_impl(c, layer, n_seqs, seq_ids, q, o, lse, c->ws, c->ws_bytes);
 }
 
 int segkv_token_scores(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_ids, const int32_t *cu_q,
@@ -1316,15 +1449,13 @@ int segkv_token_scores(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_
   const size_t rbytes = align_up(sizeof(ScoreRow) * srows.size(), 16);
   const size_t pbytes = sizeof(int32_t) * pidx.size();
   const size_t bytes = tbytes + ibytes + rbytes + pbytes;
+  float *parts = nullptr;
+  rc = carve(c, c->ws, c->ws_bytes, bytes, static_cast<size_t>(std::max(n_part_rows, 1)) * kTileKeys * sizeof(float),
+             &parts);
+  if (rc) return rc;
   char *stage = nullptr;
   int slot = 0;
   rc = acquire_stage(c, bytes, &stage, &slot);
-  if (rc) return rc;
-  rc = ensure_device_buffer(c, &c->d_meta, &c->d_meta_cap, bytes, "hipMalloc(tables)");
-  if (rc) return rc;
-  rc = ensure_device_buffer(c, reinterpret_cast<char **>(&c->d_part), &c->d_part_cap,
-                            static_cast<size_t>(std::max(n_part_rows, 1)) * kTileKeys * sizeof(float),
-                            "hipMalloc(partials)");
   if (rc) return rc;
   std::vector<int32_t> qs(n_seqs), qlv(n_seqs);
   for (int32_t b = 0; b < n_seqs; ++b) {
@@ -1335,19 +1466,19 @@ int segkv_token_scores(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_
   std::memcpy(stage + tbytes, cut.data(), sizeof(PrefillItem) * cut.size());
   std::memcpy(stage + tbytes + ibytes, srows.data(), sizeof(ScoreRow) * srows.size());
   if (pbytes) std::memcpy(stage + tbytes + ibytes + rbytes, pidx.data(), pbytes);
-  rc = upload(c, slot, bytes);
+  rc = upload(c, slot, bytes, c->ws);
   if (rc) return rc;
 
   ScoreArgs a;
   a.q = static_cast<const uint16_t *>(q);
   a.lse = lse;
   a.k_pool = c->k_pool;
-  a.seqs = reinterpret_cast<const SeqDesc *>(c->d_meta);
-  a.segs = reinterpret_cast<const SegDesc *>(c->d_meta + tl.seg_off);
-  a.page_ids = reinterpret_cast<const int32_t *>(c->d_meta + tl.pid_off);
-  a.rope = rope_args(c, tl);
-  a.items = reinterpret_cast<const PrefillItem *>(c->d_meta + tbytes);
-  a.part = c->d_part;
+  a.seqs = reinterpret_cast<const SeqDesc *>(c->ws);
+  a.segs = reinterpret_cast<const SegDesc *>(c->ws + tl.seg_off);
+  a.page_ids = reinterpret_cast<const int32_t *>(c->ws + tl.pid_off);
+  a.rope = rope_args(c, tl, c->ws);
+  a.items = reinterpret_cast<const PrefillItem *>(c->ws + tbytes);
+  a.part = parts;
   a.num_q_heads = c->Hq;
   a.num_kv_heads = c->Hkv;
   a.group = G;
@@ -1361,9 +1492,9 @@ int segkv_token_scores(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_
   rc = timed_end(c, &t);
   if (rc) return rc;
   ScoreReduceArgs ra;
-  ra.part = c->d_part;
-  ra.part_idx = reinterpret_cast<const int32_t *>(c->d_meta + tbytes + ibytes + rbytes);
-  ra.rows = reinterpret_cast<const ScoreRow *>(c->d_meta + tbytes + ibytes);
+  ra.part = parts;
+  ra.part_idx = reinterpret_cast<const int32_t *>(c->ws + tbytes + ibytes + rbytes);
+  ra.rows = reinterpret_cast<const ScoreRow *>(c->ws + tbytes + ibytes);
   ra.seqs = a.seqs;
   ra.scores = scores;
   ra.n_rows = static_cast<int32_t>(srows.size());
@@ -1396,11 +1527,12 @@ int segkv_topk(segkv_ctx *c, int32_t n_seqs, const int32_t *cu_n, const float *s
   const size_t cu_bytes = align_up(sizeof(int32_t) * (nb + 1), 16);
   const size_t k_bytes = align_up(sizeof(int32_t) * nb, 16);
   const size_t bytes = cu_bytes + 2 * k_bytes;
+  float *unused = nullptr;
+  int rc = carve(c, c->ws, c->ws_bytes, bytes, 0, &unused);
+  if (rc) return rc;
   char *stage = nullptr;
   int slot = 0;
-  int rc = acquire_stage(c, bytes, &stage, &slot);
-  if (rc) return rc;
-  rc = ensure_device_buffer(c, &c->d_meta, &c->d_meta_cap, bytes, "hipMalloc(tables)");
+  rc = acquire_stage(c, bytes, &stage, &slot);
   if (rc) return rc;
   std::memcpy(stage, cu_n, sizeof(int32_t) * (nb + 1));
   std::memcpy(stage + cu_bytes, k, sizeof(int32_t) * nb);
@@ -1410,13 +1542,13 @@ int segkv_topk(segkv_ctx *c, int32_t n_seqs, const int32_t *cu_n, const float *s
     off[b] = acc;
     acc += k[b];
   }
-  rc = upload(c, slot, bytes);
+  rc = upload(c, slot, bytes, c->ws);
   if (rc) return rc;
   TopkArgs a;
   a.scores = scores;
-  a.cu = reinterpret_cast<const int32_t *>(c->d_meta);
-  a.k = reinterpret_cast<const int32_t *>(c->d_meta + cu_bytes);
-  a.out_off = reinterpret_cast<const int32_t *>(c->d_meta + cu_bytes + k_bytes);
+  a.cu = reinterpret_cast<const int32_t *>(c->ws);
+  a.k = reinterpret_cast<const int32_t *>(c->ws + cu_bytes);
+  a.out_off = reinterpret_cast<const int32_t *>(c->ws + cu_bytes + k_bytes);
   a.out = out_idx;
   TimedLaunch t{};
   rc = timed_begin(c, &t, SEGKV_KERNEL_TOPK);

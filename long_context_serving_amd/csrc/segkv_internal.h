@@ -19,6 +19,7 @@ namespace segkv {
 constexpr int kTileKeys = 64;      // keys per prefill KV tile (one LDS stage)
 constexpr int kPrefillRows = 256;  // (query position, query head) rows per prefill workgroup
 constexpr int kPrefillThreads = 512;  // 8 waves, 32 rows each, two per SIMD
+constexpr int kPrefillWideThreads = 256;  // wide variant: 4 waves, 64 rows each, one per SIMD
 constexpr int kDecodeThreads = 512;  // 8 waves, two per SIMD
 constexpr int kDecodeCols = 16;    // query heads handled by one decode work item (GQA group, padded)
 constexpr int kDecodeSlots = 16;   // LDS partials of one decode workgroup: (piece, wave) pairs of a batch
@@ -252,6 +253,7 @@ struct MergeArgs {
 // Launchers (kernels.hip).  Return the launch status.
 hipError_t launch_scatter(const ScatterArgs &a, int n_items, int head_dim, int page_size, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs &a, int n_items, int head_dim, int page_size, hipStream_t s);
+hipError_t launch_prefill_wide(const PrefillArgs &a, int n_items, int head_dim, int page_size, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int n_wgs, int head_dim, int page_size, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, int n_items, int max_entries, int head_dim, hipStream_t s);
 hipError_t launch_merge(const MergeArgs &a, int n_wgs, int head_dim, hipStream_t s);

@@ -64,7 +64,8 @@ class WorkloadRun:
         self.ctx = S.SegKV(1, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size, max(w.n_seqs, 1),
                            num_pages or pages_for(w), self.windows, softmax_scale=w.scale,
                            page_order_seed=w.page_order_seed if page_order_seed is None else page_order_seed,
-                           rope_theta=rope_theta, rope_style=rope_style, rope_dims=rope_dims)
+                           rope_theta=rope_theta, rope_style=rope_style, rope_dims=rope_dims,
+                           max_batch_q_tokens=max(1, sum(w.q_lens)))
         self.seq_ids = list(range(w.n_seqs))
 
     def append_fill(self):

@@ -43,7 +43,7 @@ EXPORTED = (
     "segkv_create", "segkv_destroy", "segkv_append_pages", "segkv_prefill", "segkv_decode",
     "segkv_release", "segkv_page_table", "segkv_free_pages", "segkv_set_timing",
     "segkv_read_timing", "segkv_set_tuning", "segkv_last_error", "segkv_set_relocation", "segkv_merge",
-    "segkv_fork", "segkv_token_scores", "segkv_topk",
+    "segkv_fork", "segkv_token_scores", "segkv_topk", "segkv_workspace_bytes",
 )
 
 MERGE_TAKE_A = 0
@@ -78,6 +78,10 @@ class _Config(ctypes.Structure):
         ("rope_theta", ctypes.c_float),
         ("rope_style", ctypes.c_int32),
         ("rope_dims", ctypes.c_int32),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_uint64),
+        ("max_batch_q_tokens", ctypes.c_int32),
+        ("pad0", ctypes.c_int32),
     ]
 
 
@@ -97,6 +101,8 @@ def load_library(path: Optional[str] = None):
     lib = ctypes.CDLL(p)
     i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
     pi32 = ctypes.POINTER(ctypes.c_int32)
+    lib.segkv_workspace_bytes.argtypes = [ctypes.POINTER(_Config), i32]
+    lib.segkv_workspace_bytes.restype = ctypes.c_size_t
     lib.segkv_create.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(vp)]
     lib.segkv_create.restype = ctypes.c_int
     lib.segkv_destroy.argtypes = [vp]
@@ -172,14 +178,18 @@ class SegKV:
     ``planning=True`` builds a host-only context (allocator and page tables,
     no device pools, no HIP call).  Otherwise K/V pools are allocated with
     torch on the current device unless given: K [num_pages][page][D], V
-    [num_pages][D][page] (each V page transposed).
+    [num_pages][D][page] (each V page transposed).  The device workspace is a
+    torch uint8 tensor, ``workspace`` if given, else one of
+    ``workspace_bytes`` or segkv_workspace_bytes(config, max_batch_q_tokens)
+    bytes; the library allocates no device memory of its own.
     """
 
     def __init__(self, num_layers: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                  page_size: int, max_seqs: int, num_pages: int, head_window: Sequence[int],
                  softmax_scale: float = 0.0, page_order_seed: int = 0, planning: bool = False,
                  k_pool=None, v_pool=None, stream=None, rope_theta: float = 0.0, rope_style: int = 0,
-                 rope_dims: int = 0):
+                 rope_dims: int = 0, workspace=None, workspace_bytes: Optional[int] = None,
+                 max_batch_q_tokens: int = 16384):
         self._lib = load_library()
         self.num_layers, self.num_q_heads, self.num_kv_heads = num_layers, num_q_heads, num_kv_heads
         self.head_dim, self.page_size, self.max_seqs, self.num_pages = head_dim, page_size, max_seqs, num_pages
@@ -195,6 +205,8 @@ class SegKV:
         cfg.softmax_scale = softmax_scale
         cfg.page_order_seed = page_order_seed
         cfg.rope_theta, cfg.rope_style, cfg.rope_dims = rope_theta, rope_style, rope_dims
+        cfg.max_batch_q_tokens = max_batch_q_tokens
+        self.workspace = None
         if not planning:
             import torch
             if k_pool is None:
@@ -210,6 +222,15 @@ class SegKV:
             cfg.k_pool = k_pool.data_ptr()
             cfg.v_pool = v_pool.data_ptr()
             cfg.stream = self.stream.cuda_stream
+            if workspace is None:
+                n = workspace_bytes or self._lib.segkv_workspace_bytes(ctypes.byref(cfg), max_batch_q_tokens)
+                if n == 0:
+                    raise ValueError("invalid configuration (segkv_workspace_bytes returned 0)")
+                workspace = torch.empty(int(n), dtype=torch.uint8, device=k_pool.device)
+            _check_dev(workspace, "workspace", torch.uint8)
+            self.workspace = workspace
+            cfg.workspace = workspace.data_ptr()
+            cfg.workspace_bytes = workspace.numel()
         self._cfg = cfg
         h = ctypes.c_void_p()
         rc = self._lib.segkv_create(ctypes.byref(cfg), ctypes.byref(h))
@@ -222,6 +243,18 @@ class SegKV:
         if rc != SEGKV_OK:
             raise SegKVError(rc, self.last_error())
         return rc
+
+    @staticmethod
+    def workspace_bytes_for(num_layers, num_q_heads, num_kv_heads, head_dim, page_size, max_seqs, num_pages,
+                            head_window, max_batch_q_tokens) -> int:
+        """segkv_workspace_bytes of a configuration (0 if it is invalid)."""
+        lib = load_library()
+        win, win_p = _i32(np.asarray(head_window, dtype=np.int32).reshape(-1))
+        cfg = _Config()
+        cfg.num_layers, cfg.num_q_heads, cfg.num_kv_heads = num_layers, num_q_heads, num_kv_heads
+        cfg.head_dim, cfg.page_size, cfg.max_seqs, cfg.num_pages = head_dim, page_size, max_seqs, num_pages
+        cfg.head_window = win_p
+        return int(lib.segkv_workspace_bytes(ctypes.byref(cfg), max_batch_q_tokens))
 
     def last_error(self) -> str:
         return self._lib.segkv_last_error(self._h).decode()

@@ -147,3 +147,59 @@ def test_scores_and_topk_refused_in_planning_context(lib):
     k = (ctypes.c_int32 * 1)(1)
     assert lib.segkv_token_scores(kv._h, 0, 1, ids, cu, None, None, None) == S.SEGKV_E_STATE
     assert lib.segkv_topk(kv._h, 1, cu, None, k, None) == S.SEGKV_E_STATE
+
+
+def _ws(lib, q_tokens, **kw):
+    c = _cfg(**kw)
+    return S.SegKV.workspace_bytes_for(c["num_layers"], c["num_q_heads"], c["num_kv_heads"], c["head_dim"],
+                                       c["page_size"], c["max_seqs"], c["num_pages"], c["head_window"], q_tokens)
+
+
+def test_workspace_bytes_bound(lib):
+    n0 = _ws(lib, 0)
+    n1 = _ws(lib, 4096)
+    n2 = _ws(lib, 65536)
+    assert 0 < n0 <= n1 <= n2
+    # more sequences, pages or a wider head dim never need less
+    assert _ws(lib, 4096, max_seqs=64) >= n1
+    assert _ws(lib, 4096, num_pages=100_000) >= n1 + 4 * (100_000 - 100) - 16
+    assert _ws(lib, 4096, head_dim=64) <= n1
+    # a global head's token-score partial rows grow with the square of the chunk
+    g = _ws(lib, 65536, head_window=[0, 0])
+    loc = _ws(lib, 65536, head_window=[64, 64])
+    assert g > loc
+    # the prefill's split partials alone: two per resident workgroup of >= 1 CU, 256 rows x (D + 1) fp32
+    assert n0 >= 2 * 256 * 129 * 4
+
+
+@pytest.mark.parametrize("kw", [dict(num_q_heads=6, num_kv_heads=4), dict(head_dim=96), dict(max_seqs=0),
+                                dict(num_pages=0), dict(num_layers=0)])
+def test_workspace_bytes_of_invalid_config_is_zero(lib, kw):
+    assert _ws(lib, 16, **kw) == 0
+
+
+def test_workspace_bytes_of_negative_tokens_is_zero(lib):
+    assert _ws(lib, -1) == 0
+
+
+def test_create_rejects_bad_workspace(lib):
+    import ctypes as ct
+    c = _cfg()
+    win, win_p = S._i32(c["head_window"])
+    cfg = S._Config()
+    cfg.num_layers, cfg.num_q_heads, cfg.num_kv_heads = c["num_layers"], c["num_q_heads"], c["num_kv_heads"]
+    cfg.head_dim, cfg.page_size, cfg.max_seqs, cfg.num_pages = c["head_dim"], c["page_size"], c["max_seqs"], c["num_pages"]
+    cfg.head_window = win_p
+    h = ct.c_void_p()
+    cfg.max_batch_q_tokens = -5
+    assert lib.segkv_create(ct.byref(cfg), ct.byref(h)) == S.SEGKV_E_INVAL
+    assert b"max_batch_q_tokens" in lib.segkv_last_error(None)
+    cfg.max_batch_q_tokens = 0
+    # a workspace given with a bad alignment or no size (checked before any device use)
+    cfg.workspace, cfg.workspace_bytes = 0x1001, 4096
+    cfg.k_pool = cfg.v_pool = 0x10000
+    assert lib.segkv_create(ct.byref(cfg), ct.byref(h)) == S.SEGKV_E_INVAL
+    assert b"aligned" in lib.segkv_last_error(None)
+    cfg.workspace, cfg.workspace_bytes = 0x1000, 0
+    assert lib.segkv_create(ct.byref(cfg), ct.byref(h)) == S.SEGKV_E_INVAL
+    assert b"0 bytes" in lib.segkv_last_error(None)
