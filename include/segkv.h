@@ -192,6 +192,24 @@ int segkv_decode(segkv_ctx *ctx, int32_t layer, int32_t n_seqs, const int32_t *s
                  const void *q, void *o, float *lse);
 
 /*
+ * segkv_decode for callers that cannot allocate memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same kernels and results, but the call's tables and split partials go to
+ * a fixed device scratch array of 8 MiB that the library holds on each GPU
+ * for the life of the process, instead of the context's workspace.  The
+ * call allocates nothing (no device, pinned or host buffer, no timing
+ * event: kernel timing is not recorded for it).  A batch whose tables and
+ * partials exceed 8 MiB, or whose tables exceed the host staging buffers
+ * sized at create, fails with SEGKV_E_NOMEM before anything is enqueued.
+ * Every context on a GPU shares that GPU's array and each call overwrites
+ * it: calls that overlap in time on one GPU (two streams, two contexts,
+ * two threads) race and must not be issued.  Arguments and errors are
+ * those of segkv_decode.
+ */
+int segkv_decode_noalloc(segkv_ctx *ctx, int32_t layer, int32_t n_seqs, const int32_t *seq_ids,
+                         const void *q, void *o, float *lse);
+
+/*
  * Query-side RoPE relocation ("RedKnot-MLA: Multi-Head Offline-Online Reuse
  * for DeepSeek-V4 Long-Context Serving" review, "Summary"; the paper page's
  * abstract).  A reused document's KV is encoded at canonical positions

@@ -18,6 +18,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "segkv_internal.h"
@@ -1968,6 +1969,31 @@ hipError_t launch_decode(const DecodeArgs &a, int n_wgs, int head_dim, int page_
 __global__ __launch_bounds__(256) void upload_kernel(uint4 *dst, const uint4 *src, size_t n16) {
   const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i < n16) dst[i] = src[i];
+}
+
+// Device scratch of segkv_decode_noalloc: its tables and split partials,
+// one array per GPU for the life of the process.  Host code never uses the
+// array's name as a device address; scratch_address() resolves the device
+// copy of the current GPU once and hands out that pointer.
+constexpr int kMaxScratchDevices = 64;
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t scratch_address(void **out) {
+  static std::mutex mu;
+  static void *ptr[kMaxScratchDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_upload(void *dst, const void *src_pinned, size_t bytes, hipStream_t s) {

@@ -101,6 +101,7 @@ struct segkv_ctx {
   size_t ws_bytes = 0;
   bool ws_owned = false;
   int32_t max_q = 0;  // query tokens the staging was sized for
+  char *fixed_scratch = nullptr;  // this device's copy of the fixed scratch (segkv_decode_noalloc)
   // host staging
   char *h_stage[kStages] = {};
   char *h_stage_dev[kStages] = {};  // the same pinned memory as seen by kernels
@@ -752,6 +753,16 @@ int segkv_create(const segkv_config *cfg, segkv_ctx **out) {
       }
       c->ws_owned = true;
     }
+    {
+      void *p = nullptr;
+      hipError_t e = scratch_address(&p);
+      if (e != hipSuccess) {
+        g_create_error = std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e);
+        segkv_destroy(c);
+        return SEGKV_E_DEVICE;
+      }
+      c->fixed_scratch = static_cast<char *>(p);
+    }
     c->pre_room = std::max(c->pre_room, std::min(wb.tables, c->ws_bytes));
     for (int i = 0; i < kStages; ++i) {
       const int rc = ensure_stage(c, i, align_up(wb.tables, 16) + c->pre_room);
@@ -1187,7 +1198,7 @@ namespace {
 // One-token decode with its tables at `base` and its partials after them,
 // within cap bytes of device memory.
 int decode_impl(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_ids, const void *q, void *o,
-                float *lse, char *base, size_t cap) {
+                float *lse, char *base, size_t cap, bool no_alloc) {
   if (!c) return SEGKV_E_INVAL;
   if (c->planning) return c->fail(SEGKV_E_STATE, "decode needs device pools (planning-only context)");
   int rc = check_layer_seqs(c, layer, n_seqs, seq_ids);
@@ -1291,6 +1302,9 @@ int decode_impl(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_
   float *parts = nullptr;
   rc = carve(c, base, cap, bytes, part_bytes, &parts);
   if (rc) return rc;
+  if (no_alloc && bytes > c->h_stage_cap[c->stage_next])
+    return c->fail(SEGKV_E_NOMEM, "decode tables of %zu bytes exceed the host staging buffer of %zu bytes", bytes,
+                   c->h_stage_cap[c->stage_next]);
   char *stage = nullptr;
   int slot = 0;
   rc = acquire_stage(c, bytes, &stage, &slot);
@@ -1351,7 +1365,19 @@ extern "C" {
 int segkv_decode(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_ids, const void *q, void *o,
                  float *lse) {
   if (!c) return SEGKV_E_INVAL;
-  return decode_impl(c, layer, n_seqs, seq_ids, q, o, lse, c->ws, c->ws_bytes);
+  return decode_impl(c, layer, n_seqs, seq_ids, q, o, lse, c->ws, c->ws_bytes, false);
+}
+
+int segkv_decode_noalloc(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_ids, const void *q,
+                         void *o, float *lse) {
+  if (!c) return SEGKV_E_INVAL;
+  if (c->planning) return c->fail(SEGKV_E_STATE, "decode needs device pools (planning-only context)");
+  // No timing events (creating one allocates); the mask is left as it is.
+  const int32_t mask = c->timing_mask;
+  c->timing_mask = 0;
+  const int rc = decode_impl(c, layer, n_seqs, seq_ids, q, o, lse, c->fixed_scratch, kStaticScratchBytes, true);
+  c->timing_mask = mask;
+  return rc;
 }
 
 int segkv_token_scores(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_ids, const int32_t *cu_q,

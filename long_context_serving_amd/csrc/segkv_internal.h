@@ -263,4 +263,9 @@ hipError_t launch_topk(const TopkArgs &a, int n_seqs, hipStream_t s);
 // bytes are rounded up to 16; both buffers must hold the rounded size
 hipError_t launch_upload(void *dst, const void *src_pinned, size_t bytes, hipStream_t s);
 
+// The fixed device scratch of segkv_decode_noalloc (kernels.hip): its size,
+// and its address on the current device (resolved once per device).
+constexpr size_t kStaticScratchBytes = size_t(8) << 20;
+hipError_t scratch_address(void **out);
+
 }  // namespace segkv

@@ -43,7 +43,7 @@ EXPORTED = (
     "segkv_create", "segkv_destroy", "segkv_append_pages", "segkv_prefill", "segkv_decode",
     "segkv_release", "segkv_page_table", "segkv_free_pages", "segkv_set_timing",
     "segkv_read_timing", "segkv_set_tuning", "segkv_last_error", "segkv_set_relocation", "segkv_merge",
-    "segkv_fork", "segkv_token_scores", "segkv_topk", "segkv_workspace_bytes",
+    "segkv_fork", "segkv_token_scores", "segkv_topk", "segkv_workspace_bytes", "segkv_decode_noalloc",
 )
 
 MERGE_TAKE_A = 0
@@ -113,6 +113,8 @@ def load_library(path: Optional[str] = None):
     lib.segkv_prefill.restype = ctypes.c_int
     lib.segkv_decode.argtypes = [vp, i32, i32, pi32, vp, vp, vp]
     lib.segkv_decode.restype = ctypes.c_int
+    lib.segkv_decode_noalloc.argtypes = [vp, i32, i32, pi32, vp, vp, vp]
+    lib.segkv_decode_noalloc.restype = ctypes.c_int
     lib.segkv_release.argtypes = [vp, i32]
     lib.segkv_release.restype = ctypes.c_int
     lib.segkv_page_table.argtypes = [vp, i32, i32, i32, pi32, pi32, pi32, pi32, i32]
@@ -364,9 +366,14 @@ class SegKV:
         self._check(self._lib.segkv_topk(self._h, len(kk), cu_p, scores.data_ptr(), k_p, out.data_ptr()))
         return out
 
-    def decode(self, layer: int, seq_ids, q, o=None, lse=None, want_lse: bool = True):
-        """One-token decode; q bf16 [n_seqs][Hq][D].  Returns (o, lse)."""
+    def decode(self, layer: int, seq_ids, q, o=None, lse=None, want_lse: bool = True, no_alloc: bool = False):
+        """One-token decode; q bf16 [n_seqs][Hq][D].  Returns (o, lse).
+        ``no_alloc`` calls segkv_decode_noalloc (fixed device scratch); o and
+        lse must then be given when wanted, since the binding allocates
+        nothing either."""
         import torch
+        if no_alloc and (o is None or (lse is None and want_lse)):
+            raise ValueError("no_alloc decode needs o (and lse) preallocated")
         ids, ids_p = _i32(seq_ids)
         _check_dev(q, "q", torch.bfloat16)
         if tuple(q.shape) != (len(ids), self.num_q_heads, self.head_dim):
@@ -378,8 +385,9 @@ class SegKV:
             lse = torch.empty((len(ids), self.num_q_heads), dtype=torch.float32, device=q.device)
         if lse is not None:
             _check_dev(lse, "lse", torch.float32)
-        self._check(self._lib.segkv_decode(self._h, layer, len(ids), ids_p, q.data_ptr(), o.data_ptr(),
-                                           lse.data_ptr() if lse is not None else None))
+        fn = self._lib.segkv_decode_noalloc if no_alloc else self._lib.segkv_decode
+        self._check(fn(self._h, layer, len(ids), ids_p, q.data_ptr(), o.data_ptr(),
+                       lse.data_ptr() if lse is not None else None))
         return o, lse
 
     def merge(self, o_a, lse_a, o_b, lse_b, mode, o=None, lse=None, want_lse: bool = True):
