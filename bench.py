@@ -126,6 +126,9 @@ def warm_clock(step):
             return
 
 
+PREFILL_KERNEL = 0  # SEGKV_TUNE_PREFILL_KERNEL of every prefill arm (--prefill-kernel)
+
+
 def prefill_arm(w, dev, steps, warmup, windows=None, split_tiles=None, deltas=None):
     import torch
     from long_context_serving_amd import runner as R
@@ -133,6 +136,8 @@ def prefill_arm(w, dev, steps, warmup, windows=None, split_tiles=None, deltas=No
     run = R.WorkloadRun(w, dev, windows=windows, deltas=deltas)
     if split_tiles:
         run.ctx.set_tuning(S.TUNE_PREFILL_SPLIT_TILES, split_tiles)
+    if PREFILL_KERNEL:
+        run.ctx.set_tuning(S.TUNE_PREFILL_KERNEL, PREFILL_KERNEL)
     o = torch.empty_like(dev.q)
     lse = torch.empty(dev.q.shape[:2], dtype=torch.float32, device=dev.q.device)
 
@@ -506,6 +511,8 @@ def main():
                     help="profiling runs: only the segmented headline prefill, the 128K chunk, the Mistral-7B-shaped "
                          "prefill, segmented decode, the merge or the router")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-kernel", type=int, default=0, choices=[0, 1, 2],
+                    help="prefill kernel variant (SEGKV_TUNE_PREFILL_KERNEL); 0 = the library's default")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -537,6 +544,8 @@ def main():
     from long_context_serving_amd import segkv as S
     S.load_library()
     K, Wm = args.steps, args.warmup
+    global PREFILL_KERNEL
+    PREFILL_KERNEL = args.prefill_kernel
     full = args.only == "all"
     out = {"metric": METRIC, "n_gpus": 1, "steps": K, "warmup": Wm, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16",

@@ -366,12 +366,19 @@ int segkv_read_timing(segkv_ctx *ctx, int32_t kernel, double *total_ms, int64_t 
  *                                      eight cost-balanced runs grouped by
  *                                      head, each sorted longest first, and
  *                                      the runs are interleaved.
+ *   SEGKV_TUNE_PREFILL_KERNEL          0 (default) or 1: the prefill kernel of
+ *                                      8 waves x 32 rows (two waves per SIMD);
+ *                                      2: the kernel of 4 waves x 64 rows (one
+ *                                      wave per SIMD, each K/V^T operand read
+ *                                      from LDS feeds two products, softmax
+ *                                      pipelined under the products).
  * Results do not depend on the knobs beyond fp32 rounding of split merges.
  */
 enum segkv_tune {
   SEGKV_TUNE_DECODE_MIN_PAGES = 0,
   SEGKV_TUNE_PREFILL_SPLIT_TILES = 1,
-  SEGKV_TUNE_PREFILL_ORDER = 2
+  SEGKV_TUNE_PREFILL_ORDER = 2,
+  SEGKV_TUNE_PREFILL_KERNEL = 3
 };
 int segkv_set_tuning(segkv_ctx *ctx, int32_t knob, int64_t value);
 

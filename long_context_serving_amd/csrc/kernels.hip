@@ -702,16 +702,50 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
 // ===========================================================================
 // Prefill, wide variant: 4 waves of 64 rows each (one wave per SIMD), so
 // that every K and V^T operand read from LDS feeds two products (one per
-// 32-row column block) instead of one.  The tile loop is software
-// pipelined: while the products S^T = K Q^T of tile i+1 run, the same wave
-// turns tile i's scores into probabilities (exp, row sums, bf16 packing), so
-// the softmax's vector work overlaps the matrix work of one wave instead of
-// relying on a second wave per SIMD.  Then O^T += V^T P^T for tile i.
-// Stage s of a four-stage LDS ring holds one tile's K and V^T; tile i's V^T
-// and tile i+1's K are read in iteration i, tiles i+2 and i+3 are loading.
-// Work items, the queue, the split partials and the output layout are those
-// of prefill_kernel.
+// 32-row column block) instead of one.  Each 64-key tile is taken in two
+// 32-key steps, software pipelined within the wave: while the products S^T
+// = K Q^T of step j+1 run, the wave turns step j's scores into bf16
+// probabilities, and while O^T += V^T P^T of step j runs, it masks and
+// takes the row maxima of step j+1.  The softmax's vector work thus
+// overlaps the same wave's matrix work.
+//
+// The QK products are issued as inline asm so that their accumulators (the
+// scores, read by vector code) stay in ordinary VGPRs; the compiler's own
+// PV products then keep the O^T accumulators in AGPRs, and the wave fits its
+// registers: 64 (Q) + 2 x 32 (scores of two steps) + 16 (probabilities) +
+// operands in VGPRs, 128 accumulators in AGPRs.  The asm products start
+// from a zero accumulator or chain on the same registers (which the
+// hardware orders), and their results are read by vector code only after
+// mfma_guard(), which spaces the read from the last product.
+//
+// Stage s of a four-stage LDS ring holds one tile's K and V^T: tiles i+2
+// and i+3 load while tile i is read (and tile i+1's first half of K, for
+// the pipelined step).  Work items, the queue, the split partials and the
+// output layout are those of prefill_kernel.
 // ===========================================================================
+
+// Accumulator d = A B (first k-step) or d += A B, for 32x32x16 bf16, with
+// B (the query operand) read straight from AGPRs, where it stays for the
+// whole work item.
+__device__ __forceinline__ void mfma_qk_first(f32x16 &d, const bf16x8 &a, const bf16x8 &b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_qk(f32x16 &d, const bf16x8 &a, const bf16x8 &b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+// Results of the asm products are read by vector instructions only after
+// this (24 wait states cover the 32x32x16 product's write-back; the
+// compiler does not know the asm's latency and would not insert them).
+__device__ __forceinline__ void mfma_guard(f32x16 &x, f32x16 &y) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
+}
+
+__device__ __forceinline__ float max16(const f32x16 &x) {
+  const float a = fmaxf(fmaxf(x[0], x[1]), x[2]), b = fmaxf(fmaxf(x[3], x[4]), x[5]);
+  const float c = fmaxf(fmaxf(x[6], x[7]), x[8]), d = fmaxf(fmaxf(x[9], x[10]), x[11]);
+  const float e = fmaxf(fmaxf(x[12], x[13]), x[14]);
+  return fmaxf(fmaxf(fmaxf(a, b), c), fmaxf(fmaxf(d, e), x[15]));
+}
 
 template <int D, int P>
 __global__ __launch_bounds__(kPrefillWideThreads, 1) void prefill_wide_kernel(PrefillArgs a) {
@@ -725,6 +759,7 @@ __global__ __launch_bounds__(kPrefillWideThreads, 1) void prefill_wide_kernel(Pr
   constexpr int LOADS_PER_TILE = K_INSTR + V_INSTR;
   static_assert(kPrefillRows == 64 * NW, "two 32-row column blocks per wave");
   static_assert(K_INSTR >= 1 && V_INSTR >= 1, "tile smaller than one load per lane");
+  static_assert(8 % NKK == 0 || NKK % 8 == 0, "softmax slices per k-step");
   __shared__ __attribute__((aligned(16))) uint4 smem4[NSTAGE * L::STAGE_BYTES / 16];
   __shared__ int s_next[2];
   __shared__ __attribute__((aligned(16))) float s_rope[NW][2 * D];
@@ -835,7 +870,7 @@ __global__ __launch_bounds__(kPrefillWideThreads, 1) void prefill_wide_kernel(Pr
   };
   // Tile g of the sequence must be ready before it is read: when the
   // producer fell behind (short items), issue it now and wait for it.
-  auto ensure_landed = [&](int g) {
+  auto ensure_ready = [&](int g) {
     if (ready <= g) {
       produce(g + 1);
       sync_tiles(0);
@@ -844,7 +879,7 @@ __global__ __launch_bounds__(kPrefillWideThreads, 1) void prefill_wide_kernel(Pr
 
   produce(3);
   sync_tiles(issued - 1);
-  int consumed = 0;  // tiles of the sequence whose PV product is done
+  int consumed = 0;  // tiles of the sequence fully computed
 
   const int key_a0 = st_row_key(col);
   const int vrow_swz = L::v_swz(col);
@@ -889,10 +924,14 @@ __global__ __launch_bounds__(kPrefillWideThreads, 1) void prefill_wide_kernel(Pr
         relocate_row<D, NKK>(qv[c], qrow, 16, half * 8, valid[c], a.rope.tables + sg.rope_off, s_rope[wave], a.rope);
       }
     }
+    // Q is waited for here, once per item, and moved to AGPRs; the two wait
+    // states after the last of those writes precede its first read by an
+    // asm product.
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+v"(qv[c][kk]));
+      for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+a"(qv[c][kk]));
+    asm volatile("s_nop 1" ::: "memory");
 
     f32x16 oacc[2][NDB];
 #pragma unroll
@@ -904,160 +943,197 @@ __global__ __launch_bounds__(kPrefillWideThreads, 1) void prefill_wide_kernel(Pr
     float msc[2] = {0.f, 0.f};
 
     auto stage_of = [&](int g) { return smem + (g % NSTAGE) * L::STAGE_BYTES; };
-    auto k_frag = [&](const char *st, int kk, int kb) {
+    // K operand of k-step kk for the 32-key half h of a tile; V^T operand of
+    // 16-key step ks (0..3) of a tile, channel block db.
+    auto k_frag = [&](const char *st, int kk, int h) {
       const int c = (2 * kk + half) ^ L::k_swz(key_a0);
-      return as_bf16x8(*reinterpret_cast<const u32x4 *>(st + ((key_a0 + 32 * kb) * L::KCPR + c) * 16));
+      return as_bf16x8(*reinterpret_cast<const u32x4 *>(st + ((key_a0 + 32 * h) * L::KCPR + c) * 16));
     };
-    auto v_frag = [&](const char *st, int ks, int db) {  // ks: 16-key step (kb = ks / 2, s = ks % 2)
+    auto v_frag = [&](const char *st, int ks, int db) {
       const int c = ((ks >> 1) * 4 + (ks & 1) * 2 + half) ^ vrow_swz;
       return as_bf16x8(*reinterpret_cast<const u32x4 *>(st + ((L::K_CHUNKS + (db * 32 + col) * 8) + c) * 16));
     };
-    auto tile_empty = [&](int k0) { return k0 > p_wmax || (W > 0 && k0 + kTileKeys - 1 < p_wmin - W + 1); };
-    auto tile_full = [&](int k0) { return k0 + kTileKeys - 1 <= p_wmin && (W == 0 || k0 >= p_wmax - W + 1); };
+    // A 32-key step is fully visible to every row of this wave when:
+    auto step_full = [&](int k0) { return k0 + 31 <= p_wmin && (W == 0 || k0 >= p_wmax - W + 1); };
 
-    // Scores of two tiles alternate between sA and sB (the tile loop is
-    // unrolled by two so that neither is copied).
-    f32x16 sA[2][2], sB[2][2];
+    f32x16 sc[2];          // scores of the current 32-key step (c = 0, 1)
+    bf16x8 pkA[2][2], pkB[2][2];  // probabilities of even / odd steps: [c][16-key half]
+    float alpha[2] = {1.f, 1.f};
+    bool rescale = false;  // O^T waits for its rescale until the previous step's PV is in
 
-    // S^T of tile g (K from its stage) into s, all four products per k-step,
-    // K operands one k-step ahead.  `work(kk)` runs after the products of
-    // k-step kk are issued (the softmax of the previous tile, in slices).
-    auto qk = [&](f32x16 (&s)[2][2], const char *st, auto &&work) {
-      bf16x8 k0 = k_frag(st, 0, 0), k1 = k_frag(st, 0, 1);
+    // Mask (edge steps), row maxima across the lane pair and the lazy
+    // rescale decision: the running max moves only when a step's max exceeds
+    // it by more than 2^8.  Rows with no visible key yet hold O = 0 and l = 0
+    // and need no rescale.  l is rescaled at once; O^T after the previous
+    // step's products are accumulated (it must include them).
+    auto head = [&](int k0, bool mask) {
+      bool bump[2], need[2];
+      float m_new[2];
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        __builtin_amdgcn_sched_barrier(0);
-        bf16x8 n0 = k0, n1 = k1;
-        if (kk + 1 < NKK) {
-          n0 = k_frag(st, kk + 1, 0);
-          n1 = k_frag(st, kk + 1, 1);
-        }
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          s[c][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qv[c][kk], kk ? s[c][0] : f32x16{}, 0, 0, 0);
-          s[c][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qv[c][kk], kk ? s[c][1] : f32x16{}, 0, 0, 0);
-        }
-        work(kk);
-        k0 = n0;
-        k1 = n1;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    };
-
-    // Mask (edge tiles), row max and the lazy rescale of tile k0's scores.
-    auto softmax_head = [&](f32x16 (&s)[2][2], int k0, bool mask) {
-      if (mask) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
+      for (int c = 0; c < 2; ++c) {
+        if (mask) {
           const unsigned lo_rel = static_cast<unsigned>(lo[c] - k0 - 8 * half);
           const unsigned span = static_cast<unsigned>(pp[c] - lo[c]);
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int off = ((v >> 3) << 4) + (v & 7);
-            if (static_cast<unsigned>(off) - lo_rel > span) s[c][0][v] = kNegInf;
-            if (static_cast<unsigned>(off + 32) - lo_rel > span) s[c][1][v] = kNegInf;
+            if (static_cast<unsigned>(off) - lo_rel > span) sc[c][v] = kNegInf;
           }
         }
+        float x = max16(sc[c]);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        bump[c] = x * a.scale_log2 > m[c] * a.scale_log2 + kRescaleLog2;
+        need[c] = bump[c] && m[c] != kNegInf;
+        m_new[c] = bump[c] ? x : m[c];
       }
-      bool bump[2];
-      float m_new[2];
+      rescale = __builtin_amdgcn_ballot_w64(need[0] || need[1]) != 0;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        float mx = max32(s[c][0], s[c][1]);
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        bump[c] = mx * a.scale_log2 > m[c] * a.scale_log2 + kRescaleLog2;
-        m_new[c] = bump[c] ? mx : m[c];
-      }
-      if (__builtin_expect(__builtin_amdgcn_ballot_w64(bump[0] || bump[1]) != 0, 0)) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const float ms = m_new[c] == kNegInf ? 0.f : m_new[c] * a.scale_log2;
-          const float alpha = bump[c] ? fast_exp2(m[c] * a.scale_log2 - ms) : 1.f;
-          l[c] *= alpha;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) oacc[c][db] *= alpha;
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
+        const float ms = m_new[c] == kNegInf ? 0.f : m_new[c] * a.scale_log2;
+        alpha[c] = need[c] ? fast_exp2(m[c] * a.scale_log2 - ms) : 1.f;
+        l[c] *= alpha[c];
         m[c] = m_new[c];
-        msc[c] = m[c] == kNegInf ? 0.f : m[c] * a.scale_log2;
+        msc[c] = ms;
       }
     };
-    // Probabilities of slice j (j = 4 c + 2 kb + s: 8 keys of one row block)
-    // in place, packed to bf16 for the PV product.
-    bf16x8 pk[2][2][2];
-    auto softmax_slice = [&](f32x16 (&s)[2][2], int j) {
-      const int c = j >> 2, kb = (j >> 1) & 1, sh = j & 1;
-      float e[8];
+    auto apply_rescale = [&]() {
+      if (__builtin_expect(rescale, 0)) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) e[u] = fast_exp2(fmaf(s[c][kb][8 * sh + u], a.scale_log2, -msc[c]));
-      l[c] += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-      pk[c][kb][sh] = pack8_bf16(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) oacc[c][db] *= alpha[c];
+      }
     };
-    // O^T += V^T P^T for the tile in stage st, V operands one step ahead.
-    auto pv = [&](const char *st) {
-      bf16x8 vn = v_frag(st, 0, 0);
+    // Probabilities of values v0 .. v0+nv-1 of the current scores into pk.
+    auto body = [&](bf16x8 (&pk)[2][2], int c, int v0, int nv) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      for (int u = 0; u < nv; ++u) {
+        sc[c][v0 + u] = fast_exp2(fmaf(sc[c][v0 + u], a.scale_log2, -msc[c]));
+        l[c] += sc[c][v0 + u];
+      }
+      // pack each group of 8 whose last value this slice computed
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const bf16x8 va = vn;
-          const int nks = db + 1 < NDB ? ks : ks + 1, ndb = db + 1 < NDB ? db + 1 : 0;
-          if (nks < 4) vn = v_frag(st, nks, ndb);
-#pragma unroll
-          for (int c = 0; c < 2; ++c)
-            oacc[c][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk[c][ks >> 1][ks & 1], oacc[c][db], 0, 0, 0);
+      for (int w = 0; w < 2; ++w) {
+        if (v0 <= 8 * w + 7 && 8 * w + 7 < v0 + nv) {
+          const f32x16 &x = sc[c];
+          pk[c][w] = pack8_bf16(x[8 * w], x[8 * w + 1], x[8 * w + 2], x[8 * w + 3], x[8 * w + 4], x[8 * w + 5],
+                                x[8 * w + 6], x[8 * w + 7]);
         }
+      }
+    };
+    // S^T of half h of the tile in st into sc (K operands one k-step ahead).
+    auto qk_step = [&](const char *st, int h) {
+      bf16x8 kf = k_frag(st, 0, h);
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8 kn = kk + 1 < NKK ? k_frag(st, kk + 1, h) : kf;
+        if (kk == 0) {
+          mfma_qk_first(sc[0], kf, qv[0][0]);
+          mfma_qk_first(sc[1], kf, qv[1][0]);
+        } else {
+          mfma_qk(sc[0], kf, qv[0][kk]);
+          mfma_qk(sc[1], kf, qv[1][kk]);
+        }
+        kf = kn;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_guard(sc[0], sc[1]);
+    };
+    // O^T += V^T P^T for half h of the tile in st with probabilities pk_prev,
+    // and after each product pair a slice of the current step's body into
+    // pk_cur (pk_prev == nullptr: the body alone).
+    auto pv_body = [&](const char *st, int h, bf16x8 (*pk_prev)[2][2], bf16x8 (&pk_cur)[2][2]) {
+      constexpr int NG = 2 * NDB;   // product pairs
+      constexpr int VPG = 32 / NG;  // body values per pair
+      if (!pk_prev) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) body(pk_cur, c, 0, 16);
+        return;
+      }
+      bf16x8 vf = v_frag(st, 2 * h, 0);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int ks = g / NDB, db = g % NDB;
+        const bf16x8 vn = g + 1 < NG ? v_frag(st, 2 * h + (g + 1) / NDB, (g + 1) % NDB) : vf;
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          oacc[c][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, (*pk_prev)[c][ks], oacc[c][db], 0, 0, 0);
+        const int j0 = g * VPG;
+        body(pk_cur, j0 / 16, j0 % 16, VPG);
+        vf = vn;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // PV of the last step alone.
+    auto pv_last = [&](const char *st, int h, bf16x8 (&pk)[2][2]) {
+      bf16x8 vf = v_frag(st, 2 * h, 0);
+#pragma unroll
+      for (int g = 0; g < 2 * NDB; ++g) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int ks = g / NDB, db = g % NDB;
+        const bf16x8 vn = g + 1 < 2 * NDB ? v_frag(st, 2 * h + (g + 1) / NDB, (g + 1) % NDB) : vf;
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          oacc[c][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[c][ks], oacc[c][db], 0, 0, 0);
+        vf = vn;
       }
     };
 
     const int n_tiles = it.tile_end - it.tile_begin;
-    const int fetch_i = max(0, n_tiles - 4);  // iteration whose end publishes the next item's index
-    const int g0 = consumed;                   // this item's first tile in the sequence
-    auto no_work = [](int) {};
+    const int fetch_t = max(0, n_tiles - 3);  // tile whose closing barrier publishes the next item's index
+    const int g0 = consumed;
+    const int kb0 = it.tile_begin * kTileKeys;
 
-    // One iteration: softmax + PV of tile i (scores in s_cur), with the QK of
-    // tile i + 1 (into s_nxt) under the softmax.
-    auto iteration = [&](int i, f32x16 (&s_cur)[2][2], f32x16 (&s_nxt)[2][2]) {
-      const int k0 = (it.tile_begin + i) * kTileKeys;
-      if (i == fetch_i && tid == 0) s_next[fslot] = atomicAdd(a.counter, 1);
-      produce(g0 + i + 4);
-      const bool has_next = i + 1 < n_tiles;
-      const bool next_live = has_next && !tile_empty(k0 + kTileKeys);
-      const bool live = !tile_empty(k0);
-      if (live) softmax_head(s_cur, k0, !tile_full(k0));
-      if (next_live) {
-        ensure_landed(g0 + i + 1);
-        const char *stk = stage_of(g0 + i + 1);
-        if (live)
-          qk(s_nxt, stk, [&](int kk) {
-#pragma unroll
-            for (int j = kk * 8 / NKK; j < (kk + 1) * 8 / NKK; ++j) softmax_slice(s_cur, j);
-          });
-        else
-          qk(s_nxt, stk, no_work);
-      } else if (live) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) softmax_slice(s_cur, j);
-      }
-      if (live) pv(stage_of(g0 + i));
-      sync_tiles(issued - (g0 + i) - 3);
-      if (i == fetch_i) {
+    // Tile t's bookkeeping around its two steps: the producer before, the
+    // barrier (and the next item's index) after.
+    auto tile_begin = [&](int t) {
+      if (t == fetch_t && tid == 0) s_next[fslot] = atomicAdd(a.counter, 1);
+      produce(g0 + t + 3);
+      ensure_ready(g0 + t);
+    };
+    auto tile_end = [&](int t) {
+      sync_tiles(issued - (g0 + t) - 2);
+      if (t == fetch_t) {
         nxt = __builtin_amdgcn_readfirstlane(s_next[fslot]);
         fslot ^= 1;
         if (p_item < 0 && nxt < n_items) p_set(nxt);
       }
     };
-
-    // Prologue: QK of the first tile.
-    ensure_landed(g0);
-    if (!tile_empty(it.tile_begin * kTileKeys)) qk(sA, stage_of(g0), no_work);
-    for (int i = 0; i < n_tiles; i += 2) {
-      iteration(i, sA, sB);
-      if (i + 1 < n_tiles) iteration(i + 1, sB, sA);
+    // Tile 0: its first step has no previous products (and O^T = 0 needs no
+    // rescale).
+    {
+      tile_begin(0);
+      const char *st = stage_of(g0);
+      qk_step(st, 0);
+      head(kb0, !step_full(kb0));
+      pv_body(st, 1, nullptr, pkA);
+      qk_step(st, 1);
+      head(kb0 + 32, !step_full(kb0 + 32));
+      pv_body(st, 0, &pkA, pkB);
+      apply_rescale();
+      tile_end(0);
     }
+    for (int t = 1; t < n_tiles; ++t) {
+      tile_begin(t);
+      const char *st = stage_of(g0 + t);
+      const int k0 = kb0 + t * kTileKeys;
+      // step 2t: half 0 of tile t; the products of step 2t-1 (half 1 of the
+      // previous tile) run under its softmax body
+      qk_step(st, 0);
+      head(k0, !step_full(k0));
+      pv_body(stage_of(g0 + t - 1), 1, &pkB, pkA);
+      apply_rescale();
+      // step 2t+1: half 1 of tile t, with the products of step 2t
+      qk_step(st, 1);
+      head(k0 + 32, !step_full(k0 + 32));
+      pv_body(st, 0, &pkA, pkB);
+      apply_rescale();
+      tile_end(t);
+    }
+    pv_last(stage_of(g0 + n_tiles - 1), 1, pkB);
     consumed = g0 + n_tiles;
 
 #pragma unroll

@@ -121,6 +121,7 @@ struct segkv_ctx {
   int32_t decode_pps = kDefaultDecodeMinPages;  // minimum pages per decode workgroup
   int64_t prefill_split_tiles = kDefaultPrefillSplitTiles;  // 0 = automatic
   int32_t prefill_order = 0;  // 0 = longest-first, 1 = XCD-aware
+  int32_t prefill_kernel = 0;  // 0 = default, 1 = 8 waves x 32 rows, 2 = 4 waves x 64 rows
 
   // timing
   int32_t timing_mask = 0;  // bit k: record events around kernel k
@@ -1167,7 +1168,8 @@ int segkv_prefill(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *se
   TimedLaunch t{};
   rc = timed_begin(c, &t, SEGKV_KERNEL_PREFILL);
   if (rc) return rc;
-  hipError_t e = launch_prefill(a, static_cast<int>(n_wgs), c->D, c->P, c->stream);
+  hipError_t e = c->prefill_kernel == 2 ? launch_prefill_wide(a, static_cast<int>(n_wgs), c->D, c->P, c->stream)
+                                        : launch_prefill(a, static_cast<int>(n_wgs), c->D, c->P, c->stream);
   if (e != hipSuccess) return c->device_fail(e, "prefill launch");
   rc = timed_end(c, &t);
   if (rc) return rc;
@@ -1656,6 +1658,10 @@ int segkv_set_tuning(segkv_ctx *c, int32_t knob, int64_t value) {
     case SEGKV_TUNE_PREFILL_ORDER:
       if (value > 1) return c->fail(SEGKV_E_INVAL, "prefill order must be 0 (longest first) or 1 (XCD-aware)");
       c->prefill_order = value > 0 ? static_cast<int32_t>(value) : 0;
+      return SEGKV_OK;
+    case SEGKV_TUNE_PREFILL_KERNEL:
+      if (value > 2) return c->fail(SEGKV_E_INVAL, "prefill kernel must be 0 (default), 1 (8 x 32 rows) or 2 (4 x 64 rows)");
+      c->prefill_kernel = value > 0 ? static_cast<int32_t>(value) : 0;
       return SEGKV_OK;
     default:
       return c->fail(SEGKV_E_INVAL, "unknown tuning knob %d", knob);

@@ -54,9 +54,10 @@ class WorkloadRun:
 
     def __init__(self, w: Workload, dev: DeviceInputs, page_order_seed: Optional[int] = None,
                  windows=None, num_pages: Optional[int] = None, deltas=None, rope_theta: float = 0.0,
-                 rope_style: int = 0, rope_dims: int = 0):
+                 rope_style: int = 0, rope_dims: int = 0, pools=None):
         """``deltas[b][g]``: query relocation offset of sequence b, KV head g
-        (None = no relocation)."""
+        (None = no relocation).  ``pools``: (k_pool, v_pool) tensors to use
+        instead of allocating them."""
         self.w = w
         self.dev = dev
         self.windows = tuple(w.windows if windows is None else windows)
@@ -65,7 +66,8 @@ class WorkloadRun:
                            num_pages or pages_for(w), self.windows, softmax_scale=w.scale,
                            page_order_seed=w.page_order_seed if page_order_seed is None else page_order_seed,
                            rope_theta=rope_theta, rope_style=rope_style, rope_dims=rope_dims,
-                           max_batch_q_tokens=max(1, sum(w.q_lens)))
+                           max_batch_q_tokens=max(1, sum(w.q_lens)),
+                           k_pool=None if pools is None else pools[0], v_pool=None if pools is None else pools[1])
         self.seq_ids = list(range(w.n_seqs))
 
     def append_fill(self):
@@ -76,9 +78,15 @@ class WorkloadRun:
     def append_queries(self):
         self.ctx.append_pages(0, self.seq_ids, self.w.q_lens, self.w.q_lens, self.dev.k_q, self.dev.v_q)
 
-    def load(self):
+    def load(self, after_append=None):
+        """Appends the fill and the queries (``after_append(ctx)`` runs after
+        each), then sets the relocation offsets."""
         self.append_fill()
+        if after_append:
+            after_append(self.ctx)
         self.append_queries()
+        if after_append:
+            after_append(self.ctx)
         if self.deltas is not None:
             for b, s in enumerate(self.seq_ids):
                 self.ctx.set_relocation(s, self.deltas[b])

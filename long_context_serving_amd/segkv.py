@@ -37,6 +37,7 @@ KERNEL_COUNT = 9
 TUNE_DECODE_MIN_PAGES = 0
 TUNE_PREFILL_SPLIT_TILES = 1
 TUNE_PREFILL_ORDER = 2
+TUNE_PREFILL_KERNEL = 3
 
 # Every entry point include/segkv.h declares.
 EXPORTED = (

@@ -3,6 +3,7 @@ and compare with the fp64 oracle on the same seeded inputs."""
 
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
@@ -16,9 +17,62 @@ from oracle import rope as RP
 O_TOL = 2e-2    # max-abs on bf16 outputs against the unrounded fp64 oracle
 LSE_TOL = 1e-3  # max-abs on fp32 log-sum-exp
 
+# Prefill kernel the parity runs select (SEGKV_TUNE_PREFILL_KERNEL): the
+# suite can be run once per kernel variant.
+PREFILL_KERNEL = int(os.environ.get("SEGKV_TEST_PREFILL_KERNEL", "0"))
+
 
 def say(*msg):
     print("[gpu]", *msg, file=sys.stderr, flush=True)
+
+
+CANARY_BITS = 0x7F7F  # bf16 bit pattern of every byte pair the library must not write (3.39e38)
+GUARD_PAGES = 4
+
+
+class GuardedPools:
+    """K and V pools with canary guard pages on both sides: the whole
+    allocation is filled with a pattern before the context is created; after
+    a run, the guard pages and every page no segment ever held must still
+    hold it.  A scatter or copy-on-write write to a wrong page id, or past
+    either end of the pool, shows up here even when no later read meets it."""
+
+    def __init__(self, num_pages, page_size, head_dim, device="cuda"):
+        import torch
+        self.n, self.g = int(num_pages), GUARD_PAGES
+        shape = (self.n + 2 * self.g, page_size, head_dim)
+        self.k_all = torch.empty(shape, dtype=torch.bfloat16, device=device)
+        self.v_all = torch.empty((self.n + 2 * self.g, head_dim, page_size), dtype=torch.bfloat16, device=device)
+        for t in (self.k_all, self.v_all):
+            t.view(torch.int16).fill_(CANARY_BITS)
+        self.k = self.k_all[self.g:self.g + self.n]
+        self.v = self.v_all[self.g:self.g + self.n]
+        self.used = set()
+
+    @property
+    def pools(self):
+        return self.k, self.v
+
+    def note(self, ctx):
+        """Record every page some segment of ctx holds now."""
+        for layer in range(ctx.num_layers):
+            for s in range(ctx.max_seqs):
+                for g in range(ctx.num_kv_heads):
+                    self.used.update(int(p) for p in ctx.page_table(layer, s, g)[2])
+
+    def check(self):
+        import torch
+        if self.k_all.is_cuda:
+            torch.cuda.synchronize()
+        for name, t in (("K", self.k_all), ("V", self.v_all)):
+            intact = (t.view(torch.int16) == CANARY_BITS).flatten(1).all(dim=1).cpu().numpy()
+            assert intact[:self.g].all(), f"{name} guard pages before the pool were written"
+            assert intact[self.g + self.n:].all(), f"{name} guard pages after the pool were written"
+            never = np.array(sorted(set(range(self.n)) - self.used), dtype=np.int64)
+            if len(never):
+                bad = never[~intact[self.g + never]]
+                assert len(bad) == 0, f"{name} pages {bad[:8].tolist()} were written but never held by a segment"
+        return True
 
 
 def gpu_run(w, x, mode="prefill", seed=None, windows=None, split_tiles=None, pps=None, repeat=1, rope=None):
@@ -31,18 +85,22 @@ def gpu_run(w, x, mode="prefill", seed=None, windows=None, split_tiles=None, pps
     dev = R.to_device(w, x)
     rkw = {} if rope is None else dict(deltas=rope["deltas"], rope_theta=rope.get("theta", 0.0),
                                        rope_style=rope.get("style", 0), rope_dims=rope.get("dims", 0))
-    run = R.WorkloadRun(w, dev, page_order_seed=seed, windows=windows, **rkw)
+    canary = GuardedPools(R.pages_for(w), w.page_size, w.head_dim)
+    run = R.WorkloadRun(w, dev, page_order_seed=seed, windows=windows, pools=canary.pools, **rkw)
     try:
+        if PREFILL_KERNEL:
+            run.ctx.set_tuning(S.TUNE_PREFILL_KERNEL, PREFILL_KERNEL)
         if split_tiles is not None:
             run.ctx.set_tuning(S.TUNE_PREFILL_SPLIT_TILES, split_tiles)
         if pps is not None:
             run.ctx.set_tuning(S.TUNE_DECODE_MIN_PAGES, pps)
-        run.load()
+        run.load(after_append=canary.note)
         outs = []
         for _ in range(repeat):
             o, lse = run.prefill() if mode == "prefill" else run.decode()
             torch.cuda.synchronize()
             outs.append((S.bf16_bits(o), lse.cpu().numpy().astype(np.float64)))
+        canary.check()
         return outs if repeat > 1 else outs[0]
     finally:
         run.close()

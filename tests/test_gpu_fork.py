@@ -11,7 +11,7 @@ from long_context_serving_amd import segkv as S
 from long_context_serving_amd import workloads as wl
 from oracle import attention as A
 
-from gpu_helpers import LSE_TOL, O_TOL, say
+from gpu_helpers import LSE_TOL, O_TOL, GuardedPools, say
 
 pytestmark = pytest.mark.gpu
 
@@ -36,8 +36,9 @@ class Scenario:
         self.v = S.bf16_tensor(self.x.v)
         self.windows = tuple(windows)
         n_pages = pages or (seqs * (n_tokens // p + 2) * hkv)
+        self.canary = GuardedPools(n_pages, p, d)
         self.kv = S.SegKV(1, hq, hkv, d, p, seqs, n_pages, list(windows), softmax_scale=self.w.scale,
-                          page_order_seed=seed + 1)
+                          page_order_seed=seed + 1, k_pool=self.canary.k, v_pool=self.canary.v)
         self.hist = {}
         self.next_row = 0
         self.torch = torch
@@ -54,6 +55,7 @@ class Scenario:
         idx = self.torch.from_numpy(np.concatenate(rows + [np.zeros(0, np.int64)])).cuda()
         self.kv.append_pages(0, seqs, counts, n_query, self.k.index_select(0, idx).contiguous(),
                              self.v.index_select(0, idx).contiguous())
+        self.canary.note(self.kv)
 
     def fork(self, src, dst):
         self.kv.fork(src, dst)
@@ -90,6 +92,7 @@ class Scenario:
         assert worst[0] <= O_TOL and worst[1] <= LSE_TOL
 
     def close(self):
+        self.canary.check()
         self.kv.close()
 
 
