@@ -297,6 +297,14 @@ __device__ __forceinline__ void lds_dma16(const void *src, void *lds_dst) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0));
 }
 
+// The same copy with the source given as a wave-uniform base (SGPRs) plus a
+// per-lane 32-bit byte offset (global_load_lds_dwordx4's saddr form): the
+// address arithmetic per tile is then scalar.
+__device__ __forceinline__ void lds_dma16_s(const void *sbase, uint32_t voff, void *lds_dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_dst)));
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0));
+}
+
 // Load of a per-call table entry (4, 16 or 32 bytes at a wave-uniform,
 // 4-byte aligned address; no kernel writes these tables) through the scalar
 // cache.  Written as asm because the compiler turns such reads into vector
@@ -426,30 +434,30 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
       const int c = (j * NW + wave) * 64 + lane;
       const int row = c / L::KCPR;
       const int logical = (c % L::KCPR) ^ L::k_swz(row);
-      const uint16_t *src;
       if constexpr (P == kTileKeys) {
-        src = a.k_pool + static_cast<size_t>(pid[0]) * (P * D) + row * D + logical * 8;
+        // one page per tile: a scalar page base and a 32-bit lane offset
+        lds_dma16_s(a.k_pool + static_cast<size_t>(pid[0]) * (P * D), static_cast<uint32_t>((row * D + logical * 8) * 2),
+                    st + (j * NW + wave) * 1024);
       } else {
         int slot;
         const int page = page_of(row, &slot);
-        src = a.k_pool + (static_cast<size_t>(page) * P + slot) * D + logical * 8;
+        lds_dma16(a.k_pool + (static_cast<size_t>(page) * P + slot) * D + logical * 8, st + (j * NW + wave) * 1024);
       }
-      lds_dma16(src, st + (j * NW + wave) * 1024);
     }
 #pragma unroll
     for (int j = 0; j < V_INSTR; ++j) {
       const int c = (j * NW + wave) * 64 + lane;
       const int d = c / 8;
       const int logical = (c % 8) ^ L::v_swz(d);
-      const uint16_t *src;
       if constexpr (P == kTileKeys) {
-        src = a.v_pool + static_cast<size_t>(pid[0]) * (P * D) + d * P + logical * 8;
+        lds_dma16_s(a.v_pool + static_cast<size_t>(pid[0]) * (P * D), static_cast<uint32_t>((d * P + logical * 8) * 2),
+                    st + L::K_CHUNKS * 16 + (j * NW + wave) * 1024);
       } else {
         int slot;
         const int page = page_of(logical * 8, &slot);
-        src = a.v_pool + static_cast<size_t>(page) * (P * D) + d * P + slot;
+        lds_dma16(a.v_pool + static_cast<size_t>(page) * (P * D) + d * P + slot,
+                  st + L::K_CHUNKS * 16 + (j * NW + wave) * 1024);
       }
-      lds_dma16(src, st + L::K_CHUNKS * 16 + (j * NW + wave) * 1024);
     }
   };
   auto produce = [&](int limit) {
@@ -1308,9 +1316,10 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void score_kernel(ScoreArgs a) 
       const int c = (j * NW + wave) * 64 + lane;
       const int row = c / L::KCPR;
       const int logical = (c % L::KCPR) ^ L::k_swz(row);
-      const uint16_t *src;
       if constexpr (P == kTileKeys) {
-        src = a.k_pool + static_cast<size_t>(pid[0]) * (P * D) + row * D + logical * 8;
+        // one page per tile: a scalar page base and a 32-bit lane offset
+        lds_dma16_s(a.k_pool + static_cast<size_t>(pid[0]) * (P * D), static_cast<uint32_t>((row * D + logical * 8) * 2),
+                    st + (j * NW + wave) * 1024);
       } else {
         const int rel = k0 + row - sg.first_token;
         const int slot = rel >= 0 && rel / P <= last_page ? row % P : 0;
@@ -1318,9 +1327,8 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void score_kernel(ScoreArgs a) 
 #pragma unroll
         for (int i = 1; i < NP; ++i)
           if (row / P == i) page = pid[i];
-        src = a.k_pool + (static_cast<size_t>(page) * P + slot) * D + logical * 8;
+        lds_dma16(a.k_pool + (static_cast<size_t>(page) * P + slot) * D + logical * 8, st + (j * NW + wave) * 1024);
       }
-      lds_dma16(src, st + (j * NW + wave) * 1024);
     }
   };
 

@@ -1,7 +1,8 @@
 // Internal layout shared by the host library and its HIP kernels.
 //
-// Device tables are rebuilt on the host for every call and uploaded with
-// one host-to-device copy into the context's metadata buffer, in this order:
+// Device tables are rebuilt on the host for every call and copied from
+// pinned staging to the start of the call's device workspace (caller-owned,
+// or the fixed scratch of segkv_decode_noalloc), in this order:
 //   SeqDesc  [n_seqs]
 //   SegDesc  [n_seqs * num_kv_heads]
 //   int32    page ids of every listed segment (SegDesc::page_off indexes here)
@@ -9,6 +10,7 @@
 //            offset of the listed segments (SegDesc::rope_off indexes here)
 //   work items of the call (ScatterItem, PrefillItem or DecodeItem)
 //   combine items (CombineItem), when the call has split work
+// Split partials follow the tables at the next 256-byte boundary.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -75,12 +75,15 @@ class GuardedPools:
         return True
 
 
-def gpu_run(w, x, mode="prefill", seed=None, windows=None, split_tiles=None, pps=None, repeat=1, rope=None):
+def gpu_run(w, x, mode="prefill", seed=None, windows=None, split_tiles=None, pps=None, repeat=1, rope=None,
+            prefill_kernel=None):
     """``rope``: dict(deltas=[n_seqs][Hkv], theta=, style=, dims=) for query
-    relocation, or None."""
+    relocation, or None.  ``prefill_kernel``: SEGKV_TUNE_PREFILL_KERNEL value
+    (None = PREFILL_KERNEL)."""
     import torch
     say(f"{mode} {w.name} kv={w.kv_lens[:4]} q={w.q_lens[:4]} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
         f"D={w.head_dim} P={w.page_size} W={windows or w.windows} seed={seed} split={split_tiles} pps={pps}"
+        f" kernel={PREFILL_KERNEL if prefill_kernel is None else prefill_kernel}"
         + ("" if rope is None else f" rope={rope}"))
     dev = R.to_device(w, x)
     rkw = {} if rope is None else dict(deltas=rope["deltas"], rope_theta=rope.get("theta", 0.0),
@@ -88,8 +91,9 @@ def gpu_run(w, x, mode="prefill", seed=None, windows=None, split_tiles=None, pps
     canary = GuardedPools(R.pages_for(w), w.page_size, w.head_dim)
     run = R.WorkloadRun(w, dev, page_order_seed=seed, windows=windows, pools=canary.pools, **rkw)
     try:
-        if PREFILL_KERNEL:
-            run.ctx.set_tuning(S.TUNE_PREFILL_KERNEL, PREFILL_KERNEL)
+        kernel = PREFILL_KERNEL if prefill_kernel is None else prefill_kernel
+        if kernel:
+            run.ctx.set_tuning(S.TUNE_PREFILL_KERNEL, kernel)
         if split_tiles is not None:
             run.ctx.set_tuning(S.TUNE_PREFILL_SPLIT_TILES, split_tiles)
         if pps is not None:

@@ -80,6 +80,8 @@ def test_zero_or_cleared_offsets_are_bitwise_the_plain_path():
     o1, l1 = gpu_run(w, x, rope=dict(deltas=[[0, 0]]))
     assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
     run = R.WorkloadRun(w, R.to_device(w, x), deltas=[[900, 900]])
+    if PREFILL_KERNEL:
+        run.ctx.set_tuning(S.TUNE_PREFILL_KERNEL, PREFILL_KERNEL)
     run.load()
     run.ctx.set_relocation(0, None)
     o2, l2 = run.prefill()
