@@ -70,7 +70,15 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "visible-token attention TFLOP/s (prefill) & visible-KV GB/s (decode), 1 MI355X"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "long_context_serving_amd", "csrc", "kernels.hip")
+CSRC = os.path.join(ROOT, "long_context_serving_amd", "csrc")
+# Sources whose digest identifies each measured kernel: its own file plus the
+# shared device helpers and the argument layouts.
+KERNEL_SRC = {
+    "prefill": ["prefill.hip", "kernels_common.h", "segkv_internal.h"],
+    "score": ["score.hip", "kernels_common.h", "segkv_internal.h"],
+    "decode": ["decode.hip", "kernels_common.h", "segkv_internal.h"],
+    "merge": ["merge.hip", "kernels_common.h", "segkv_internal.h"],
+}
 RELOCATION_OFFSET = 8192    # document offset of the relocation arm
 
 
@@ -78,21 +86,30 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_source_hash(kind: str) -> str:
+    """First 16 hex digits of the sha256 over the kernel's source files."""
+    h = hashlib.sha256()
+    for name in KERNEL_SRC[kind]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(key: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when the kernel source changed since the counters were taken."""
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    ("<kind>_<workload>"), or None when the kernel's sources changed since
+    the counters were taken (or a prefill variant other than the default is
+    timed)."""
+    kind = key.split("_", 1)[0]
+    if kind not in KERNEL_SRC or (kind == "prefill" and PREFILL_KERNEL not in (0, 1)):
+        return None
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     e = t.get(key)
-    if not e or e.get("kernel_source_sha256_16") != kernel_source_hash():
+    if not e or e.get("kernel_source_sha256_16") != kernel_source_hash(kind):
         return None
     return e.get("bytes_per_launch")
 
@@ -313,7 +330,8 @@ def router_arm(w, dev, steps, warmup, flops_qk):
     return {"workload": w.name, "k_per_seq": k, "ms_per_call": dt * 1e3, "score_kernel_ms": s_ms,
             "reduce_kernel_ms": r_ms, "topk_kernel_ms": k_ms, "qk_flops": flops_qk,
             "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": tf / PEAK_BF16_TFLOPS, "traffic": None, "kernel": "score_kernel<128,64>",
+                         "frac": tf / PEAK_BF16_TFLOPS, "traffic": measured_traffic("score_" + w.name),
+                         "kernel": "score_kernel<128,64>",
                          "avg_launch_ms": s_ms}}
 
 
@@ -511,7 +529,7 @@ def main():
                     help="profiling runs: only the segmented headline prefill, the 128K chunk, the Mistral-7B-shaped "
                          "prefill, segmented decode, the merge or the router")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--prefill-kernel", type=int, default=0, choices=[0, 1, 2],
+    ap.add_argument("--prefill-kernel", type=int, default=0, choices=[0, 1, 2, 3],
                     help="prefill kernel variant (SEGKV_TUNE_PREFILL_KERNEL); 0 = the library's default")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates rocprofv3 byte counters)")

@@ -371,7 +371,12 @@ int segkv_read_timing(segkv_ctx *ctx, int32_t kernel, double *total_ms, int64_t 
  *                                      2: the kernel of 4 waves x 64 rows (one
  *                                      wave per SIMD, each K/V^T operand read
  *                                      from LDS feeds two products, softmax
- *                                      pipelined under the products).
+ *                                      pipelined under the products);
+ *                                      3: the 8 x 32-row kernel as two groups
+ *                                      of four waves one phase apart (one
+ *                                      group's products beside the other's
+ *                                      softmax), over per-workgroup item lists
+ *                                      balanced on the host.
  * Results do not depend on the knobs beyond fp32 rounding of split merges.
  */
 enum segkv_tune {

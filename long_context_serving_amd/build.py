@@ -1,8 +1,9 @@
 """Build libsegkv.so for gfx950 with hipcc, in-tree.
 
 The library is the C ABI declared in include/segkv.h: host code
-(csrc/segkv_host.cpp) and HIP kernels (csrc/kernels.hip).  Packed fp32
-instructions are disabled for the device code (-packed-fp32-ops).
+(csrc/segkv_host.cpp) and HIP kernels (csrc/*.hip, one file per kernel
+family, sharing csrc/kernels_common.h).  Packed fp32 instructions are
+disabled for the device code (-packed-fp32-ops).
 """
 
 from __future__ import annotations
@@ -17,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libsegkv.so")
-SOURCES = [os.path.join(CSRC, "segkv_host.cpp"), os.path.join(CSRC, "kernels.hip")]
+KERNEL_SOURCES = ["scatter.hip", "prefill.hip", "prefill_variants.hip", "score.hip", "decode.hip", "merge.hip"]
+SOURCES = [os.path.join(CSRC, "segkv_host.cpp")] + [os.path.join(CSRC, f) for f in KERNEL_SOURCES]
 ARCH = "gfx950"
 
 

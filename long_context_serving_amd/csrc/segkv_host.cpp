@@ -1,5 +1,5 @@
 // Host side of libsegkv: the C ABI, the per-head segment page allocator and
-// the per-call device table builder.  Device work is in kernels.hip.
+// the per-call device table builder.  Device work is in the csrc/*.hip kernels.
 //
 // The allocator follows the storage rule of SegPagedAttention: KV pages are
 // kept per (layer, head) and per segment, and a head stores only the tokens
@@ -24,6 +24,7 @@
 
 #include "segkv.h"
 #include "segkv_internal.h"
+#include "segkv_sched.h"
 
 using namespace segkv;
 
@@ -37,6 +38,12 @@ constexpr int kDefaultDecodeMinPages = 8;
 constexpr size_t kPrestageRoom = 64 << 10;  // initial room for prefill tables staged by an append
 constexpr int kDefaultPrefillSplitTiles = 0;  // automatic
 constexpr int64_t kMinSplitTiles = 16;
+// Cost of starting an item and writing its output, in tile steps, when the
+// two-group prefill's items are balanced over its workgroups.
+constexpr int64_t kItemCostTiles = 2;
+// SEGKV_TUNE_PREFILL_KERNEL values of the two variants beside the default kernel
+constexpr int32_t kPrefillWide = 2;
+constexpr int32_t kPrefillTwoGroup = 3;
 
 struct Segment {
   int32_t first_token = 0;
@@ -121,7 +128,7 @@ struct segkv_ctx {
   int32_t decode_pps = kDefaultDecodeMinPages;  // minimum pages per decode workgroup
   int64_t prefill_split_tiles = kDefaultPrefillSplitTiles;  // 0 = automatic
   int32_t prefill_order = 0;  // 0 = longest-first, 1 = XCD-aware
-  int32_t prefill_kernel = 0;  // 0 = default, 1 = 8 waves x 32 rows, 2 = 4 waves x 64 rows
+  int32_t prefill_kernel = 0;  // 0/1 = 8 waves x 32 rows in step (default), 2 = 4 waves x 64 rows, 3 = two-group schedule
 
   // timing
   int32_t timing_mask = 0;  // bit k: record events around kernel k
@@ -132,6 +139,10 @@ struct segkv_ctx {
 
   // scratch reused across calls
   std::vector<int32_t> scratch_i32;
+  std::vector<int32_t> scratch_wg;     // per-workgroup item offsets of the two-group prefill
+  std::vector<int32_t> scratch_owner;  // workgroup of each prefill item
+  std::vector<int32_t> scratch_order;  // prefill items grouped by workgroup
+  std::vector<int64_t> scratch_cost;
   std::vector<int32_t> scratch_cnt;  // counting sort of the prefill work list (an append plans a prefill too)
   std::vector<int32_t> scratch_deltas;  // distinct nonzero offsets of the current call
   std::vector<int32_t> scratch_release;  // pages whose reference an append drops after it allocated
@@ -412,11 +423,12 @@ void write_seq_tables(const segkv_ctx *c, int32_t layer, int32_t n_seqs, const i
 }
 
 // A prefill call's device tables, in upload order: sequence tables, work
-// items, combine items, then the work-queue counter (16 bytes, zero).
+// items, combine items, the work-queue counter (16 bytes, zero), then the
+// per-workgroup item ranges of the two-group kernel.
 struct PrefillPlan {
   SeqTables tl;
-  size_t tbytes = 0, ibytes = 0, cbytes = 0, bytes = 0;
-  int32_t n_items = 0, n_parts = 0;
+  size_t tbytes = 0, ibytes = 0, cbytes = 0, wbytes = 0, bytes = 0;
+  int32_t n_items = 0, n_parts = 0, n_wgs = 0;
 };
 
 // Plans a prefill of the queries cu_q over the current state: the work list
@@ -522,15 +534,33 @@ void build_prefill_plan(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32
   } else {
     lpt_sort(items);
   }
+  const int32_t n_wgs = static_cast<int32_t>(std::min<int64_t>(
+      static_cast<int64_t>(items.size()), std::max<int64_t>(1, static_cast<int64_t>(c->num_cus) * kPrefillWgPerCu)));
+  std::vector<int32_t> &wg_off = c->scratch_wg;
+  wg_off.assign(static_cast<size_t>(n_wgs) + 1, 0);
+  if (c->prefill_kernel == kPrefillTwoGroup && n_wgs > 0) {
+    // The two-group kernel runs a fixed list per workgroup: longest first,
+    // each item to the least loaded workgroup (cost = tiles plus a constant
+    // for the item's start and output).
+    std::vector<int64_t> &cost = c->scratch_cost;
+    cost.resize(items.size());
+    for (size_t i = 0; i < items.size(); ++i) cost[i] = (items[i].tile_end - items[i].tile_begin) + kItemCostTiles;
+    balance_items(cost, n_wgs, &c->scratch_owner, &wg_off, &c->scratch_order);
+    std::vector<PrefillItem> grouped(items.size());
+    for (size_t j = 0; j < items.size(); ++j) grouped[j] = items[static_cast<size_t>(c->scratch_order[j])];
+    items.swap(grouped);
+  }
 
   const SeqTables tl = seq_tables_layout(c, layer, n_seqs, seq_ids);
   pp->tl = tl;
   pp->tbytes = align_up(tl.bytes, 16);
   pp->ibytes = align_up(sizeof(PrefillItem) * items.size(), 16);
   pp->cbytes = align_up(sizeof(CombineItem) * citems.size(), 16);
-  pp->bytes = pp->tbytes + pp->ibytes + pp->cbytes + 16;
+  pp->wbytes = align_up(sizeof(int32_t) * wg_off.size(), 16);
+  pp->bytes = pp->tbytes + pp->ibytes + pp->cbytes + 16 + pp->wbytes;
   pp->n_items = static_cast<int32_t>(items.size());
   pp->n_parts = n_parts;
+  pp->n_wgs = n_wgs;
   out->assign(pp->bytes, 0);
   std::vector<int32_t> qs(n_seqs), ql(n_seqs);
   for (int32_t b = 0; b < n_seqs; ++b) {
@@ -541,6 +571,7 @@ void build_prefill_plan(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32
   std::memcpy(out->data() + pp->tbytes, items.data(), sizeof(PrefillItem) * items.size());
   if (!citems.empty())
     std::memcpy(out->data() + pp->tbytes + pp->ibytes, citems.data(), sizeof(CombineItem) * citems.size());
+  std::memcpy(out->data() + pp->tbytes + pp->ibytes + pp->cbytes + 16, wg_off.data(), sizeof(int32_t) * wg_off.size());
 }
 
 RopeArgs rope_args(const segkv_ctx *c, const SeqTables &t, const char *tables) {
@@ -586,7 +617,8 @@ WsBound workspace_bound(const segkv_config *cfg, int64_t Q, int64_t slots) {
   const int64_t base_items = Hkv * nq_tiles;
   const int64_t p_parts = 2 * slots;
   const size_t p_tables = align_up(seq_tables, 16) + align_up(sizeof(PrefillItem) * (base_items + p_parts), 16) +
-                          align_up(sizeof(CombineItem) * std::min(base_items, slots), 16) + 16;
+                          align_up(sizeof(CombineItem) * std::min(base_items, slots), 16) + 16 +
+                          align_up(sizeof(int32_t) * static_cast<size_t>(slots + 1), 16);
   const size_t p_part = static_cast<size_t>(p_parts) * kPrefillRows * (D + 1) * sizeof(float);
   // decode
   const int64_t pieces = nseg + slots;
@@ -1163,13 +1195,14 @@ int segkv_prefill(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *se
   a.scale_log2 = c->scale * 1.4426950408889634f;
   a.n_items = pp.n_items;
   a.counter = reinterpret_cast<int32_t *>(c->ws + tbytes + ibytes + cbytes);
-  const int64_t n_wgs = std::min<int64_t>(static_cast<int64_t>(pp.n_items),
-                                          std::max<int64_t>(1, static_cast<int64_t>(c->num_cus) * kPrefillWgPerCu));
+  a.wg_items = reinterpret_cast<const int32_t *>(c->ws + tbytes + ibytes + cbytes + 16);
+  const int n_wgs = pp.n_wgs;
   TimedLaunch t{};
   rc = timed_begin(c, &t, SEGKV_KERNEL_PREFILL);
   if (rc) return rc;
-  hipError_t e = c->prefill_kernel == 2 ? launch_prefill_wide(a, static_cast<int>(n_wgs), c->D, c->P, c->stream)
-                                        : launch_prefill(a, static_cast<int>(n_wgs), c->D, c->P, c->stream);
+  hipError_t e = c->prefill_kernel == kPrefillTwoGroup ? launch_prefill_pp(a, n_wgs, c->D, c->P, c->stream)
+                 : c->prefill_kernel == kPrefillWide   ? launch_prefill_wide(a, n_wgs, c->D, c->P, c->stream)
+                                                       : launch_prefill(a, n_wgs, c->D, c->P, c->stream);
   if (e != hipSuccess) return c->device_fail(e, "prefill launch");
   rc = timed_end(c, &t);
   if (rc) return rc;
@@ -1660,7 +1693,8 @@ int segkv_set_tuning(segkv_ctx *c, int32_t knob, int64_t value) {
       c->prefill_order = value > 0 ? static_cast<int32_t>(value) : 0;
       return SEGKV_OK;
     case SEGKV_TUNE_PREFILL_KERNEL:
-      if (value > 2) return c->fail(SEGKV_E_INVAL, "prefill kernel must be 0 (default), 1 (8 x 32 rows) or 2 (4 x 64 rows)");
+      if (value > kPrefillTwoGroup)
+        return c->fail(SEGKV_E_INVAL, "prefill kernel must be 0 (default), 1 (8 x 32 rows), 2 (4 x 64 rows) or 3 (two groups)");
       c->prefill_kernel = value > 0 ? static_cast<int32_t>(value) : 0;
       return SEGKV_OK;
     default:

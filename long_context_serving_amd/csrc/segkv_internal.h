@@ -159,6 +159,7 @@ struct PrefillArgs {
   RopeArgs rope;
   int32_t n_items;        // work items; workgroups take them in list order from *counter
   int32_t *counter;       // zero at launch (part of the uploaded tables)
+  const int32_t *wg_items;  // two-group kernel: workgroup w runs items [wg_items[w], wg_items[w + 1])
 };
 
 struct DecodeArgs {
@@ -252,9 +253,10 @@ struct MergeArgs {
   int64_t n_pairs;  // rows * query heads
 };
 
-// Launchers (kernels.hip).  Return the launch status.
+// Launchers (csrc/*.hip, one file per kernel family).  Return the launch status.
 hipError_t launch_scatter(const ScatterArgs &a, int n_items, int head_dim, int page_size, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs &a, int n_items, int head_dim, int page_size, hipStream_t s);
+hipError_t launch_prefill_pp(const PrefillArgs &a, int n_wgs, int head_dim, int page_size, hipStream_t s);
 hipError_t launch_prefill_wide(const PrefillArgs &a, int n_items, int head_dim, int page_size, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int n_wgs, int head_dim, int page_size, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, int n_items, int max_entries, int head_dim, hipStream_t s);
@@ -265,7 +267,7 @@ hipError_t launch_topk(const TopkArgs &a, int n_seqs, hipStream_t s);
 // bytes are rounded up to 16; both buffers must hold the rounded size
 hipError_t launch_upload(void *dst, const void *src_pinned, size_t bytes, hipStream_t s);
 
-// The fixed device scratch of segkv_decode_noalloc (kernels.hip): its size,
+// The fixed device scratch of segkv_decode_noalloc (decode.hip): its size,
 // and its address on the current device (resolved once per device).
 constexpr size_t kStaticScratchBytes = size_t(8) << 20;
 hipError_t scratch_address(void **out);

@@ -34,19 +34,28 @@ def test_traffic_reported_only_for_the_measured_source(tmp_path, monkeypatch):
     f = tmp_path / "traffic.json"
     f.write_text(json.dumps({"prefill_x": {"bytes_per_launch": 1234, "kernel_source_sha256_16": "aaaa"}}))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
-    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "aaaa")
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda kind: "aaaa")
     assert bench.measured_traffic("prefill_x") == 1234
     assert bench.measured_traffic("decode_y") is None
-    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "bbbb")
+    monkeypatch.setattr(bench, "PREFILL_KERNEL", 3)  # a variant other than the measured default
+    assert bench.measured_traffic("prefill_x") is None
+    monkeypatch.setattr(bench, "PREFILL_KERNEL", 0)
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda kind: "bbbb")
     assert bench.measured_traffic("prefill_x") is None
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.json"))
-    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "aaaa")
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda kind: "aaaa")
     assert bench.measured_traffic("prefill_x") is None
 
 
-def test_kernel_source_hash_is_the_kernel_file_digest():
+def test_kernel_source_hash_is_the_kernel_files_digest():
     import hashlib
     bench = load_bench()
-    with open(os.path.join(ROOT, "long_context_serving_amd", "csrc", "kernels.hip"), "rb") as fh:
-        want = hashlib.sha256(fh.read()).hexdigest()[:16]
-    assert bench.kernel_source_hash() == want
+    csrc = os.path.join(ROOT, "long_context_serving_amd", "csrc")
+    for kind, files in (("prefill", ["prefill.hip", "kernels_common.h", "segkv_internal.h"]),
+                        ("decode", ["decode.hip", "kernels_common.h", "segkv_internal.h"])):
+        h = hashlib.sha256()
+        for name in files:
+            with open(os.path.join(csrc, name), "rb") as fh:
+                h.update(fh.read())
+        assert bench.kernel_source_hash(kind) == h.hexdigest()[:16]
+    assert bench.kernel_source_hash("prefill") != bench.kernel_source_hash("decode")

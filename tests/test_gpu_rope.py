@@ -12,7 +12,7 @@ from long_context_serving_amd import workloads as wl
 from oracle import attention as A
 from oracle import rope as RP
 
-from gpu_helpers import compare, gpu_run, say
+from gpu_helpers import PREFILL_KERNEL, compare, gpu_run, say
 
 pytestmark = pytest.mark.gpu
 
