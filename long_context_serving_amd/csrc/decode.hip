@@ -2,6 +2,7 @@
 // fixed device scratch of the decode entry point that allocates nothing.
 
 #include "kernels_common.h"
+#include "segkv_launch.h"
 
 #include <mutex>
 

@@ -1,6 +1,7 @@
 // HIP kernel of libsegkv: the head-decomposition merge.
 
 #include "kernels_common.h"
+#include "segkv_launch.h"
 
 namespace segkv {
 namespace {

@@ -1,6 +1,7 @@
 // HIP kernel of libsegkv: varlen prefill attention (8 waves x 32 rows, the default).
 
 #include "kernels_common.h"
+#include "segkv_launch.h"
 
 namespace segkv {
 namespace {

@@ -1,7 +1,8 @@
-// HIP kernels of libsegkv: the two prefill variants beside the default kernel
-// (two groups one phase apart; four waves of 64 rows).
+// HIP kernels of libsegkv: the prefill variants beside the default kernel
+// (two groups one phase apart; four waves of 64 rows; software pipelined).
 
 #include "kernels_common.h"
+#include "segkv_launch.h"
 
 namespace segkv {
 namespace {
@@ -942,7 +943,416 @@ __global__ __launch_bounds__(kPrefillWideThreads, 1) void prefill_wide_kernel(Pr
   }
 }
 
+// ===========================================================================
+// Prefill, software pipelined (SEGKV_TUNE_PREFILL_KERNEL = 4).  The same
+// work items, queue, tile loads and output as prefill_kernel, with the tile
+// loop of each item reordered so that every wave has independent vector
+// work to issue while its own products run:
+//
+//   step c:  S^T(c+1) = K(c+1) Q^T      beside   exp / row sum / pack of tile c
+//            O^T += V^T(c) P^T(c)        beside   mask / max of tile c+1
+//            rescale for tile c+1 (when its max moved), then the tile barrier
+//
+// (the first tile's product is issued before the item's first step, the
+// last step has no next tile).  A step reads K of tile c+1 and V^T of tile
+// c, so the LDS ring has four stages and the barrier that ends step c waits
+// for tile c+2; tile c+4 starts loading right after it, into the stage tile
+// c used.  The products and the vector work of a step sit in one basic
+// block, and scheduling group barriers ask the compiler to alternate them.
+// ===========================================================================
+template <int D, int P>
+__global__ __launch_bounds__(kPrefillThreads, 2) void prefill_sp_kernel(PrefillArgs a) {
+  using L = PrefillLds<D>;
+  constexpr int NKK = D / 16;  // k-steps of the QK product
+  constexpr int NDB = D / 32;  // 32-channel blocks of O^T
+  constexpr int NW = kPrefillThreads / 64;
+  constexpr int K_INSTR = L::K_CHUNKS / kPrefillThreads;  // direct loads per lane per tile (K)
+  constexpr int V_INSTR = L::V_CHUNKS / kPrefillThreads;  // (V^T)
+  constexpr int NSTAGE = 4;
+  constexpr int LOADS_PER_TILE = K_INSTR + V_INSTR;
+  static_assert(kPrefillRows == 32 * NW, "one 32-row column block per wave");
+  static_assert(K_INSTR >= 1 && V_INSTR >= 1, "tile smaller than one load per lane");
+  static_assert(L::KCPR * 16 >= 128 && (L::KCPR * 16) % 128 == 0 && L::STAGE_BYTES % 256 == 0 &&
+                    (L::K_CHUNKS * 16) % 256 == 0, "row starts leave the chunk bits free");
+  __shared__ __attribute__((aligned(16))) uint4 smem4[NSTAGE * L::STAGE_BYTES / 16];
+  __shared__ int s_next[2];  // item indices fetched by thread 0; consecutive fetches alternate slots
+  __shared__ __attribute__((aligned(16))) float s_rope[NW][2 * D];  // per-wave relocation table
+  char *smem = reinterpret_cast<char *>(smem4);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int G = a.group;
+  const int rows = a.rows_per_tile;
+  const int n_items = a.n_items;
+  const int r = wave * 32 + col;  // this lane's row of the item
+  const int pos_off = r / G;
+
+  if (tid == 0) s_next[0] = atomicAdd(a.counter, 1);
+  __syncthreads();
+  int cur = __builtin_amdgcn_readfirstlane(s_next[0]);
+  if (cur >= n_items) return;
+  int nxt = -1;
+  int fslot = 1;
+
+  // ---- producer: global->LDS tile loads, across item boundaries ----------
+  int p_item = -1, p_tile = 0, p_end = 0;
+  SegDesc psg;
+  auto p_set = [&](int idx) {
+    const PrefillItem pi_ = sload(a.items + idx);
+    p_item = idx;
+    p_tile = pi_.tile_begin;
+    p_end = pi_.tile_end;
+    psg = sload(a.segs + pi_.seq * a.num_kv_heads + pi_.kv_head);
+  };
+  p_set(cur);
+  int issued = 0, consumed = 0;  // tiles issued / steps finished so far (the stream of the workgroup's tiles)
+  auto issue_tile = [&](int tile, int stage) {
+    const int k0 = tile * kTileKeys;
+    const int last_page = psg.n_pages - 1;
+    char *st = smem + stage * L::STAGE_BYTES;
+    constexpr int NP = kTileKeys / P;
+    int pid[NP];
+    const int pg0 = (k0 - psg.first_token) / P;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) pid[i] = sload(a.page_ids + psg.page_off + min(max(pg0 + i, 0), last_page));
+    auto page_of = [&](int key_in_tile, int *slot) {
+      const int rel = k0 + key_in_tile - psg.first_token;
+      *slot = rel >= 0 && rel / P <= last_page ? key_in_tile % P : 0;
+      int page = pid[0];
+#pragma unroll
+      for (int i = 1; i < NP; ++i)
+        if (key_in_tile / P == i) page = pid[i];
+      return page;
+    };
+#pragma unroll
+    for (int j = 0; j < K_INSTR; ++j) {
+      const int c = (j * NW + wave) * 64 + lane;
+      const int row = c / L::KCPR;
+      const int logical = (c % L::KCPR) ^ L::k_swz(row);
+      if constexpr (P == kTileKeys) {
+        lds_dma16_s(a.k_pool + static_cast<size_t>(pid[0]) * (P * D), static_cast<uint32_t>((row * D + logical * 8) * 2),
+                    st + (j * NW + wave) * 1024);
+      } else {
+        int slot;
+        const int page = page_of(row, &slot);
+        lds_dma16(a.k_pool + (static_cast<size_t>(page) * P + slot) * D + logical * 8, st + (j * NW + wave) * 1024);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < V_INSTR; ++j) {
+      const int c = (j * NW + wave) * 64 + lane;
+      const int d = c / 8;
+      const int logical = (c % 8) ^ L::v_swz(d);
+      if constexpr (P == kTileKeys) {
+        lds_dma16_s(a.v_pool + static_cast<size_t>(pid[0]) * (P * D), static_cast<uint32_t>((d * P + logical * 8) * 2),
+                    st + L::K_CHUNKS * 16 + (j * NW + wave) * 1024);
+      } else {
+        int slot;
+        const int page = page_of(logical * 8, &slot);
+        lds_dma16(a.v_pool + static_cast<size_t>(page) * (P * D) + d * P + slot,
+                  st + L::K_CHUNKS * 16 + (j * NW + wave) * 1024);
+      }
+    }
+  };
+  auto produce = [&](int limit) {
+    while (issued < limit && p_item >= 0) {
+      issue_tile(p_tile, issued % NSTAGE);
+      ++issued;
+      if (++p_tile >= p_end) {
+        if (p_item == cur && nxt >= 0 && nxt < n_items)
+          p_set(nxt);
+        else
+          p_item = -1;  // resumes once the consumer knows the item after this one
+      }
+    }
+  };
+  // Workgroup barrier that leaves the newest `pending` issued tiles' loads
+  // in flight (this wave's LDS operations and older tile loads complete
+  // first).
+  auto sync_tiles = [&](int pending) {
+    if (pending >= 2)
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * LOADS_PER_TILE) : "memory");
+    else if (pending == 1)
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LOADS_PER_TILE) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  // Make tiles [0, need) of the stream resident: issue what is missing and
+  // wait, leaving later tiles in flight.  `ready` counts the tiles known
+  // resident (all waves take the same decisions: the counts are uniform).
+  int ready = 0;
+  auto ensure = [&](int need) {
+    if (issued < need) produce(need);
+    sync_tiles(issued - need);
+    ready = min(need, issued);
+  };
+
+  produce(3);
+  ensure(2);
+
+  // LDS byte offsets of this lane's operand chunks within a stage: chunk
+  // 2 j + half of the lane's row sits at lane_off ^ (j << 5).
+  const int key_a0 = st_row_key(col);  // K row this lane feeds to block 0 (block 1: +32)
+  const int k_lane = key_a0 * L::KCPR * 16 + ((half ^ L::k_swz(key_a0)) << 4);
+  const int v_lane = L::K_CHUNKS * 16 + col * 128 + ((half ^ L::v_swz(col)) << 4);
+
+  while (true) {
+    const PrefillItem it = sload(a.items + cur);
+    const SeqDesc sd = sload(a.seqs + it.seq);
+    const SegDesc sg = sload(a.segs + it.seq * a.num_kv_heads + it.kv_head);
+    const int h = it.kv_head * G + (r - pos_off * G);
+    const int t0 = it.qtile * rows;
+    const int t_last = min(t0 + rows, sd.q_len) - 1;
+    const int t = t0 + pos_off;
+    const bool valid = pos_off < rows && t < sd.q_len;
+    const int base = sd.kv_len - sd.q_len;
+    const int p = base + min(t, t_last);
+    const int W = sg.window;
+    const int vis_lo = W > 0 ? p - W + 1 : 0;
+    const int p_wmin = __builtin_amdgcn_readfirstlane(base + min(t0 + (wave * 32) / G, t_last));
+    const int p_wmax = __builtin_amdgcn_readfirstlane(base + min(t0 + (wave * 32 + 31) / G, t_last));
+
+    bf16x8 qv[NKK];
+    {
+      const uint16_t *qrow = a.q + (static_cast<size_t>(sd.q_start + min(t, t_last)) * a.num_q_heads + h) * D;
+      if (sg.rope_off < 0) {
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) qv[kk] = as_bf16x8(ld16(qrow + kk * 16 + half * 8));
+      } else {
+        relocate_row<D, NKK>(qv, qrow, 16, half * 8, valid, a.rope.tables + sg.rope_off, s_rope[wave], a.rope);
+      }
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+v"(qv[kk]));
+    }
+
+    f32x16 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+    float m = kNegInf;  // running (lazy) max of raw scores of this column
+    float msc = 0.f;    // m * scale_log2 (0 while m is -inf)
+    float l = 0.f;      // this lane's share of the running sum
+
+    // per-wave tile class: 0 empty, 1 edge (per-key mask), 2 full
+    auto tile_class = [&](int tile) {
+      const int k0 = tile * kTileKeys;
+      const bool empty = k0 > p_wmax || (W > 0 && k0 + kTileKeys - 1 < p_wmin - W + 1);
+      const bool full = k0 + kTileKeys - 1 <= p_wmin && (W == 0 || k0 >= p_wmax - W + 1);
+      return empty ? 0 : (full ? 2 : 1);
+    };
+    // QK product of one tile into (s0, s1); K operand reads run four
+    // products ahead.
+    auto qk = [&](int st_off, f32x16 &s0, f32x16 &s1) {
+      s0 = f32x16{};
+      s1 = f32x16{};
+      constexpr int N = 2 * NKK;
+      constexpr int LA = 4;
+      const int kb = st_off + k_lane;
+      bf16x8 kr[LA];
+      auto kread = [&](int i) {
+        kr[i % LA] = as_bf16x8(*reinterpret_cast<const u32x4 *>(smem + (kb ^ ((i >> 1) << 5)) + (i & 1) * 32 * L::KCPR * 16));
+      };
+#pragma unroll
+      for (int i = 0; i < LA; ++i) kread(i);
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        if (i & 1)
+          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[i % LA], qv[i >> 1], s1, 0, 0, 0);
+        else
+          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[i % LA], qv[i >> 1], s0, 0, 0, 0);
+        if (i + LA < N) kread(i + LA);
+      }
+    };
+    // PV product of one tile from pb; V^T operand reads run four products ahead.
+    auto pv = [&](int st_off, const bf16x8 (&pb)[4]) {
+      constexpr int N = 4 * NDB;
+      constexpr int LA = 4;
+      const int vb = st_off + v_lane;
+      bf16x8 va[LA];
+      auto vread = [&](int i) {
+        va[i % LA] = as_bf16x8(*reinterpret_cast<const u32x4 *>(smem + (vb ^ ((i / NDB) << 5)) + (i % NDB) * 32 * 128));
+      };
+#pragma unroll
+      for (int i = 0; i < LA; ++i) vread(i);
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        oacc[i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % LA], pb[i / NDB], oacc[i % NDB], 0, 0, 0);
+        if (i + LA < N) vread(i + LA);
+      }
+    };
+    auto mask = [&](f32x16 &s0, f32x16 &s1, int k0) {
+      const unsigned lo_rel = static_cast<unsigned>(vis_lo - k0 - 8 * half);
+      const unsigned span = static_cast<unsigned>(p - vis_lo);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int off = ((v >> 3) << 4) + (v & 7);
+        if (static_cast<unsigned>(off) - lo_rel > span) s0[v] = kNegInf;
+        if (static_cast<unsigned>(off + 32) - lo_rel > span) s1[v] = kNegInf;
+      }
+    };
+    // Row max of a tile (both lanes of a column).
+    auto tile_max = [&](const f32x16 &s0, const f32x16 &s1) {
+      float mx = max32(s0, s1);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    };
+    // Lazy running max: move it (and rescale O and l) only when the tile's
+    // max exceeds it by more than 2^kRescaleLog2.
+    auto update_max = [&](float mx) {
+      const bool bump = mx * a.scale_log2 > m * a.scale_log2 + kRescaleLog2;
+      const float m_new = bump ? mx : m;
+      const float msc_new = m_new == kNegInf ? 0.f : m_new * a.scale_log2;
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(bump) != 0, 0)) {
+        const float alpha = bump ? fast_exp2(m * a.scale_log2 - msc_new) : 1.f;
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      }
+      m = m_new;
+      msc = msc_new;
+    };
+    // exp, row sum and bf16 probabilities of a tile (scores in place).
+    auto probs = [&](f32x16 &s0, f32x16 &s1, bf16x8 (&pb)[4]) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        s0[v] = fast_exp2(fmaf(s0[v], a.scale_log2, -msc));
+        s1[v] = fast_exp2(fmaf(s1[v], a.scale_log2, -msc));
+      }
+      l += sum32(s0, s1);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const f32x16 &sv = kb ? s1 : s0;
+          pb[2 * kb + s] = pack8_bf16(sv[8 * s + 0], sv[8 * s + 1], sv[8 * s + 2], sv[8 * s + 3], sv[8 * s + 4],
+                                      sv[8 * s + 5], sv[8 * s + 6], sv[8 * s + 7]);
+        }
+    };
+
+    const int fetch_tile = max(it.tile_begin, it.tile_end - 4);
+    // The item's first two tiles may have been issued only after the last
+    // wait (short items: the next item's index arrives late).
+    {
+      const int need = consumed + min(2, it.tile_end - it.tile_begin);
+      if (ready < need) ensure(need);
+    }
+    // Scores of the tile the next step takes.  Tiles a wave's rows cannot see
+    // at all are computed like edge tiles (every score masked to -inf, so
+    // they add nothing): the step stays one block of code.
+    f32x16 sc0, sc1;
+    {
+      qk((consumed % NSTAGE) * L::STAGE_BYTES, sc0, sc1);
+      if (tile_class(it.tile_begin) != 2) mask(sc0, sc1, it.tile_begin * kTileKeys);
+      update_max(tile_max(sc0, sc1));
+    }
+    // After a step: wait for tile c + 2 of the stream (the next step reads
+    // tile c + 1's V^T and tile c + 2's K), then refill the freed stage.
+    auto end_step = [&](int tile) {
+      ensure(consumed + 3);
+      ++consumed;
+      if (tile == fetch_tile) {
+        nxt = __builtin_amdgcn_readfirstlane(s_next[fslot]);
+        fslot ^= 1;
+        if (p_item < 0 && nxt < n_items) p_set(nxt);
+      }
+      produce(consumed + NSTAGE);
+      // a step may read the item's next tile only once it is resident
+      if (tile + 2 < it.tile_end && ready < consumed + 2) ensure(consumed + 2);
+    };
+    for (int tile = it.tile_begin; tile + 1 < it.tile_end; ++tile) {
+      if (tile == fetch_tile && tid == 0) s_next[fslot] = atomicAdd(a.counter, 1);
+      const int st_c = (consumed % NSTAGE) * L::STAGE_BYTES;
+      const int st_n = ((consumed + 1) % NSTAGE) * L::STAGE_BYTES;
+      f32x16 sn0, sn1;
+      bf16x8 pb[4];
+      qk(st_n, sn0, sn1);
+      probs(sc0, sc1, pb);
+#pragma unroll
+      for (int i = 0; i < 2 * NKK; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
+      }
+      pv(st_c, pb);
+      if (tile_class(tile + 1) != 2) mask(sn0, sn1, (tile + 1) * kTileKeys);
+      const float mx = tile_max(sn0, sn1);
+#pragma unroll
+      for (int i = 0; i < 4 * NDB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 1);
+      }
+      update_max(mx);
+      sc0 = sn0;
+      sc1 = sn1;
+      end_step(tile);
+    }
+    {
+      const int tile = it.tile_end - 1;
+      if (tile == fetch_tile && tid == 0) s_next[fslot] = atomicAdd(a.counter, 1);
+      bf16x8 pb[4];
+      probs(sc0, sc1, pb);
+      pv((consumed % NSTAGE) * L::STAGE_BYTES, pb);
+      end_step(tile);
+    }
+
+    const float l_tot = l + __shfl_xor(l, 32);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float lse_val = l_tot > 0.f ? m * a.scale + logf(l_tot) : kNegInf;
+    if (it.part < 0) {
+      u32x4 w[NDB][2];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int ip = 0; ip < 2; ++ip) {
+          const f32x16 &ac = oacc[db];
+          const u32x2 p0 = pack4_bf16(ac[8 * ip] * inv, ac[8 * ip + 1] * inv, ac[8 * ip + 2] * inv, ac[8 * ip + 3] * inv);
+          const u32x2 p1 =
+              pack4_bf16(ac[8 * ip + 4] * inv, ac[8 * ip + 5] * inv, ac[8 * ip + 6] * inv, ac[8 * ip + 7] * inv);
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(p0[k], p1[k], false, false);
+            w[db][ip][k] = sw[0];
+            w[db][ip][2 + k] = sw[1];
+          }
+        }
+      }
+      if (valid) {
+        uint16_t *orow = a.o + (static_cast<size_t>(sd.q_start + t) * a.num_q_heads + h) * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int ip = 0; ip < 2; ++ip) *reinterpret_cast<u32x4 *>(orow + db * 32 + ip * 16 + half * 8) = w[db][ip];
+        if (half == 0 && a.lse) a.lse[static_cast<size_t>(sd.q_start + t) * a.num_q_heads + h] = lse_val;
+      }
+    } else {
+      float *prow = a.part_o + (static_cast<size_t>(it.part) * kPrefillRows + r) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d0 = db * 32 + i * 8 + half * 4;
+          f32x4 x = {oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv, oacc[db][4 * i + 2] * inv,
+                     oacc[db][4 * i + 3] * inv};
+          *reinterpret_cast<f32x4 *>(prow + d0) = x;
+        }
+      }
+      if (half == 0) a.part_lse[static_cast<size_t>(it.part) * kPrefillRows + r] = lse_val;
+    }
+
+    if (nxt >= n_items) break;
+    cur = nxt;
+    nxt = -1;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_prefill_sp(const PrefillArgs &a, int n_wgs, int head_dim, int page_size, hipStream_t s) {
+  if (n_wgs <= 0) return hipSuccess;
+  SEGKV_DISPATCH_DP(prefill_sp_kernel, head_dim, page_size, dim3(n_wgs), dim3(kPrefillThreads), s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_prefill_pp(const PrefillArgs &a, int n_wgs, int head_dim, int page_size, hipStream_t s) {
   if (n_wgs <= 0) return hipSuccess;

@@ -1,6 +1,7 @@
 // HIP kernels of libsegkv: KV append scatter and the per-call table upload.
 
 #include "kernels_common.h"
+#include "segkv_launch.h"
 
 namespace segkv {
 namespace {

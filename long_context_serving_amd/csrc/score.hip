@@ -1,6 +1,7 @@
 // HIP kernels of libsegkv: attention-mass token scores and their top-k.
 
 #include "kernels_common.h"
+#include "segkv_launch.h"
 
 namespace segkv {
 namespace {

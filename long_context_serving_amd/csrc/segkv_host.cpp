@@ -24,6 +24,7 @@
 
 #include "segkv.h"
 #include "segkv_internal.h"
+#include "segkv_launch.h"
 #include "segkv_sched.h"
 
 using namespace segkv;
@@ -44,6 +45,7 @@ constexpr int64_t kItemCostTiles = 2;
 // SEGKV_TUNE_PREFILL_KERNEL values of the two variants beside the default kernel
 constexpr int32_t kPrefillWide = 2;
 constexpr int32_t kPrefillTwoGroup = 3;
+constexpr int32_t kPrefillPipelined = 4;
 
 struct Segment {
   int32_t first_token = 0;
@@ -1200,7 +1202,8 @@ int segkv_prefill(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *se
   TimedLaunch t{};
   rc = timed_begin(c, &t, SEGKV_KERNEL_PREFILL);
   if (rc) return rc;
-  hipError_t e = c->prefill_kernel == kPrefillTwoGroup ? launch_prefill_pp(a, n_wgs, c->D, c->P, c->stream)
+  hipError_t e = c->prefill_kernel == kPrefillPipelined ? launch_prefill_sp(a, n_wgs, c->D, c->P, c->stream)
+                 : c->prefill_kernel == kPrefillTwoGroup ? launch_prefill_pp(a, n_wgs, c->D, c->P, c->stream)
                  : c->prefill_kernel == kPrefillWide   ? launch_prefill_wide(a, n_wgs, c->D, c->P, c->stream)
                                                        : launch_prefill(a, n_wgs, c->D, c->P, c->stream);
   if (e != hipSuccess) return c->device_fail(e, "prefill launch");
@@ -1693,8 +1696,9 @@ int segkv_set_tuning(segkv_ctx *c, int32_t knob, int64_t value) {
       c->prefill_order = value > 0 ? static_cast<int32_t>(value) : 0;
       return SEGKV_OK;
     case SEGKV_TUNE_PREFILL_KERNEL:
-      if (value > kPrefillTwoGroup)
-        return c->fail(SEGKV_E_INVAL, "prefill kernel must be 0 (default), 1 (8 x 32 rows), 2 (4 x 64 rows) or 3 (two groups)");
+      if (value > kPrefillPipelined)
+        return c->fail(SEGKV_E_INVAL,
+                       "prefill kernel must be 0 (default), 1 (8 x 32 rows), 2 (4 x 64 rows), 3 (two groups) or 4 (pipelined)");
       c->prefill_kernel = value > 0 ? static_cast<int32_t>(value) : 0;
       return SEGKV_OK;
     default:
