@@ -14,215 +14,306 @@ namespace {
 // work: with the rows' final LSE known, key j receives sum over rows (t, h)
 // of exp(scale q.k_j - lse).  The product is taken as S = Q K^T (operands of
 // the prefill's S^T swapped), so a lane holds one key column and 16 query
-// rows and the sum over queries is in-lane plus one lane-pair swap.  The 8
-// waves' per-tile key sums meet in a double-buffered LDS exchange that rides
-// on the K pipeline's per-tile barrier; one wave writes the tile's 64 sums
-// as a partial row.  Partial rows are added by score_reduce_kernel in a
-// fixed order, so the scores do not depend on the work order.
+// rows per 32-row block and the sum over queries is in-lane plus one
+// lane-pair swap.  A workgroup covers the prefill's 256 rows with 4 waves
+// of 64 rows (two blocks, so each K operand read from LDS feeds two
+// products), and two workgroups share a CU.  The waves' per-tile key sums
+// meet in a double-buffered LDS exchange that rides on the K pipeline's
+// per-tile barrier; one wave writes the tile's 64 sums as a partial row.
+// Partial rows are added by score_reduce_kernel in a fixed order, so the
+// scores do not depend on the work order.  The grid is persistent (one
+// workgroup per resident slot) and takes the pieces from a queue.
 // ===========================================================================
 
+constexpr int kScoreThreads = 256;  // 4 waves of 64 rows: two workgroups per CU
+
 template <int D, int P>
-__global__ __launch_bounds__(kPrefillThreads, 2) void score_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreArgs a) {
   using L = PrefillLds<D>;
   constexpr int NKK = D / 16;
-  constexpr int NW = kPrefillThreads / 64;
-  constexpr int K_INSTR = L::K_CHUNKS / kPrefillThreads;
-  constexpr int NSTAGE = 3;
+  constexpr int NW = kScoreThreads / 64;
+  constexpr int RB = 2;  // 32-row blocks per wave: each K operand read feeds RB products
+  constexpr int K_INSTR = L::K_CHUNKS / kScoreThreads;
+  constexpr int NSTAGE = 4;  // K tiles in LDS: the one read and NSTAGE - 1 in flight
+  constexpr int AHEAD = NSTAGE - 1;
   constexpr int KSTAGE = L::K_CHUNKS * 16;  // bytes of one K tile
   constexpr float kLog2e = 1.4426950408889634f;
-  static_assert(kPrefillRows == 32 * NW && K_INSTR >= 1, "tile layout");
+  static_assert(kPrefillRows == 32 * RB * NW && K_INSTR >= 1 && L::K_CHUNKS % kScoreThreads == 0, "tile layout");
   __shared__ __attribute__((aligned(16))) uint4 smem4[NSTAGE * KSTAGE / 16];
   __shared__ float sx[2][NW][kTileKeys];
   __shared__ __attribute__((aligned(16))) float s_rope[NW][2 * D];  // per-wave relocation table
   char *smem = reinterpret_cast<char *>(smem4);
 
-  const PrefillItem it = sload(a.items + blockIdx.x);
-  const SeqDesc sd = sload(a.seqs + it.seq);
-  const SegDesc sg = sload(a.segs + it.seq * a.num_kv_heads + it.kv_head);
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 31, half = lane >> 5;
   const int G = a.group;
   const int rows = a.rows_per_tile;
-  const int t0 = it.qtile * rows;
-  const int t_last = min(t0 + rows, sd.q_len) - 1;
-  const int base = sd.kv_len - sd.q_len;
-  const int W = sg.window;
-  const int p_wmin = base + min(t0 + (wave * 32) / G, t_last);
-  const int p_wmax = base + min(t0 + (wave * 32 + 31) / G, t_last);
+  // Work queue: workgroup w starts with item w, and each item fetches the
+  // index of this workgroup's next one (thread 0's atomic, issued at the
+  // item's start and handed over through LDS at its end, alternating two
+  // slots so that a slot is rewritten only after a later barrier).  Between
+  // two items the barrier ending an item and the one after the next item's
+  // first loads keep the K stages and the sum exchange apart.
+  __shared__ int s_next[2];
+  int ii = blockIdx.x;
+  for (int slot = 0; ii < a.n_items; slot ^= 1) {
+    // The thread index passes an empty asm statement per item, so values
+    // derived from it are rebuilt per item rather than held in registers
+    // across items.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 31, half = lane >> 5;
+    const PrefillItem it = sload(a.items + ii);
+    int nxt = 0;
+    if (tid == 0) nxt = atomicAdd(a.counter, 1);
+    const SeqDesc sd = sload(a.seqs + it.seq);
+    const SegDesc sg = sload(a.segs + it.seq * a.num_kv_heads + it.kv_head);
+    const int t0 = it.qtile * rows;
+    const int t_last = min(t0 + rows, sd.q_len) - 1;
+    const int base = sd.kv_len - sd.q_len;
+    const int W = sg.window;
+    const int p_wmin = base + min(t0 + (wave * 64) / G, t_last);
+    const int p_wmax = base + min(t0 + (wave * 64 + 63) / G, t_last);
 
-  // Q operand (A of S = Q K^T): this lane supplies query row wave*32 + col.
-  bf16x8 qv[NKK];
-  {
-    const int r = wave * 32 + col;
-    const int po = r / G;
-    const int h = it.kv_head * G + (r - po * G);
-    const int t = t0 + po;
-    const bool valid = po < rows && t < sd.q_len;
-    // Loads are unconditional (an invalid row reads the tile's last valid
-    // row and is zeroed afterwards), so they are in flight together.
-    const uint16_t *qrow = a.q + (static_cast<size_t>(sd.q_start + min(t, t_last)) * a.num_q_heads + h) * D;
-    if (sg.rope_off < 0) {
+    // Q operands (A of S = Q K^T): in block b this lane supplies query row
+    // 64 wave + 32 b + col.  Loads are unconditional (an invalid row reads the
+    // tile's last valid row and is zeroed afterwards), so they are in flight
+    // together.
+    bf16x8 qv[RB][NKK];
+    float lse_own[RB];
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      const int r = wave * 64 + 32 * b + col;
+      const int po = r / G;
+      const int h = it.kv_head * G + (r - po * G);
+      const int t = t0 + po;
+      const bool valid = po < rows && t < sd.q_len;
+      const size_t qi = static_cast<size_t>(sd.q_start + min(t, t_last)) * a.num_q_heads + h;
+      if (sg.rope_off < 0) {
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          const u32x4 x = ld16(a.q + qi * D + kk * 16 + half * 8);
+          qv[b][kk] = as_bf16x8(valid ? x : z);
+        }
+      } else {
+        relocate_row<D, NKK>(qv[b], a.q + qi * D, 16, half * 8, valid, a.rope.tables + sg.rope_off, s_rope[wave],
+                             a.rope);
+      }
+      // Rows past the chunk get lse = +inf, hence probability 0.
+      lse_own[b] = valid ? a.lse[qi] * kLog2e : __builtin_inff();
+    }
+    // The rows of S this lane holds: in block b, register v is row
+    // n = 64 wave + 32 b + 8 (v/4) + 4 half + v%4 of the workgroup; its LSE
+    // comes from the lane that loaded it.  Its query position minus t0,
+    // min(n / G, t_last - t0) (below rows <= 256), is kept as byte v%4 of
+    // pos4[b][v/4].  n / G is taken in fp32: with n < 256 and G <= 256,
+    // (n + 1/2) / G lies at least 1/(2G) from an integer, far above the
+    // rounding error, so truncation gives the integer quotient.
+    float lse2[RB][16];
+    uint32_t pos4[RB][4];
+    {
+      const float rg = 1.f / static_cast<float>(G);
+      const int rel_max = t_last - t0;
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+        const float nb = static_cast<float>(wave * 64 + 32 * b + 4 * half) + 0.5f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) pos4[b][q] = 0u;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int rw = 8 * (v >> 2) + 4 * half + (v & 3);
+          lse2[b][v] = __shfl(lse_own[b], rw);
+          const int quo = static_cast<int>((nb + static_cast<float>(8 * (v >> 2) + (v & 3))) * rg);
+          pos4[b][v >> 2] |= static_cast<uint32_t>(min(quo, rel_max)) << (8 * (v & 3));
+        }
+      }
+    }
+    // Wait for Q and the LSE values once, here; inside the tile loop the
+    // compiler would otherwise wait for every outstanding load (the
+    // prefetched tiles included) before their first use in each tile.
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+v"(qv[b][kk]));
+#pragma unroll
+      for (int v = 0; v < 16; ++v) asm volatile("" : "+v"(lse2[b][v]));
+    }
+
+    const int last_page = sg.n_pages - 1;
+    auto issue_tile = [&](int tile, int stage) {
+      const int k0 = tile * kTileKeys;
+      char *st = smem + stage * KSTAGE;
+      // Page ids of the tile's NP whole pages by scalar loads (as in the
+      // prefill); keys outside the stored pages read slot 0 of the nearest.
+      constexpr int NP = kTileKeys / P;
+      int pid[NP];
+      const int pg0 = (k0 - sg.first_token) / P;
+#pragma unroll
+      for (int i = 0; i < NP; ++i) pid[i] = sload(a.page_ids + sg.page_off + min(max(pg0 + i, 0), last_page));
+#pragma unroll
+      for (int j = 0; j < K_INSTR; ++j) {
+        const int c = (j * NW + wave) * 64 + lane;
+        const int row = c / L::KCPR;
+        const int logical = (c % L::KCPR) ^ L::k_swz(row);
+        if constexpr (P == kTileKeys) {
+          // one page per tile: a scalar page base and a 32-bit lane offset
+          lds_dma16_s(a.k_pool + static_cast<size_t>(pid[0]) * (P * D), static_cast<uint32_t>((row * D + logical * 8) * 2),
+                      st + (j * NW + wave) * 1024);
+        } else {
+          const int rel = k0 + row - sg.first_token;
+          const int slot = rel >= 0 && rel / P <= last_page ? row % P : 0;
+          int page = pid[0];
+#pragma unroll
+          for (int i = 1; i < NP; ++i)
+            if (row / P == i) page = pid[i];
+          lds_dma16(a.k_pool + (static_cast<size_t>(page) * P + slot) * D + logical * 8, st + (j * NW + wave) * 1024);
+        }
+      }
+    };
+
+    const int kswz = L::k_swz(col);  // keys col and col + 32 share it
+    // Entry (row, key) is visible iff prow - W < key <= prow (W = 0: key <=
+    // prow): with d = prow - key taken as unsigned, iff d < wlim.
+    const uint32_t wlim = W > 0 ? static_cast<uint32_t>(W) : 0x80000000u;
+    // Masked scores become -inf, hence probability 0 whatever the row's LSE.
+    auto apply_mask = [&](f32x16 (&s)[RB], int key) {
+      const int krel = key - base - t0;  // prow - key = (position - t0) - krel
+      // (opaque here, so that the compiler keeps no per-entry differences
+      // live across the tile loop)
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) asm volatile("" : "+v"(pos4[b][q]));
+      }
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int rel = static_cast<int>(__builtin_amdgcn_ubfe(pos4[b][v >> 2], 8 * (v & 3), 8));
+          if (static_cast<uint32_t>(rel - krel) >= wlim) s[b][v] = kNegInf;
+        }
+      }
+    };
+    // Each wave keeps its matrix cores and its vector ALU busy together: a
+    // half step runs the RB x NKK products of one 32-key half of a tile (keys
+    // k0 + 32 hk + col, from the stage at st) into acc, each K operand read
+    // feeding RB of them, and between them the exponentials and the row sum
+    // of the scores prev of the half before it, which no product of this step
+    // reads.  Returns that half's key sums over this wave's 64 rows (both
+    // lanes of a pair end with the full sum).
+    constexpr int VPK = RB * 16 / NKK;  // entries of prev per K operand
+    constexpr int KAHEAD = 2;           // K operand reads in flight ahead of the products
+    auto half_step = [&](const char *st, int hk, f32x16 (&acc)[RB], const f32x16 (&prev)[RB]) -> float {
+      const char *kb = st + (col + 32 * hk) * L::KCPR * 16;
+      bf16x8 kr[NKK];
+      auto kread = [&](int kk) {
+        kr[kk] = as_bf16x8(*reinterpret_cast<const u32x4 *>(kb + ((2 * kk + half) ^ kswz) * 16));
+      };
+#pragma unroll
+      for (int kk = 0; kk < KAHEAD; ++kk) kread(kk);
+      f32x16 s[RB];
+#pragma unroll
+      for (int b = 0; b < RB; ++b) s[b] = f32x16{};
+      float e = 0.f;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        const u32x4 x = ld16(qrow + kk * 16 + half * 8);
-        qv[kk] = as_bf16x8(valid ? x : z);
+        // Empty asm statements pin the program order (the products of k-step
+        // kk, the next operand read, then entries of prev under the
+        // products); pure arithmetic would otherwise drift to its first use.
+        asm volatile("" : "+v"(kr[kk]));
+#pragma unroll
+        for (int b = 0; b < RB; ++b) s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qv[b][kk], kr[kk], s[b], 0, 0, 0);
+        if (kk + KAHEAD < NKK) kread(kk + KAHEAD);
+#pragma unroll
+        for (int j = 0; j < VPK; ++j) {
+          const int m = kk * VPK + j;  // entries in the order (block, register)
+          e += fast_exp2(fmaf(prev[m / 16][m % 16], a.scale_log2, -lse2[m / 16][m % 16]));
+        }
+        asm volatile("" : "+v"(e));
+        __builtin_amdgcn_sched_barrier(0);
       }
-    } else {
-      relocate_row<D, NKK>(qv, qrow, 16, half * 8, valid, a.rope.tables + sg.rope_off, s_rope[wave], a.rope);
-    }
-  }
-  // The rows of S this lane holds: register v is row 8 (v/4) + 4 half + v%4
-  // of the wave.  Rows past the chunk get lse = +inf, hence probability 0.
-  // Each lane loads the LSE of its own row (one coalesced load: an invalid
-  // row reads the tile's last valid row and gets +inf); lane v's rows are
-  // then taken from the lanes that loaded them.
-  float lse_own;
-  {
-    const int r = wave * 32 + col;
-    const int po = r / G;
-    const int t = t0 + po;
-    const bool valid = po < rows && t < sd.q_len;
-    const float raw = a.lse[static_cast<size_t>(sd.q_start + min(t, t_last)) * a.num_q_heads + it.kv_head * G +
-                            (r - po * G)];
-    lse_own = valid ? raw * kLog2e : __builtin_inff();
-  }
-  float lse2[16];
-  int prow[16];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int rw = 8 * (v >> 2) + 4 * half + (v & 3);  // row within the wave
-    const int po = (wave * 32 + rw) / G;
-    const int t = t0 + po;
-    lse2[v] = __shfl(lse_own, rw);
-    prow[v] = base + min(t, t_last);
-  }
-  // Wait for Q and the LSE values once, here; inside the tile loop the
-  // compiler would otherwise wait for every outstanding load (the
-  // prefetched tiles included) before their first use in each tile.
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+v"(qv[kk]));
-#pragma unroll
-  for (int v = 0; v < 16; ++v) asm volatile("" : "+v"(lse2[v]));
-
-  const int last_page = sg.n_pages - 1;
-  auto issue_tile = [&](int tile, int stage) {
-    const int k0 = tile * kTileKeys;
-    char *st = smem + stage * KSTAGE;
-    // Page ids of the tile's NP whole pages by scalar loads (as in the
-    // prefill); keys outside the stored pages read slot 0 of the nearest.
-    constexpr int NP = kTileKeys / P;
-    int pid[NP];
-    const int pg0 = (k0 - sg.first_token) / P;
-#pragma unroll
-    for (int i = 0; i < NP; ++i) pid[i] = sload(a.page_ids + sg.page_off + min(max(pg0 + i, 0), last_page));
-#pragma unroll
-    for (int j = 0; j < K_INSTR; ++j) {
-      const int c = (j * NW + wave) * 64 + lane;
-      const int row = c / L::KCPR;
-      const int logical = (c % L::KCPR) ^ L::k_swz(row);
-      if constexpr (P == kTileKeys) {
-        // one page per tile: a scalar page base and a 32-bit lane offset
-        lds_dma16_s(a.k_pool + static_cast<size_t>(pid[0]) * (P * D), static_cast<uint32_t>((row * D + logical * 8) * 2),
-                    st + (j * NW + wave) * 1024);
-      } else {
-        const int rel = k0 + row - sg.first_token;
-        const int slot = rel >= 0 && rel / P <= last_page ? row % P : 0;
-        int page = pid[0];
-#pragma unroll
-        for (int i = 1; i < NP; ++i)
-          if (row / P == i) page = pid[i];
-        lds_dma16(a.k_pool + (static_cast<size_t>(page) * P + slot) * D + logical * 8, st + (j * NW + wave) * 1024);
-      }
-    }
-  };
-
-  const int kswz = L::k_swz(col);  // keys col and col + 32 share it
-  // Key sums of one tile over this wave's 32 rows: c0 for key k0 + col, c1
-  // for key k0 + 32 + col (both lanes of a pair end with the full sums).
-  auto process = [&](const char *st, int k0, auto mask_tag, float &c0, float &c1) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    f32x16 s0 = f32x16{}, s1 = f32x16{};
-    // K operands stream two k-steps ahead of the products (scheduling
-    // fences keep the compiler from loading all of them up front).
-    bf16x8 kr[NKK][2];
-    auto kread = [&](int kk) {
-      const int c = (2 * kk + half) ^ kswz;
-      kr[kk][0] = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + (col * L::KCPR + c) * 16));
-      kr[kk][1] = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + ((col + 32) * L::KCPR + c) * 16));
+      for (int b = 0; b < RB; ++b) acc[b] = s[b];
+      return e + __shfl_xor(e, 32);
     };
-    kread(0);
-    kread(1);
+    // Tile i's sums of all waves are in sx[i % 2] after the barrier ending
+    // iteration i + 1; wave i % NW adds them (fixed order) during iteration
+    // i + 2 (or after the loop).
+    auto flush = [&](int i) {
+      if (wave == i % NW) {
+        float acc = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      __builtin_amdgcn_sched_barrier(0);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qv[kk], kr[kk][0], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qv[kk], kr[kk][1], s1, 0, 0, 0);
-      if (kk + 2 < NKK) kread(kk + 2);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    float e0 = 0.f, e1 = 0.f;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      float x0 = fmaf(s0[v], a.scale_log2, -lse2[v]);
-      float x1 = fmaf(s1[v], a.scale_log2, -lse2[v]);
-      if constexpr (MASK) {
-        const int key0 = k0 + col, key1 = key0 + 32;
-        const int lo = W > 0 ? prow[v] - W + 1 : 0;
-        if (key0 > prow[v] || key0 < lo) x0 = kNegInf;
-        if (key1 > prow[v] || key1 < lo) x1 = kNegInf;
+        for (int w = 0; w < NW; ++w) acc += sx[i & 1][w][lane];
+        a.part[(static_cast<size_t>(it.part) + i) * kTileKeys + lane] = acc;
       }
-      e0 += fast_exp2(x0);
-      e1 += fast_exp2(x1);
-    }
-    c0 = e0 + __shfl_xor(e0, 32);
-    c1 = e1 + __shfl_xor(e1, 32);
-  };
-  // Tile i's sums of all waves are in sx[i % 2] after the barrier ending
-  // iteration i; wave i % NW adds them (fixed order) during iteration i + 1.
-  auto flush = [&](int i) {
-    if (wave == i % NW) {
-      float acc = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) acc += sx[i & 1][w][lane];
-      a.part[(static_cast<size_t>(it.part) + i) * kTileKeys + lane] = acc;
-    }
-  };
+    };
+    // Whether every entry of this wave's rows against tile k0 is visible.
+    // Masked entries are still multiplied (they give 0).
+    auto tile_full = [&](int k0) {
+      return k0 + kTileKeys - 1 <= p_wmin && (W == 0 || k0 >= p_wmax - W + 1);
+    };
 
-  constexpr int LOADS_PER_TILE = K_INSTR;
-  const int tb = it.tile_begin, te = it.tile_end;
-  // Barriers leave the newest tile's loads in flight (see the prefill).
-  if (tb < te) issue_tile(tb, 0);
-  if (tb + 1 < te) {
-    issue_tile(tb + 1, 1);
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LOADS_PER_TILE) : "memory");
-  } else {
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  }
-  for (int tile = tb; tile < te; ++tile) {
-    const int i = tile - tb;
-    const bool ahead2 = tile + 2 < te;
-    if (ahead2) issue_tile(tile + 2, (i + 2) % NSTAGE);
-    if (i > 0) flush(i - 1);
-    const char *st = smem + (i % NSTAGE) * KSTAGE;
-    const int k0 = tile * kTileKeys;
-    const bool empty = k0 > p_wmax || (W > 0 && k0 + kTileKeys - 1 < p_wmin - W + 1);
-    const bool full = k0 + kTileKeys - 1 <= p_wmin && (W == 0 || k0 >= p_wmax - W + 1);
-    float c0 = 0.f, c1 = 0.f;
-    if (!empty) {
-      if (full)
-        process(st, k0, std::integral_constant<bool, false>{}, c0, c1);
+    constexpr int LOADS_PER_TILE = K_INSTR;
+    static_assert(AHEAD >= 1 && AHEAD <= 4, "wait counts below");
+    // Waits until at most `pending` tiles' loads are in flight (loads land in
+    // issue order), then meets the other waves: barriers leave the newest
+    // tiles' loads in flight (see the prefill).
+    auto wait_barrier = [&](int pending) {
+      if (pending >= 3)
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(3 * LOADS_PER_TILE) : "memory");
+      else if (pending == 2)
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * LOADS_PER_TILE) : "memory");
+      else if (pending == 1)
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LOADS_PER_TILE) : "memory");
       else
-        process(st, k0, std::integral_constant<bool, true>{}, c0, c1);
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+    const int tb = it.tile_begin, te = it.tile_end;
+    if (tb >= te) {  // (the host cuts no empty pieces; the hand-over stays uniform)
+      if (tid == 0) s_next[slot] = nxt + static_cast<int>(gridDim.x);
+      __syncthreads();
+      ii = __builtin_amdgcn_readfirstlane(s_next[slot]);
+      continue;
     }
-    sx[i & 1][wave][half * 32 + col] = half ? c1 : c0;
-    if (ahead2)
-      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LOADS_PER_TILE) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    for (int j = 0; j < AHEAD && tb + j < te; ++j) issue_tile(tb + j, j);
+    wait_barrier(min(AHEAD, te - tb) - 1);
+    // sa / sb: scores of the current tile's first / second key half.  The
+    // second half of tile i is exponentiated during the first half step of
+    // tile i + 1 (at the first tile, during a step over zeros whose sum is
+    // dropped), so tile i's sums go to sx one iteration late.
+    f32x16 sa[RB], sb[RB];
+#pragma unroll
+    for (int b = 0; b < RB; ++b) sa[b] = sb[b] = f32x16{};
+    float c0 = 0.f;
+    bool full_prev = true;
+    for (int tile = tb; tile < te; ++tile) {
+      const int i = tile - tb;
+      if (tile + AHEAD < te) issue_tile(tile + AHEAD, (i + AHEAD) % NSTAGE);
+      if (i >= 2) flush(i - 2);
+      const char *st = smem + (i % NSTAGE) * KSTAGE;
+      const int k0 = tile * kTileKeys;
+      const bool full = tile_full(k0);
+      if (!full_prev) apply_mask(sb, k0 - 32 + col);
+      const float c1 = half_step(st, 0, sa, sb);
+      if (i >= 1) sx[(i - 1) & 1][wave][half * 32 + col] = half ? c1 : c0;
+      if (!full) apply_mask(sa, k0 + col);
+      c0 = half_step(st, 1, sb, sa);
+      full_prev = full;
+      wait_barrier(min(AHEAD, te - 1 - tile) - 1);  // tile + 1 has landed
+    }
+    const int n = te - tb;
+    if (n >= 2) flush(n - 2);
+    if (!full_prev) apply_mask(sb, te * kTileKeys - 32 + col);
+    float e = 0.f;
+#pragma unroll
+    for (int m = 0; m < RB * 16; ++m) e += fast_exp2(fmaf(sb[m / 16][m % 16], a.scale_log2, -lse2[m / 16][m % 16]));
+    const float c1 = e + __shfl_xor(e, 32);
+    sx[(n - 1) & 1][wave][half * 32 + col] = half ? c1 : c0;
+    if (tid == 0) s_next[slot] = nxt + static_cast<int>(gridDim.x);
+    __syncthreads();
+    flush(n - 1);
+    ii = __builtin_amdgcn_readfirstlane(s_next[slot]);
   }
-  if (te > tb) flush(te - tb - 1);
 }
 
 // Scores of the chunk's keys: one workgroup per 64-key tile, 16 waves.  A
@@ -434,9 +525,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
 
 }  // namespace
 
-hipError_t launch_score(const ScoreArgs &a, int n_items, int head_dim, int page_size, hipStream_t s) {
-  if (n_items <= 0) return hipSuccess;
-  SEGKV_DISPATCH_DP(score_kernel, head_dim, page_size, dim3(n_items), dim3(kPrefillThreads), s, a);
+hipError_t launch_score(const ScoreArgs &a, int n_wgs, int head_dim, int page_size, hipStream_t s) {
+  if (n_wgs <= 0) return hipSuccess;
+  SEGKV_DISPATCH_DP(score_kernel, head_dim, page_size, dim3(n_wgs), dim3(kScoreThreads), s, a);
   return hipGetLastError();
 }
 

@@ -647,7 +647,7 @@ WsBound workspace_bound(const segkv_config *cfg, int64_t Q, int64_t slots) {
   // items are cut into pieces of at least kMinSplitTiles tiles
   const int64_t cut_items = base_items + ceil_div(part_rows, kMinSplitTiles);
   const size_t s_tables = align_up(seq_tables, 16) + align_up(sizeof(PrefillItem) * cut_items, 16) +
-                          align_up(sizeof(ScoreRow) * srows, 16) + sizeof(int32_t) * part_rows;
+                          align_up(sizeof(ScoreRow) * srows, 16) + align_up(sizeof(int32_t) * part_rows, 16) + 16;
   const size_t s_part = static_cast<size_t>(std::max<int64_t>(part_rows, 1)) * kTileKeys * sizeof(float);
   b.tables = std::max({p_tables, d_tables, k_tables});
   b.total = std::max({with_parts(p_tables, p_part), with_parts(d_tables, d_part), with_parts(s_tables, s_part),
@@ -1463,10 +1463,14 @@ int segkv_token_scores(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_
       }
     }
   }
+  // Pieces of at most `split` tiles; a persistent grid of resident
+  // workgroups takes them from a queue, longest first (sorted below), so
+  // workgroups that run faster (the CU's arbitration favours older waves)
+  // take more of them.
   int64_t split = c->prefill_split_tiles;
   if (split <= 0) {
-    const int64_t slots = std::max<int64_t>(1, static_cast<int64_t>(c->num_cus) * kPrefillWgPerCu);
-    split = std::max<int64_t>(kMinSplitTiles, ceil_div(total_cost, slots));
+    const int64_t slots = std::max<int64_t>(1, static_cast<int64_t>(c->num_cus) * kScoreWgPerCu);
+    split = std::max<int64_t>(kMinSplitTiles, ceil_div(total_cost, kScorePiecesPerSlot * slots));
   }
   std::vector<PrefillItem> cut;
   int32_t n_part_rows = 0;
@@ -1502,17 +1506,19 @@ int segkv_token_scores(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_
       first = last;
     }
   }
-  // Schedule longest first (the sums do not depend on it).
+  // Longest first (the sums do not depend on the order).
   std::stable_sort(cut.begin(), cut.end(), [](const PrefillItem &x, const PrefillItem &y) {
     return x.tile_end - x.tile_begin > y.tile_end - y.tile_begin;
   });
+  const int64_t n_wgs = std::min<int64_t>(static_cast<int64_t>(cut.size()),
+                                          std::max<int64_t>(1, static_cast<int64_t>(c->num_cus) * kScoreWgPerCu));
 
   const SeqTables tl = seq_tables_layout(c, layer, n_seqs, seq_ids);
   const size_t tbytes = align_up(tl.bytes, 16);
   const size_t ibytes = align_up(sizeof(PrefillItem) * cut.size(), 16);
   const size_t rbytes = align_up(sizeof(ScoreRow) * srows.size(), 16);
-  const size_t pbytes = sizeof(int32_t) * pidx.size();
-  const size_t bytes = tbytes + ibytes + rbytes + pbytes;
+  const size_t pbytes = align_up(sizeof(int32_t) * pidx.size(), 16);
+  const size_t bytes = tbytes + ibytes + rbytes + pbytes + 16;  // + the queue counter (uploaded as 0)
   float *parts = nullptr;
   rc = carve(c, c->ws, c->ws_bytes, bytes, static_cast<size_t>(std::max(n_part_rows, 1)) * kTileKeys * sizeof(float),
              &parts);
@@ -1529,7 +1535,8 @@ int segkv_token_scores(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_
   write_seq_tables(c, layer, n_seqs, seq_ids, qs.data(), qlv.data(), tl, stage);
   std::memcpy(stage + tbytes, cut.data(), sizeof(PrefillItem) * cut.size());
   std::memcpy(stage + tbytes + ibytes, srows.data(), sizeof(ScoreRow) * srows.size());
-  if (pbytes) std::memcpy(stage + tbytes + ibytes + rbytes, pidx.data(), pbytes);
+  if (!pidx.empty()) std::memcpy(stage + tbytes + ibytes + rbytes, pidx.data(), sizeof(int32_t) * pidx.size());
+  std::memset(stage + tbytes + ibytes + rbytes + pbytes, 0, 16);
   rc = upload(c, slot, bytes, c->ws);
   if (rc) return rc;
 
@@ -1542,6 +1549,8 @@ int segkv_token_scores(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_
   a.page_ids = reinterpret_cast<const int32_t *>(c->ws + tl.pid_off);
   a.rope = rope_args(c, tl, c->ws);
   a.items = reinterpret_cast<const PrefillItem *>(c->ws + tbytes);
+  a.counter = reinterpret_cast<int32_t *>(c->ws + tbytes + ibytes + rbytes + pbytes);
+  a.n_items = static_cast<int32_t>(cut.size());
   a.part = parts;
   a.num_q_heads = c->Hq;
   a.num_kv_heads = c->Hkv;
@@ -1551,7 +1560,7 @@ int segkv_token_scores(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_
   TimedLaunch t{};
   rc = timed_begin(c, &t, SEGKV_KERNEL_SCORE);
   if (rc) return rc;
-  hipError_t e = launch_score(a, static_cast<int>(cut.size()), c->D, c->P, c->stream);
+  hipError_t e = launch_score(a, static_cast<int>(n_wgs), c->D, c->P, c->stream);
   if (e != hipSuccess) return c->device_fail(e, "score launch");
   rc = timed_end(c, &t);
   if (rc) return rc;

@@ -32,6 +32,8 @@ constexpr int kTopkThreads = 1024;
 constexpr int kTopkRun = 8;  // consecutive keys per thread per batch
 constexpr int kMergeUnroll = 4;    // (row, head) pairs in flight per lane of the merge kernel
 constexpr int kPrefillWgPerCu = 1;  // resident prefill workgroups per CU (104 KiB of LDS each at D = 128): the persistent grid
+constexpr int kScoreWgPerCu = 2;  // resident token-score workgroups per CU (4 waves of 64 rows each)
+constexpr int kScorePiecesPerSlot = 2;  // automatic token-score pieces: about this many per resident workgroup
 constexpr int kDecodeWgPerCu = 1;   // resident decode workgroups per CU (the stream-K grid size)
 constexpr int kXcds = 8;           // MI355X: workgroup i of a launch runs on XCD i % 8
 
@@ -207,6 +209,8 @@ struct ScoreArgs {
   const SegDesc *segs;
   const int32_t *page_ids;
   const PrefillItem *items;
+  int32_t *counter;      // work queue: items taken past the grid's first ones (0 at launch)
+  int32_t n_items;
   float *part;           // [partial rows][64]
   int32_t num_q_heads;
   int32_t num_kv_heads;

@@ -18,7 +18,7 @@ hipError_t launch_prefill_wide(const PrefillArgs &a, int n_items, int head_dim, 
 hipError_t launch_decode(const DecodeArgs &a, int n_wgs, int head_dim, int page_size, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, int n_items, int max_entries, int head_dim, hipStream_t s);
 hipError_t launch_merge(const MergeArgs &a, int n_wgs, int head_dim, hipStream_t s);
-hipError_t launch_score(const ScoreArgs &a, int n_items, int head_dim, int page_size, hipStream_t s);
+hipError_t launch_score(const ScoreArgs &a, int n_wgs, int head_dim, int page_size, hipStream_t s);
 hipError_t launch_score_reduce(const ScoreReduceArgs &a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs &a, int n_seqs, hipStream_t s);
 // bytes are rounded up to 16; both buffers must hold the rounded size
