@@ -809,11 +809,16 @@ __global__ __launch_bounds__(kPrefillWideThreads, 1) void prefill_wide_kernel(Pr
         __builtin_amdgcn_sched_barrier(0);
         const int ks = g / NDB, db = g % NDB;
         const bf16x8 vn = g + 1 < NG ? v_frag(st, 2 * h + (g + 1) / NDB, (g + 1) % NDB) : vf;
+        // Empty asm statements pin the program order (the product pair, then
+        // the body slice under it): the body's pure arithmetic would
+        // otherwise be hoisted above all the products of the step.
+        asm volatile("" : "+v"(vf));
 #pragma unroll
         for (int c = 0; c < 2; ++c)
           oacc[c][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, (*pk_prev)[c][ks], oacc[c][db], 0, 0, 0);
         const int j0 = g * VPG;
         body(pk_cur, j0 / 16, j0 % 16, VPG);
+        asm volatile("" : "+v"(l[j0 / 16]));
         vf = vn;
       }
       __builtin_amdgcn_sched_barrier(0);
