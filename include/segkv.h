@@ -361,6 +361,10 @@ int segkv_read_timing(segkv_ctx *ctx, int32_t kernel, double *total_ms, int64_t 
  *                                      batch's total tiles over the GPU's
  *                                      resident workgroup slots (at least
  *                                      16); a huge value disables splitting.
+ *                                      The token-score pass cuts its items
+ *                                      into pieces of at most this many tiles
+ *                                      too (automatic: the total over twice
+ *                                      its resident workgroups, at least 16).
  *   SEGKV_TUNE_PREFILL_ORDER           0 (default): the work list is taken
  *                                      longest first; 1: the list is cut into
  *                                      eight cost-balanced runs grouped by
@@ -376,7 +380,14 @@ int segkv_read_timing(segkv_ctx *ctx, int32_t kernel, double *total_ms, int64_t 
  *                                      of four waves one phase apart (one
  *                                      group's products beside the other's
  *                                      softmax), over per-workgroup item lists
- *                                      balanced on the host.
+ *                                      balanced on the host;
+ *                                      4: the 8 x 32-row kernel software
+ *                                      pipelined across tiles (each tile's
+ *                                      exponentials under the next tile's QK
+ *                                      products, its mask and max under the
+ *                                      PV products).
+ *                                      Values outside 0 .. 4 are rejected
+ *                                      (SEGKV_E_INVAL).
  * Results do not depend on the knobs beyond fp32 rounding of split merges.
  */
 enum segkv_tune {
