@@ -439,7 +439,7 @@ def _blas_threads():
         return None
 
 
-def cpu_baseline(w, x, budget_s=15.0):
+def cpu_baseline(w, x, budget_s=30.0):
     """The fp64 oracle, as it stands, on a seeded sample of query rows of the
     workload (all heads; rows spread over the sequences in proportion to
     their query counts), timed on the host cores."""
@@ -491,7 +491,7 @@ def cpu_baseline(w, x, budget_s=15.0):
     return out
 
 
-def cpu_baseline_decode(w, x, budget_s=8.0):
+def cpu_baseline_decode(w, x, budget_s=20.0):
     """The fp64 oracle on the decode workload's sequences (one query row each,
     all heads), as visible-KV GB/s: the same algorithmic bytes as the GPU
     figure, over the oracle's wall time, on a growing prefix of the batch."""
@@ -512,9 +512,17 @@ def cpu_baseline_decode(w, x, budget_s=8.0):
     while t < budget_s / 2 and n < w.n_seqs:
         n = min(w.n_seqs, n * 2)
         t = run(n)
+    reps = 1
+    if t < budget_s / 2:  # the whole batch is cheap: time repeated passes
+        reps = int(np.ceil(budget_s / 2 / t))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            run(n)
+        t = (time.perf_counter() - t0) / reps
     return {"value": by * n / t / 1e9, "unit": "GB/s", "cores": threads or os.cpu_count(), "kind": "oracle",
             "sample": f"{n} of {w.n_seqs} sequences of {w.name} (one query row, all {w.num_q_heads} heads), "
-                      f"{t:.1f} s; fp64 numpy, BLAS threads={threads}, host cpus={os.cpu_count()}"}
+                      f"{t:.1f} s per pass, {reps} pass(es); fp64 numpy, BLAS threads={threads}, "
+                      f"host cpus={os.cpu_count()}"}
 
 
 # ------------------------------------------------------------------ main
