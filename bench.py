@@ -74,9 +74,9 @@ CSRC = os.path.join(ROOT, "long_context_serving_amd", "csrc")
 # Sources whose digest identifies each measured kernel: its own file plus the
 # shared device helpers and the argument layouts.
 KERNEL_SRC = {
-    "prefill": ["prefill.hip", "kernels_common.h", "segkv_internal.h"],
-    "score": ["score.hip", "kernels_common.h", "segkv_internal.h"],
-    "decode": ["decode.hip", "kernels_common.h", "segkv_internal.h"],
+    "prefill": ["prefill.hip", "kernels_common.h", "page_layout.h", "segkv_internal.h"],
+    "score": ["score.hip", "kernels_common.h", "page_layout.h", "segkv_internal.h"],
+    "decode": ["decode.hip", "kernels_common.h", "page_layout.h", "segkv_internal.h"],
     "merge": ["merge.hip", "kernels_common.h", "segkv_internal.h"],
 }
 RELOCATION_OFFSET = 8192    # document offset of the relocation arm

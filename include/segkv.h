@@ -82,9 +82,12 @@ typedef struct segkv_config {
                                  Copied at create. */
   float softmax_scale;    /* 0 => 1/sqrt(head_dim) */
   uint64_t page_order_seed; /* 0 => free list hands out pages in index order; else a seeded permutation */
-  void *k_pool;           /* device bf16 [num_pages][page_size][head_dim]: one page = page_size K rows of one
-                             (layer, sequence, KV head) */
-  void *v_pool;           /* device bf16 [num_pages][head_dim][page_size]: each V page is stored transposed */
+  void *k_pool;           /* device bf16, num_pages * page_size * head_dim elements: one page = page_size K rows
+                             of one (layer, sequence, KV head).  Inside a page the rows go in pairs, and each
+                             128-byte line holds the same 64-byte group of both rows of a pair. */
+  void *v_pool;           /* device bf16, the same size: each V page is stored transposed (head_dim channel rows
+                             of page_size keys), channel rows paired the same way when longer than 64 bytes.
+                             The library alone reads and writes both pools. */
   void *stream;           /* hipStream_t for all device work; NULL = the default stream */
   /* Rotary position code of the queries, used only by segkv_set_relocation
      (zero-initialised fields give the defaults). */

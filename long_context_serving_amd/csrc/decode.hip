@@ -2,6 +2,7 @@
 // fixed device scratch of the decode entry point that allocates nothing.
 
 #include "kernels_common.h"
+#include "page_layout.h"
 #include "segkv_launch.h"
 
 #include <mutex>
@@ -38,6 +39,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
   constexpr int NW = kDecodeThreads / 64;
   constexpr int TPC = D / 4;   // merge threads per column
   constexpr int NSLOT = kDecodeSlots;
+  using PL = PageLayout<D, P>;
   constexpr int MAXP = NSLOT - NW + 1;  // pieces per batch: (piece, wave) pairs fit the slots
   static_assert(MAXP >= 1, "too few partial slots");
   __shared__ float s_m[NSLOT][kDecodeCols];
@@ -117,11 +119,11 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
           const int rel = key - sg.first_token;
           const bool ok = key < key_end;
           const int page = P == 64 ? upage : (ok ? a.page_ids[sg.page_off + rel / P] : 0);
-          const uint16_t *krow = a.k_pool + (static_cast<size_t>(page) * P + rel % P) * D;
+          const uint16_t *kpage = a.k_pool + static_cast<size_t>(page) * P * D;
 #pragma unroll
           for (int kk = 0; kk < NKK; ++kk) {
             u32x4 x = {0u, 0u, 0u, 0u};
-            if (ok) x = ld16(krow + kk * 32 + u * 8);
+            if (ok) x = ld16(kpage + PL::k_elem(rel % P, 4 * kk + u));
             kb_[hb][kk] = x;
           }
         }
@@ -129,11 +131,11 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
         const int rel = key - sg.first_token;
         const bool ok = key < key_end;
         const int page = P == 64 ? upage : (ok ? a.page_ids[sg.page_off + rel / P] : 0);
-        const uint16_t *vbase = a.v_pool + static_cast<size_t>(page) * P * D + rel % P;
+        const uint16_t *vpage = a.v_pool + static_cast<size_t>(page) * P * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           u32x4 x = {0u, 0u, 0u, 0u};
-          if (ok) x = ld16(vbase + static_cast<size_t>(db * 16 + c16) * P);
+          if (ok) x = ld16(vpage + PL::v_elem(db * 16 + c16, (rel % P) >> 3));
           vb_[db] = x;
         }
       };

@@ -1,6 +1,7 @@
 // HIP kernel of libsegkv: varlen prefill attention (8 waves x 32 rows, the default).
 
 #include "kernels_common.h"
+#include "page_layout.h"
 #include "segkv_launch.h"
 
 namespace segkv {
@@ -19,6 +20,7 @@ namespace {
 template <int D, int P>
 __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs a) {
   using L = PrefillLds<D>;
+  using PL = PageLayout<D, P>;
   constexpr int NKK = D / 16;  // k-steps of the QK product
   constexpr int NDB = D / 32;  // 32-channel blocks of O^T
   constexpr int NW = kPrefillThreads / 64;
@@ -97,12 +99,12 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
       const int logical = (c % L::KCPR) ^ L::k_swz(row);
       if constexpr (P == kTileKeys) {
         // one page per tile: a scalar page base and a 32-bit lane offset
-        lds_dma16_s(a.k_pool + static_cast<size_t>(pid[0]) * (P * D), static_cast<uint32_t>((row * D + logical * 8) * 2),
+        lds_dma16_s(a.k_pool + static_cast<size_t>(pid[0]) * (P * D), static_cast<uint32_t>(PL::k_elem(row, logical) * 2),
                     st + (j * NW + wave) * 1024);
       } else {
         int slot;
         const int page = page_of(row, &slot);
-        lds_dma16(a.k_pool + (static_cast<size_t>(page) * P + slot) * D + logical * 8, st + (j * NW + wave) * 1024);
+        lds_dma16(a.k_pool + static_cast<size_t>(page) * (P * D) + PL::k_elem(slot, logical), st + (j * NW + wave) * 1024);
       }
     }
 #pragma unroll
@@ -111,12 +113,12 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
       const int d = c / 8;
       const int logical = (c % 8) ^ L::v_swz(d);
       if constexpr (P == kTileKeys) {
-        lds_dma16_s(a.v_pool + static_cast<size_t>(pid[0]) * (P * D), static_cast<uint32_t>((d * P + logical * 8) * 2),
+        lds_dma16_s(a.v_pool + static_cast<size_t>(pid[0]) * (P * D), static_cast<uint32_t>(PL::v_elem(d, logical) * 2),
                     st + L::K_CHUNKS * 16 + (j * NW + wave) * 1024);
       } else {
         int slot;
         const int page = page_of(logical * 8, &slot);
-        lds_dma16(a.v_pool + static_cast<size_t>(page) * (P * D) + d * P + slot,
+        lds_dma16(a.v_pool + static_cast<size_t>(page) * (P * D) + PL::v_elem(d, slot >> 3),
                   st + L::K_CHUNKS * 16 + (j * NW + wave) * 1024);
       }
     }

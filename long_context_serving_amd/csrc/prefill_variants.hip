@@ -2,6 +2,7 @@
 // (two groups one phase apart; four waves of 64 rows; software pipelined).
 
 #include "kernels_common.h"
+#include "page_layout.h"
 #include "segkv_launch.h"
 
 namespace segkv {
@@ -32,6 +33,7 @@ namespace {
 template <int D, int P>
 __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_pp_kernel(PrefillArgs a) {
   using L = PrefillLds<D>;
+  using PL = PageLayout<D, P>;
   constexpr int NKK = D / 16;  // k-steps of the QK product
   constexpr int NDB = D / 32;  // 32-channel blocks of O^T
   constexpr int NW = kPrefillThreads / 64;
@@ -102,12 +104,12 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_pp_kernel(PrefillA
       const int row = c / L::KCPR;
       const int logical = (c % L::KCPR) ^ L::k_swz(row);
       if constexpr (P == kTileKeys) {
-        lds_dma16_s(a.k_pool + static_cast<size_t>(pid[0]) * (P * D), static_cast<uint32_t>((row * D + logical * 8) * 2),
+        lds_dma16_s(a.k_pool + static_cast<size_t>(pid[0]) * (P * D), static_cast<uint32_t>(PL::k_elem(row, logical) * 2),
                     st + (j * PW + wave) * 1024);
       } else {
         int slot;
         const int page = page_of(row, &slot);
-        lds_dma16(a.k_pool + (static_cast<size_t>(page) * P + slot) * D + logical * 8, st + (j * PW + wave) * 1024);
+        lds_dma16(a.k_pool + static_cast<size_t>(page) * (P * D) + PL::k_elem(slot, logical), st + (j * PW + wave) * 1024);
       }
     }
 #pragma unroll
@@ -116,12 +118,12 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_pp_kernel(PrefillA
       const int d = c / 8;
       const int logical = (c % 8) ^ L::v_swz(d);
       if constexpr (P == kTileKeys) {
-        lds_dma16_s(a.v_pool + static_cast<size_t>(pid[0]) * (P * D), static_cast<uint32_t>((d * P + logical * 8) * 2),
+        lds_dma16_s(a.v_pool + static_cast<size_t>(pid[0]) * (P * D), static_cast<uint32_t>(PL::v_elem(d, logical) * 2),
                     st + L::K_CHUNKS * 16 + (j * PW + wave) * 1024);
       } else {
         int slot;
         const int page = page_of(logical * 8, &slot);
-        lds_dma16(a.v_pool + static_cast<size_t>(page) * (P * D) + d * P + slot,
+        lds_dma16(a.v_pool + static_cast<size_t>(page) * (P * D) + PL::v_elem(d, slot >> 3),
                   st + L::K_CHUNKS * 16 + (j * PW + wave) * 1024);
       }
     }
@@ -501,6 +503,7 @@ __device__ __forceinline__ float max16(const f32x16 &x) {
 template <int D, int P>
 __global__ __launch_bounds__(kPrefillWideThreads, 1) void prefill_wide_kernel(PrefillArgs a) {
   using L = PrefillLds<D>;
+  using PL = PageLayout<D, P>;
   constexpr int NKK = D / 16;  // k-steps of the QK product
   constexpr int NDB = D / 32;  // 32-channel blocks of O^T
   constexpr int NW = kPrefillWideThreads / 64;
@@ -569,11 +572,11 @@ __global__ __launch_bounds__(kPrefillWideThreads, 1) void prefill_wide_kernel(Pr
       const int logical = (c % L::KCPR) ^ L::k_swz(row);
       const uint16_t *src;
       if constexpr (P == kTileKeys) {
-        src = a.k_pool + static_cast<size_t>(pid[0]) * (P * D) + row * D + logical * 8;
+        src = a.k_pool + static_cast<size_t>(pid[0]) * (P * D) + PL::k_elem(row, logical);
       } else {
         int slot;
         const int page = page_of(row, &slot);
-        src = a.k_pool + (static_cast<size_t>(page) * P + slot) * D + logical * 8;
+        src = a.k_pool + static_cast<size_t>(page) * (P * D) + PL::k_elem(slot, logical);
       }
       lds_dma16(src, st + (j * NW + wave) * 1024);
     }
@@ -584,11 +587,11 @@ __global__ __launch_bounds__(kPrefillWideThreads, 1) void prefill_wide_kernel(Pr
       const int logical = (c % 8) ^ L::v_swz(d);
       const uint16_t *src;
       if constexpr (P == kTileKeys) {
-        src = a.v_pool + static_cast<size_t>(pid[0]) * (P * D) + d * P + logical * 8;
+        src = a.v_pool + static_cast<size_t>(pid[0]) * (P * D) + PL::v_elem(d, logical);
       } else {
         int slot;
         const int page = page_of(logical * 8, &slot);
-        src = a.v_pool + static_cast<size_t>(page) * (P * D) + d * P + slot;
+        src = a.v_pool + static_cast<size_t>(page) * (P * D) + PL::v_elem(d, slot >> 3);
       }
       lds_dma16(src, st + L::K_CHUNKS * 16 + (j * NW + wave) * 1024);
     }
@@ -968,6 +971,7 @@ __global__ __launch_bounds__(kPrefillWideThreads, 1) void prefill_wide_kernel(Pr
 template <int D, int P>
 __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_sp_kernel(PrefillArgs a) {
   using L = PrefillLds<D>;
+  using PL = PageLayout<D, P>;
   constexpr int NKK = D / 16;  // k-steps of the QK product
   constexpr int NDB = D / 32;  // 32-channel blocks of O^T
   constexpr int NW = kPrefillThreads / 64;
@@ -1036,12 +1040,12 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_sp_kernel(PrefillA
       const int row = c / L::KCPR;
       const int logical = (c % L::KCPR) ^ L::k_swz(row);
       if constexpr (P == kTileKeys) {
-        lds_dma16_s(a.k_pool + static_cast<size_t>(pid[0]) * (P * D), static_cast<uint32_t>((row * D + logical * 8) * 2),
+        lds_dma16_s(a.k_pool + static_cast<size_t>(pid[0]) * (P * D), static_cast<uint32_t>(PL::k_elem(row, logical) * 2),
                     st + (j * NW + wave) * 1024);
       } else {
         int slot;
         const int page = page_of(row, &slot);
-        lds_dma16(a.k_pool + (static_cast<size_t>(page) * P + slot) * D + logical * 8, st + (j * NW + wave) * 1024);
+        lds_dma16(a.k_pool + static_cast<size_t>(page) * (P * D) + PL::k_elem(slot, logical), st + (j * NW + wave) * 1024);
       }
     }
 #pragma unroll
@@ -1050,12 +1054,12 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_sp_kernel(PrefillA
       const int d = c / 8;
       const int logical = (c % 8) ^ L::v_swz(d);
       if constexpr (P == kTileKeys) {
-        lds_dma16_s(a.v_pool + static_cast<size_t>(pid[0]) * (P * D), static_cast<uint32_t>((d * P + logical * 8) * 2),
+        lds_dma16_s(a.v_pool + static_cast<size_t>(pid[0]) * (P * D), static_cast<uint32_t>(PL::v_elem(d, logical) * 2),
                     st + L::K_CHUNKS * 16 + (j * NW + wave) * 1024);
       } else {
         int slot;
         const int page = page_of(logical * 8, &slot);
-        lds_dma16(a.v_pool + static_cast<size_t>(page) * (P * D) + d * P + slot,
+        lds_dma16(a.v_pool + static_cast<size_t>(page) * (P * D) + PL::v_elem(d, slot >> 3),
                   st + L::K_CHUNKS * 16 + (j * NW + wave) * 1024);
       }
     }

@@ -1,6 +1,7 @@
 // HIP kernels of libsegkv: KV append scatter and the per-call table upload.
 
 #include "kernels_common.h"
+#include "page_layout.h"
 #include "segkv_launch.h"
 
 namespace segkv {
@@ -21,6 +22,7 @@ __global__ __launch_bounds__(kScatterThreads) void scatter_kernel(ScatterArgs a)
   }
   const ScatterItem it = a.items[blockIdx.x - a.copy_wgs];
   constexpr int CPR = D / 8;  // 16-byte chunks per row
+  using PL = PageLayout<D, P>;
   // 16-byte chunk c of staged V row `slot` sits at chunk c ^ (slot / 8 % CPR)
   auto vswz = [](int slot, int c) { return c ^ ((slot >> 3) & (CPR - 1)); };
   const int n_rows = it.slot_end - it.slot_begin;
@@ -32,11 +34,14 @@ __global__ __launch_bounds__(kScatterThreads) void scatter_kernel(ScatterArgs a)
   if (it.copy_from >= 0) {
     const uint16_t *ksrc = a.k_pool + static_cast<size_t>(it.copy_from) * P * D;
     const uint16_t *vsrc = a.v_pool + static_cast<size_t>(it.copy_from) * P * D;
-    for (int c = tid; c < it.slot_begin * CPR; c += kScatterThreads)
-      *reinterpret_cast<u32x4 *>(kpage + c * 8) = ld16(ksrc + c * 8);
+    for (int c = tid; c < it.slot_begin * CPR; c += kScatterThreads) {
+      const int off = PL::k_elem(c / CPR, c % CPR);
+      *reinterpret_cast<u32x4 *>(kpage + off) = ld16(ksrc + off);
+    }
     for (int c = tid; c < D * it.slot_begin; c += kScatterThreads) {
       const int d = c / it.slot_begin, sl = c - d * it.slot_begin;
-      vpage[d * P + sl] = vsrc[d * P + sl];
+      const int off = PL::v_elem(d, sl >> 3) + (sl & 7);
+      vpage[off] = vsrc[off];
     }
   }
 
@@ -60,7 +65,7 @@ __global__ __launch_bounds__(kScatterThreads) void scatter_kernel(ScatterArgs a)
     const int c = tid + i * kScatterThreads;
     if (c < n_rows * CPR) {
       const int row = c / CPR, dc = c - row * CPR;
-      *reinterpret_cast<u32x4 *>(kpage + static_cast<size_t>(it.slot_begin + row) * D + dc * 8) = kx[i];
+      *reinterpret_cast<u32x4 *>(kpage + PL::k_elem(it.slot_begin + row, dc)) = kx[i];
       *reinterpret_cast<u32x4 *>(sv + (it.slot_begin + row) * D + vswz(it.slot_begin + row, dc) * 8) = vx[i];
     }
   }
@@ -68,17 +73,17 @@ __global__ __launch_bounds__(kScatterThreads) void scatter_kernel(ScatterArgs a)
     const u32x4 z = {0u, 0u, 0u, 0u};
     for (int c = tid; c < (P - it.slot_end) * CPR; c += kScatterThreads) {
       const int row = c / CPR, dc = c - row * CPR;
-      *reinterpret_cast<u32x4 *>(kpage + static_cast<size_t>(it.slot_end + row) * D + dc * 8) = z;
+      *reinterpret_cast<u32x4 *>(kpage + PL::k_elem(it.slot_end + row, dc)) = z;
       *reinterpret_cast<u32x4 *>(sv + (it.slot_end + row) * D + vswz(it.slot_end + row, dc) * 8) = z;
     }
   }
   __syncthreads();
-  // V^T rows: channel d holds slots [slot_begin, wend) contiguously.  A
-  // lane takes a channel pair and 8 consecutive slots: one 4-byte LDS read
-  // per slot and two 16-byte stores.  Consecutive lanes take consecutive
-  // slot groups of one channel pair, so 8 lanes store a whole 128-byte
-  // channel row; the chunk swizzle of the staged rows spreads their LDS
-  // reads over the banks.
+  // V^T rows: channel d takes slots [slot_begin, wend).  A lane takes a
+  // channel pair and 8 consecutive slots: one 4-byte LDS read per slot and
+  // two 16-byte stores.  Consecutive lanes take consecutive slot groups of
+  // one channel pair, so 8 lanes store both channel rows of the pair (whole
+  // lines of the page); the chunk swizzle of the staged rows spreads their
+  // LDS reads over the banks.
   const int wend = it.zero_tail ? P : it.slot_end;
   const int n = wend - it.slot_begin;
   if ((it.slot_begin & 7) == 0 && (n & 7) == 0) {
@@ -96,13 +101,13 @@ __global__ __launch_bounds__(kScatterThreads) void scatter_kernel(ScatterArgs a)
         lo[e] = (w[2 * e] & 0xffffu) | (w[2 * e + 1] << 16);
         hi[e] = (w[2 * e] >> 16) | (w[2 * e + 1] & 0xffff0000u);
       }
-      *reinterpret_cast<u32x4 *>(vpage + static_cast<size_t>(2 * dp) * P + s0) = lo;
-      *reinterpret_cast<u32x4 *>(vpage + static_cast<size_t>(2 * dp + 1) * P + s0) = hi;
+      *reinterpret_cast<u32x4 *>(vpage + PL::v_elem(2 * dp, s0 >> 3)) = lo;
+      *reinterpret_cast<u32x4 *>(vpage + PL::v_elem(2 * dp + 1, s0 >> 3)) = hi;
     }
   } else {
     for (int c = tid; c < D * n; c += kScatterThreads) {
       const int d = c / n, s = it.slot_begin + (c - d * n);
-      vpage[static_cast<size_t>(d) * P + s] = sv[s * D + vswz(s, d >> 3) * 8 + (d & 7)];
+      vpage[PL::v_elem(d, s >> 3) + (s & 7)] = sv[s * D + vswz(s, d >> 3) * 8 + (d & 7)];
     }
   }
 }

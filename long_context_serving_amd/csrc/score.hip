@@ -1,6 +1,7 @@
 // HIP kernels of libsegkv: attention-mass token scores and their top-k.
 
 #include "kernels_common.h"
+#include "page_layout.h"
 #include "segkv_launch.h"
 
 namespace segkv {
@@ -30,6 +31,7 @@ constexpr int kScoreThreads = 256;  // 4 waves of 64 rows: two workgroups per CU
 template <int D, int P>
 __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreArgs a) {
   using L = PrefillLds<D>;
+  using PL = PageLayout<D, P>;
   constexpr int NKK = D / 16;
   constexpr int NW = kScoreThreads / 64;
   constexpr int RB = 2;  // 32-row blocks per wave: each K operand read feeds RB products
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreArgs a) {
         const int logical = (c % L::KCPR) ^ L::k_swz(row);
         if constexpr (P == kTileKeys) {
           // one page per tile: a scalar page base and a 32-bit lane offset
-          lds_dma16_s(a.k_pool + static_cast<size_t>(pid[0]) * (P * D), static_cast<uint32_t>((row * D + logical * 8) * 2),
+          lds_dma16_s(a.k_pool + static_cast<size_t>(pid[0]) * (P * D), static_cast<uint32_t>(PL::k_elem(row, logical) * 2),
                       st + (j * NW + wave) * 1024);
         } else {
           const int rel = k0 + row - sg.first_token;
@@ -166,7 +168,7 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreArgs a) {
 #pragma unroll
           for (int i = 1; i < NP; ++i)
             if (row / P == i) page = pid[i];
-          lds_dma16(a.k_pool + (static_cast<size_t>(page) * P + slot) * D + logical * 8, st + (j * NW + wave) * 1024);
+          lds_dma16(a.k_pool + static_cast<size_t>(page) * (P * D) + PL::k_elem(slot, logical), st + (j * NW + wave) * 1024);
         }
       }
     };

@@ -51,11 +51,32 @@ def test_kernel_source_hash_is_the_kernel_files_digest():
     import hashlib
     bench = load_bench()
     csrc = os.path.join(ROOT, "long_context_serving_amd", "csrc")
-    for kind, files in (("prefill", ["prefill.hip", "kernels_common.h", "segkv_internal.h"]),
-                        ("decode", ["decode.hip", "kernels_common.h", "segkv_internal.h"])):
+    for kind, files in (("prefill", ["prefill.hip", "kernels_common.h", "page_layout.h", "segkv_internal.h"]),
+                        ("decode", ["decode.hip", "kernels_common.h", "page_layout.h", "segkv_internal.h"])):
         h = hashlib.sha256()
         for name in files:
             with open(os.path.join(csrc, name), "rb") as fh:
                 h.update(fh.read())
         assert bench.kernel_source_hash(kind) == h.hexdigest()[:16]
     assert bench.kernel_source_hash("prefill") != bench.kernel_source_hash("decode")
+
+
+def test_kernel_source_hash_covers_every_included_header():
+    """Each local header a measured kernel's source includes (directly or
+    through another header) is part of its digest; the launcher
+    declarations hold no device code and are left out."""
+    import re
+    bench = load_bench()
+    csrc = os.path.join(ROOT, "long_context_serving_amd", "csrc")
+
+    def includes(name, seen):
+        with open(os.path.join(csrc, name)) as fh:
+            for inc in re.findall(r'^#include "([^"]+)"', fh.read(), re.M):
+                if inc not in seen and os.path.exists(os.path.join(csrc, inc)):
+                    seen.add(inc)
+                    includes(inc, seen)
+        return seen
+
+    for kind, files in bench.KERNEL_SRC.items():
+        needed = includes(files[0], set()) - {"segkv_launch.h"}
+        assert needed <= set(files), (kind, sorted(needed - set(files)))
