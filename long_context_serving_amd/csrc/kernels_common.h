@@ -11,8 +11,9 @@
 // predicate.
 //
 // Pool layout (one page = page_size tokens of one (layer, sequence, KV head)):
-//   K page  [page_size][head_dim]  row-major, a key row is contiguous
-//   V page  [head_dim][page_size]  transposed, a channel row is contiguous
+//   K page  page_size key rows of head_dim channels
+//   V page  head_dim channel rows of page_size keys (transposed)
+// with rows stored in pairs, 64-byte groups interleaved (page_layout.h).
 // Both operands of both products then load 16-byte runs straight into the
 // MFMA operand layout.
 #pragma once

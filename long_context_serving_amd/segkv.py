@@ -180,8 +180,9 @@ class SegKV:
 
     ``planning=True`` builds a host-only context (allocator and page tables,
     no device pools, no HIP call).  Otherwise K/V pools are allocated with
-    torch on the current device unless given: K [num_pages][page][D], V
-    [num_pages][D][page] (each V page transposed).  The device workspace is a
+    torch on the current device unless given: K and V of num_pages * page *
+    D bf16 each (pages of K rows and of transposed V rows, in the library's
+    own in-page order).  The device workspace is a
     torch uint8 tensor, ``workspace`` if given, else one of
     ``workspace_bytes`` or segkv_workspace_bytes(config, max_batch_q_tokens)
     bytes; the library allocates no device memory of its own.
