@@ -537,7 +537,7 @@ def main():
                     help="profiling runs: only the segmented headline prefill, the 128K chunk, the Mistral-7B-shaped "
                          "prefill, segmented decode, the merge or the router")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--prefill-kernel", type=int, default=0, choices=[0, 1, 2, 3, 4],
+    ap.add_argument("--prefill-kernel", type=int, default=0, choices=[0, 1, 2, 3, 4, 5],
                     help="prefill kernel variant (SEGKV_TUNE_PREFILL_KERNEL); 0 = the library's default")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates rocprofv3 byte counters)")

@@ -388,8 +388,12 @@ int segkv_read_timing(segkv_ctx *ctx, int32_t kernel, double *total_ms, int64_t 
  *                                      pipelined across tiles (each tile's
  *                                      exponentials under the next tile's QK
  *                                      products, its mask and max under the
- *                                      PV products).
- *                                      Values outside 0 .. 4 are rejected
+ *                                      PV products);
+ *                                      5: two workgroups per CU, each of 4
+ *                                      waves x 32 rows over 128-row work
+ *                                      items with two K/V stages (needs
+ *                                      num_q_heads / num_kv_heads <= 128).
+ *                                      Values outside 0 .. 5 are rejected
  *                                      (SEGKV_E_INVAL).
  * Results do not depend on the knobs beyond fp32 rounding of split merges.
  */

@@ -46,6 +46,7 @@ constexpr int64_t kItemCostTiles = 2;
 constexpr int32_t kPrefillWide = 2;
 constexpr int32_t kPrefillTwoGroup = 3;
 constexpr int32_t kPrefillPipelined = 4;
+constexpr int32_t kPrefillDuo = 5;
 
 struct Segment {
   int32_t first_token = 0;
@@ -130,7 +131,8 @@ struct segkv_ctx {
   int32_t decode_pps = kDefaultDecodeMinPages;  // minimum pages per decode workgroup
   int64_t prefill_split_tiles = kDefaultPrefillSplitTiles;  // 0 = automatic
   int32_t prefill_order = 0;  // 0 = longest-first, 1 = XCD-aware
-  int32_t prefill_kernel = 0;  // 0/1 = 8 waves x 32 rows in step (default), 2 = 4 waves x 64 rows, 3 = two-group schedule
+  int32_t prefill_kernel = 0;  // 0/1 = 8 waves x 32 rows in step (default), 2 = 4 waves x 64 rows, 3 = two-group
+                               // schedule, 4 = pipelined, 5 = two workgroups per CU of 4 waves x 32 rows
 
   // timing
   int32_t timing_mask = 0;  // bit k: record events around kernel k
@@ -424,6 +426,12 @@ void write_seq_tables(const segkv_ctx *c, int32_t layer, int32_t n_seqs, const i
   }
 }
 
+// (query position, query head) rows of one prefill work item for the
+// context's prefill kernel.
+int32_t prefill_item_rows(const segkv_ctx *c) {
+  return c->prefill_kernel == kPrefillDuo ? kPrefillDuoRows : kPrefillRows;
+}
+
 // A prefill call's device tables, in upload order: sequence tables, work
 // items, combine items, the work-queue counter (16 bytes, zero), then the
 // per-workgroup item ranges of the two-group kernel.
@@ -441,7 +449,8 @@ void build_prefill_plan(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32
                         PrefillPlan *pp, std::vector<char> *out) {
   // Work items: (seq, kv head, q tile) over the KV tiles the rows can see.
   const int32_t G = c->G;
-  const int32_t rows = kPrefillRows / G;  // query positions per workgroup
+  const int32_t rows = prefill_item_rows(c) / G;  // query positions per work item
+  const int64_t wg_per_cu = c->prefill_kernel == kPrefillDuo ? kPrefillDuoWgPerCu : kPrefillWgPerCu;
   std::vector<PrefillItem> &items = c->scratch_pitems;
   std::vector<CombineItem> &citems = c->scratch_citems;
   items.clear();
@@ -468,7 +477,7 @@ void build_prefill_plan(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32
   // their parts are merged by the combine kernel.
   int64_t split = c->prefill_split_tiles;
   if (split <= 0) {
-    const int64_t slots = std::max<int64_t>(1, static_cast<int64_t>(c->num_cus) * kPrefillWgPerCu);
+    const int64_t slots = std::max<int64_t>(1, static_cast<int64_t>(c->num_cus) * wg_per_cu);
     split = std::max<int64_t>(kMinSplitTiles, ceil_div(total_cost, slots));
   }
   int32_t n_parts = 0;
@@ -537,7 +546,7 @@ void build_prefill_plan(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32
     lpt_sort(items);
   }
   const int32_t n_wgs = static_cast<int32_t>(std::min<int64_t>(
-      static_cast<int64_t>(items.size()), std::max<int64_t>(1, static_cast<int64_t>(c->num_cus) * kPrefillWgPerCu)));
+      static_cast<int64_t>(items.size()), std::max<int64_t>(1, static_cast<int64_t>(c->num_cus) * wg_per_cu)));
   std::vector<int32_t> &wg_off = c->scratch_wg;
   wg_off.assign(static_cast<size_t>(n_wgs) + 1, 0);
   if (c->prefill_kernel == kPrefillTwoGroup && n_wgs > 0) {
@@ -614,14 +623,24 @@ WsBound workspace_bound(const segkv_config *cfg, int64_t Q, int64_t slots) {
                             sizeof(float) * 2 * D * nseg;
   auto with_parts = [](size_t t, size_t p) { return align_up(align_up(t, 16), 256) + p; };
   WsBound b;
-  // prefill
+  // prefill: the larger of the default item shape (kPrefillRows rows, slots
+  // workgroups) and the two-workgroup variant's (kPrefillDuoRows rows, twice
+  // the workgroups); partial slots hold kPrefillRows rows either way
   const int64_t nq_tiles = ceil_div(Q, rows) + S;
+  size_t p_tables = 0, p_part = 0;
+  for (int shape = 0; shape < 2; ++shape) {
+    const int64_t r = shape ? std::max<int64_t>(1, kPrefillDuoRows / G) : rows;
+    const int64_t sl = shape ? slots / kPrefillWgPerCu * kPrefillDuoWgPerCu : slots;
+    const int64_t items = Hkv * (ceil_div(Q, r) + S);
+    const int64_t parts = 2 * sl;
+    const size_t t = align_up(seq_tables, 16) + align_up(sizeof(PrefillItem) * (items + parts), 16) +
+                     align_up(sizeof(CombineItem) * std::min(items, sl), 16) + 16 +
+                     align_up(sizeof(int32_t) * static_cast<size_t>(sl + 1), 16);
+    const size_t pp = static_cast<size_t>(parts) * kPrefillRows * (D + 1) * sizeof(float);
+    p_tables = std::max(p_tables, t);
+    p_part = std::max(p_part, pp);
+  }
   const int64_t base_items = Hkv * nq_tiles;
-  const int64_t p_parts = 2 * slots;
-  const size_t p_tables = align_up(seq_tables, 16) + align_up(sizeof(PrefillItem) * (base_items + p_parts), 16) +
-                          align_up(sizeof(CombineItem) * std::min(base_items, slots), 16) + 16 +
-                          align_up(sizeof(int32_t) * static_cast<size_t>(slots + 1), 16);
-  const size_t p_part = static_cast<size_t>(p_parts) * kPrefillRows * (D + 1) * sizeof(float);
   // decode
   const int64_t pieces = nseg + slots;
   const size_t d_tables = align_up(seq_tables, 16) + align_up(sizeof(DecodeItem) * pieces, 16) +
@@ -1174,7 +1193,7 @@ int segkv_prefill(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *se
   const size_t tbytes = pp.tbytes, ibytes = pp.ibytes, cbytes = pp.cbytes;
   const std::vector<CombineItem> &citems = c->scratch_citems;
   const int32_t G = c->G;
-  const int32_t rows = kPrefillRows / G;
+  const int32_t rows = prefill_item_rows(c) / G;
 
   PrefillArgs a;
   a.q = static_cast<const uint16_t *>(q);
@@ -1202,7 +1221,8 @@ int segkv_prefill(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *se
   TimedLaunch t{};
   rc = timed_begin(c, &t, SEGKV_KERNEL_PREFILL);
   if (rc) return rc;
-  hipError_t e = c->prefill_kernel == kPrefillPipelined ? launch_prefill_sp(a, n_wgs, c->D, c->P, c->stream)
+  hipError_t e = c->prefill_kernel == kPrefillDuo         ? launch_prefill_duo(a, n_wgs, c->D, c->P, c->stream)
+                 : c->prefill_kernel == kPrefillPipelined ? launch_prefill_sp(a, n_wgs, c->D, c->P, c->stream)
                  : c->prefill_kernel == kPrefillTwoGroup ? launch_prefill_pp(a, n_wgs, c->D, c->P, c->stream)
                  : c->prefill_kernel == kPrefillWide   ? launch_prefill_wide(a, n_wgs, c->D, c->P, c->stream)
                                                        : launch_prefill(a, n_wgs, c->D, c->P, c->stream);
@@ -1705,9 +1725,11 @@ int segkv_set_tuning(segkv_ctx *c, int32_t knob, int64_t value) {
       c->prefill_order = value > 0 ? static_cast<int32_t>(value) : 0;
       return SEGKV_OK;
     case SEGKV_TUNE_PREFILL_KERNEL:
-      if (value > kPrefillPipelined)
-        return c->fail(SEGKV_E_INVAL,
-                       "prefill kernel must be 0 (default), 1 (8 x 32 rows), 2 (4 x 64 rows), 3 (two groups) or 4 (pipelined)");
+      if (value > kPrefillDuo)
+        return c->fail(SEGKV_E_INVAL, "prefill kernel must be 0 (default), 1 (8 x 32 rows), 2 (4 x 64 rows), "
+                                      "3 (two groups), 4 (pipelined) or 5 (two workgroups per CU)");
+      if (value == kPrefillDuo && c->G > kPrefillDuoRows)
+        return c->fail(SEGKV_E_INVAL, "prefill kernel 5 needs num_q_heads / num_kv_heads <= %d", kPrefillDuoRows);
       c->prefill_kernel = value > 0 ? static_cast<int32_t>(value) : 0;
       return SEGKV_OK;
     default:

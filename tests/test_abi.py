@@ -115,10 +115,10 @@ def test_tuning_knobs(lib):
     kv = S.SegKV(planning=True, **_cfg())
     kv.set_tuning(S.TUNE_DECODE_MIN_PAGES, 8)
     kv.set_tuning(S.TUNE_PREFILL_SPLIT_TILES, 0)
-    for v in (0, 1, 2, 3, 4):
+    for v in (0, 1, 2, 3, 4, 5):
         kv.set_tuning(S.TUNE_PREFILL_KERNEL, v)
     with pytest.raises(S.SegKVError):
-        kv.set_tuning(S.TUNE_PREFILL_KERNEL, 5)
+        kv.set_tuning(S.TUNE_PREFILL_KERNEL, 6)
     with pytest.raises(S.SegKVError):
         kv.set_tuning(7, 1)
 

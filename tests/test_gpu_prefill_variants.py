@@ -1,6 +1,7 @@
 """The prefill kernel variants (SEGKV_TUNE_PREFILL_KERNEL 2: four waves of
 64 rows; 3: two wave groups one phase apart over host-balanced item lists;
-4: the default's work software pipelined across tiles) against the fp64
+4: the default's work software pipelined across tiles; 5: two workgroups
+of 4 waves x 32 rows per CU over 128-row items) against the fp64
 oracle, to the same bar as the default kernel: bf16 outputs within max-abs
 2e-2 and LSE within 1e-3; bitwise repeatable."""
 
@@ -14,7 +15,7 @@ from gpu_helpers import compare, gpu_run
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = [2, 3, 4]
+VARIANTS = [2, 3, 4, 5]
 
 
 @pytest.fixture(scope="module", autouse=True)
