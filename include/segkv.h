@@ -187,7 +187,9 @@ int segkv_prefill(segkv_ctx *ctx, int32_t layer, int32_t n_seqs, const int32_t *
  * cached token of each sequence).  The visible pages of all (sequence, KV
  * head) segments are split evenly over the GPU's workgroups (a segment may
  * be split across several); partial results are merged with a log-sum-exp
- * combine.  num_q_heads / num_kv_heads must be <= 16.
+ * combine.  A work item takes up to 16 query heads of a KV group; a group of
+ * more (num_q_heads / num_kv_heads > 16) is taken as blocks of 16, each of
+ * which reads the segment's visible pages.
  *   q, o     device bf16 [n_seqs][num_q_heads][head_dim]
  *   lse      device fp32 [n_seqs][num_q_heads], or NULL
  */

@@ -17,7 +17,8 @@ namespace {
 // next; each covered piece yields either the final output (a segment held by
 // one piece) or a normalised fp32 partial merged later by combine_kernel.
 //
-// Per piece, the (up to 16) query heads of the KV group are the columns of
+// Per piece, the query heads of one block of the KV group (up to 16; a
+// larger group is split into blocks by the host) are the columns of
 // v_mfma_f32_16x16x32_bf16 (lane l holds operand row l % 16 and k-elements
 // 8*(l/16) .. +7; result lane l holds column l % 16 and rows 4*(l/16) ..
 // +3).  K rows and V^T channel rows go from HBM straight into operand
@@ -76,6 +77,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
       const DecodeItem it = a.items[pc];
       const SeqDesc sd = a.seqs[it.seq];
       const SegDesc sg = a.segs[it.seq * a.num_kv_heads + it.kv_head];
+      const int nh = min(kDecodeCols, G - it.head0);  // query heads (columns) of this item
       const int p = sd.kv_len - 1;
       const int W = sg.window;
       const int key_begin = sg.first_token + it.page_begin * P;
@@ -85,19 +87,19 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
 
       bf16x8 qv[NKK];
       {
-        // Unconditional loads (lanes past the group read its last head and
+        // Unconditional loads (lanes past the block read its last head and
         // are zeroed), so they are in flight together.
         const uint16_t *qrow =
-            a.q + (static_cast<size_t>(sd.q_start) * a.num_q_heads + it.kv_head * G + min(c16, G - 1)) * D;
+            a.q + (static_cast<size_t>(sd.q_start) * a.num_q_heads + it.kv_head * G + it.head0 + min(c16, nh - 1)) * D;
         if (sg.rope_off < 0) {
 #pragma unroll
           for (int kk = 0; kk < NKK; ++kk) {
             const u32x4 z = {0u, 0u, 0u, 0u};
             const u32x4 x = ld16(qrow + kk * 32 + u * 8);
-            qv[kk] = as_bf16x8(c16 < G ? x : z);
+            qv[kk] = as_bf16x8(c16 < nh ? x : z);
           }
         } else {
-          relocate_row<D, NKK>(qv, qrow, 32, u * 8, c16 < G, a.rope.tables + sg.rope_off, s_rope[wave], a.rope);
+          relocate_row<D, NKK>(qv, qrow, 32, u * 8, c16 < nh, a.rope.tables + sg.rope_off, s_rope[wave], a.rope);
         }
       }
 
@@ -229,8 +231,9 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
       const DecodeItem it = a.items[pc2];
       const SeqDesc sd = a.seqs[it.seq];
       const bool single = it.n_parts == 1;
-      const size_t out_row0 = static_cast<size_t>(sd.q_start) * a.num_q_heads + it.kv_head * G;
-      for (int e = tid; e < G * TPC; e += kDecodeThreads) {
+      const int nh = min(kDecodeCols, G - it.head0);
+      const size_t out_row0 = static_cast<size_t>(sd.q_start) * a.num_q_heads + it.kv_head * G + it.head0;
+      for (int e = tid; e < nh * TPC; e += kDecodeThreads) {
         const int cc = e / TPC, d0 = (e - cc * TPC) * 4;
         float mm = kNegInf;
 #pragma unroll

@@ -641,10 +641,11 @@ WsBound workspace_bound(const segkv_config *cfg, int64_t Q, int64_t slots) {
     p_part = std::max(p_part, pp);
   }
   const int64_t base_items = Hkv * nq_tiles;
-  // decode
-  const int64_t pieces = nseg + slots;
+  // decode: one piece per (segment, block of kDecodeCols query heads) plus one per share boundary
+  const int64_t nvseg = nseg * ceil_div(G, kDecodeCols);
+  const int64_t pieces = nvseg + slots;
   const size_t d_tables = align_up(seq_tables, 16) + align_up(sizeof(DecodeItem) * pieces, 16) +
-                          align_up(sizeof(int32_t) * (slots + 1), 16) + sizeof(CombineItem) * nseg;
+                          align_up(sizeof(int32_t) * (slots + 1), 16) + sizeof(CombineItem) * nvseg;
   const size_t d_part = static_cast<size_t>(pieces) * kDecodeCols * (D + 1) * sizeof(float);
   // top-k (the tables of max_seqs sequences)
   const size_t k_tables = align_up(sizeof(int32_t) * (S + 1), 16) + 2 * align_up(sizeof(int32_t) * S, 16);
@@ -1262,7 +1263,6 @@ int decode_impl(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_
   int rc = check_layer_seqs(c, layer, n_seqs, seq_ids);
   if (rc) return rc;
   if (n_seqs == 0) return SEGKV_OK;
-  if (c->G > kDecodeCols) return c->fail(SEGKV_E_INVAL, "decode supports num_q_heads / num_kv_heads <= %d", kDecodeCols);
   if (!q || !o) return c->fail(SEGKV_E_INVAL, "q / o is NULL");
   for (int32_t b = 0; b < n_seqs; ++b) {
     const SeqLayer &s = c->sl(layer, seq_ids[b]);
@@ -1271,12 +1271,17 @@ int decode_impl(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_
       return c->fail(SEGKV_E_INVAL, "seq %d: the last token was not appended as a query (n_query >= 1)", seq_ids[b]);
   }
   int32_t n_parts_total = 0;
-  // Stream-K plan: the visible pages of all segments, in (sequence, KV head)
-  // order, are cut into equal contiguous shares, one per workgroup (at most
-  // the GPU's resident decode workgroups, at least min_pages pages each).
+  // Stream-K plan: the visible pages of all segments, in (sequence, KV head,
+  // head block) order, are cut into equal contiguous shares, one per
+  // workgroup (at most the GPU's resident decode workgroups, at least
+  // min_pages pages each).  A work item takes up to kDecodeCols query heads
+  // of a KV group; a larger group is NB blocks of them, each reading the
+  // segment's pages.
   const int32_t P = c->P;
-  std::vector<int32_t> &seg_lo = c->scratch_i32;  // [n_seqs*Hkv][2]: first visible page, count
-  seg_lo.assign(static_cast<size_t>(n_seqs) * c->Hkv * 2, 0);
+  const int32_t NB = (c->G + kDecodeCols - 1) / kDecodeCols;
+  const int64_t nvs = static_cast<int64_t>(n_seqs) * c->Hkv * NB;  // (sequence, KV head, head block)
+  std::vector<int32_t> &seg_lo = c->scratch_i32;  // [nvs][2]: first visible page, count
+  seg_lo.assign(static_cast<size_t>(nvs) * 2, 0);
   int64_t total = 0;
   for (int32_t b = 0; b < n_seqs; ++b) {
     const SeqLayer &s = c->sl(layer, seq_ids[b]);
@@ -1287,23 +1292,32 @@ int decode_impl(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_
       const int32_t lo = w > 0 ? std::max(0, p - w + 1) : 0;
       const int32_t pg_lo = (lo - sg.first_token) / P;
       const int32_t pg_hi = (p - sg.first_token) / P + 1;
-      seg_lo[(static_cast<size_t>(b) * c->Hkv + g) * 2] = pg_lo;
-      seg_lo[(static_cast<size_t>(b) * c->Hkv + g) * 2 + 1] = pg_hi - pg_lo;
-      total += pg_hi - pg_lo;
+      for (int32_t hb = 0; hb < NB; ++hb) {
+        const size_t vs = (static_cast<size_t>(b) * c->Hkv + g) * NB + hb;
+        seg_lo[vs * 2] = pg_lo;
+        seg_lo[vs * 2 + 1] = pg_hi - pg_lo;
+        total += pg_hi - pg_lo;
+      }
     }
   }
   const int64_t slots = std::max<int64_t>(1, static_cast<int64_t>(c->num_cus) * kDecodeWgPerCu);
   const int64_t n_wg = std::max<int64_t>(1, std::min(slots, ceil_div(total, c->decode_pps)));
   std::vector<DecodeItem> ditems;
   std::vector<int32_t> wg_off;
-  ditems.reserve(static_cast<size_t>(n_wg + n_seqs * c->Hkv));
+  ditems.reserve(static_cast<size_t>(n_wg + nvs));
   wg_off.reserve(static_cast<size_t>(n_wg + 1));
   std::vector<CombineItem> &citems = c->scratch_citems;
   citems.clear();
   {
-    // first pass: pieces per segment (for part numbering)
-    const int64_t nseg = static_cast<int64_t>(n_seqs) * c->Hkv;
+    // first pass: pieces per segment and head block (for part numbering)
+    const int64_t nseg = nvs;
     std::vector<int32_t> seg_parts(static_cast<size_t>(nseg), 0), seg_part0(static_cast<size_t>(nseg), 0);
+    // (sequence, KV head, first query head of the block within the group) of virtual segment i
+    auto vseg = [&](int64_t i, int32_t *b, int32_t *g, int32_t *head0) {
+      *b = static_cast<int32_t>(i / (static_cast<int64_t>(c->Hkv) * NB));
+      *g = static_cast<int32_t>((i / NB) % c->Hkv);
+      *head0 = static_cast<int32_t>(i % NB) * kDecodeCols;
+    };
     auto share = [&](int64_t w) { return total * w / n_wg; };
     for (int pass = 0; pass < 2; ++pass) {
       int64_t si = 0, seg_start = 0;  // current segment and its first global page index
@@ -1322,12 +1336,13 @@ int decode_impl(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_
           if (!pass) {
             seg_parts[static_cast<size_t>(si)]++;
           } else {
-            const int32_t b = static_cast<int32_t>(si / c->Hkv), g = static_cast<int32_t>(si % c->Hkv);
+            int32_t b, g, head0;
+            vseg(si, &b, &g, &head0);
             const int32_t pg0 = seg_lo[static_cast<size_t>(si) * 2] + static_cast<int32_t>(pos - seg_start);
             const int32_t pg1 = seg_lo[static_cast<size_t>(si) * 2] + static_cast<int32_t>(stop - seg_start);
             const int32_t part = seg_part0[static_cast<size_t>(si)] + used[static_cast<size_t>(si)]++;
             ditems.push_back(DecodeItem{b, g, pg0, pg1, part, seg_part0[static_cast<size_t>(si)],
-                                        seg_parts[static_cast<size_t>(si)], 0});
+                                        seg_parts[static_cast<size_t>(si)], head0});
           }
           pos = stop;
         }
@@ -1338,9 +1353,10 @@ int decode_impl(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_
           seg_part0[static_cast<size_t>(i)] = acc;
           acc += seg_parts[static_cast<size_t>(i)];
           if (seg_parts[static_cast<size_t>(i)] > 1) {
-            const int32_t b = static_cast<int32_t>(i / c->Hkv), g = static_cast<int32_t>(i % c->Hkv);
+            int32_t b, g, head0;
+            vseg(i, &b, &g, &head0);
             citems.push_back(CombineItem{seg_part0[static_cast<size_t>(i)], seg_parts[static_cast<size_t>(i)], b, 1,
-                                         g * c->G, c->G, 0, 0});
+                                         g * c->G + head0, std::min(kDecodeCols, c->G - head0), 0, 0});
           }
         }
         n_parts_total = acc;
@@ -1411,7 +1427,7 @@ int decode_impl(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_
   TimedLaunch t2{};
   rc = timed_begin(c, &t2, SEGKV_KERNEL_COMBINE);
   if (rc) return rc;
-  e = launch_combine(ca, static_cast<int>(citems.size()), c->G, c->D, c->stream);
+  e = launch_combine(ca, static_cast<int>(citems.size()), std::min(kDecodeCols, c->G), c->D, c->stream);
   if (e != hipSuccess) return c->device_fail(e, "combine launch");
   return timed_end(c, &t2);
 }

@@ -23,7 +23,7 @@ constexpr int kPrefillRows = 256;  // (query position, query head) rows per pref
 constexpr int kPrefillThreads = 512;  // 8 waves, 32 rows each, two per SIMD
 constexpr int kPrefillWideThreads = 256;  // wide variant: 4 waves, 64 rows each, one per SIMD
 constexpr int kDecodeThreads = 512;  // 8 waves, two per SIMD
-constexpr int kDecodeCols = 16;    // query heads handled by one decode work item (GQA group, padded)
+constexpr int kDecodeCols = 16;    // query heads handled by one decode work item (a block of the GQA group, padded)
 constexpr int kDecodeSlots = 16;   // LDS partials of one decode workgroup: (piece, wave) pairs of a batch
 constexpr int kScatterThreads = 256;
 constexpr int kScatterCopyWgs = 16;  // most workgroups of a scatter launch that copy staged tables
@@ -108,7 +108,7 @@ struct DecodeItem {
   int32_t part;
   int32_t part_begin;
   int32_t n_parts;
-  int32_t pad0;
+  int32_t head0;  // first query head of the item's block within the KV group (a multiple of kDecodeCols)
 };
 
 // One combine workgroup: merge partial slots [part_begin, part_begin+n_parts)

@@ -119,6 +119,8 @@ def decode_workload(name, n, kv, hq, hkv, d, p, windows, seed):
     (4, (100, 1000, 2049, 77), 32, 2, 128, 32, (0, 300), 3),
     (2, 5000, 16, 1, 64, 64, (0,), 1),
     (2, 4097, 64, 4, 128, 16, (4096, 0, 100, 1), None),
+    (3, (900, 64, 2000), 48, 2, 128, 64, (0, 200), 8),      # G = 24: blocks of 16 and 8 query heads
+    (2, 3000, 64, 1, 64, 32, (0,), None),                   # G = 64 (one KV head): four blocks
 ])
 def test_decode_shapes(case):
     n, kv, hq, hkv, d, p, windows, pps = case
