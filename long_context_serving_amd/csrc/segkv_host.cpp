@@ -36,6 +36,9 @@ thread_local std::string g_create_error;
 constexpr int kStages = 32;     // pinned staging slots, used in ring order
 constexpr int kStageGroup = 8;  // slots covered by one completion event
 constexpr int kDefaultDecodeMinPages = 8;
+// Cost of one decode piece (its query load and partial merge) in keys of
+// streaming, from per-workgroup timings: about one 64-key chunk.
+constexpr int64_t kDecodePieceCostKeys = 64;
 constexpr size_t kPrestageRoom = 64 << 10;  // initial room for prefill tables staged by an append
 constexpr int kDefaultPrefillSplitTiles = 0;  // automatic
 constexpr int64_t kMinSplitTiles = 16;
@@ -1318,7 +1321,12 @@ int decode_impl(segkv_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_
       *g = static_cast<int32_t>((i / NB) % c->Hkv);
       *head0 = static_cast<int32_t>(i % NB) * kDecodeCols;
     };
-    auto share = [&](int64_t w) { return total * w / n_wg; };
+    // Shares of equal cost: pages plus one 64-key chunk's time per piece (a
+    // share's pieces each load their queries and merge their partial).
+    std::vector<int32_t> lens(static_cast<size_t>(nseg));
+    for (int64_t i = 0; i < nseg; ++i) lens[static_cast<size_t>(i)] = seg_lo[static_cast<size_t>(i) * 2 + 1];
+    const std::vector<int64_t> bnd = decode_share_bounds(lens, total, n_wg, ceil_div(kDecodePieceCostKeys, P));
+    auto share = [&](int64_t w) { return bnd[static_cast<size_t>(w)]; };
     for (int pass = 0; pass < 2; ++pass) {
       int64_t si = 0, seg_start = 0;  // current segment and its first global page index
       std::vector<int32_t> used(pass ? static_cast<size_t>(nseg) : 0, 0);

@@ -62,3 +62,58 @@ def test_ranges_match_greedy_assignment(driver, n_bins, cost):
         assert got == [i for i in range(len(cost)) if owner[i] == b]
     if len(cost) >= n_bins:
         assert all(off[b + 1] > off[b] for b in range(n_bins)), "a workgroup was left without items"
+
+
+# ---------------------------------------------------------------- decode cut
+
+def decode_bounds(exe, n_wg, piece_cost, lens):
+    out = subprocess.run([exe, "decode"], input=f"{n_wg} {piece_cost} {len(lens)} " + " ".join(map(str, lens)),
+                         capture_output=True, text=True, check=True).stdout.split()
+    return [int(x) for x in out]
+
+
+def share_costs(bnd, lens, piece_cost):
+    """Each share's pages plus piece_cost per segment it intersects (direct
+    interval count)."""
+    starts = np.concatenate([[0], np.cumsum(lens)])
+    costs = []
+    for a, b in zip(bnd, bnd[1:]):
+        pieces = sum(1 for i in range(len(lens)) if starts[i] < b and starts[i + 1] > a)
+        costs.append((b - a) + piece_cost * pieces)
+    return costs
+
+
+def decode_32k_lens():
+    # 31 sequences of 32,769 keys on 64-key pages: 1 global head (513 pages), 7 local (W 4096: 65 pages)
+    return [513] + [65] * 7
+
+
+@pytest.mark.parametrize("n_wg,piece_cost,lens", [
+    (256, 1, decode_32k_lens() * 31),
+    (256, 0, decode_32k_lens() * 31),
+    (7, 2, [5, 1, 1, 30, 2, 2, 9]),
+    (3, 4, [100]),                                   # one segment, more shares than pieces needed
+    (40, 1, list(np.random.default_rng(3).integers(1, 300, 500))),
+    (1, 1, [4, 4]),
+])
+def test_decode_shares_cover_the_list_in_order(driver, n_wg, piece_cost, lens):
+    bnd = decode_bounds(driver, n_wg, piece_cost, lens)
+    assert len(bnd) == n_wg + 1 and bnd[0] == 0 and bnd[-1] == sum(lens)
+    assert all(a <= b for a, b in zip(bnd, bnd[1:]))
+    if piece_cost == 0:
+        assert bnd == [sum(lens) * w // n_wg for w in range(n_wg + 1)]
+
+
+@pytest.mark.parametrize("n_wg,lens", [
+    (256, decode_32k_lens() * 31),
+    (40, list(np.random.default_rng(3).integers(1, 300, 500))),
+    (100, list(np.random.default_rng(4).integers(50, 600, 60))),
+])
+def test_decode_shares_even_out_piece_costs(driver, n_wg, lens):
+    """With a piece cost, the dearest share costs less than with equal page
+    counts, and no share is more than two pieces' cost above the mean."""
+    c = 1
+    even = share_costs(decode_bounds(driver, n_wg, 0, lens), lens, c)
+    cut = share_costs(decode_bounds(driver, n_wg, c, lens), lens, c)
+    assert max(cut) <= max(even)
+    assert max(cut) <= np.mean(cut) + 2 * c + 1
