@@ -334,8 +334,8 @@ hipError_t launch_combine(const CombineArgs &a, int n_items, int max_entries, in
   if (n_items <= 0) return hipSuccess;
   const int epp = 256 / (head_dim / 4);
   const dim3 grid(n_items, (max_entries + epp - 1) / epp);
-  if (head_dim == 64) hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(256), 0, s, a);
-  else if (head_dim == 128) hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(256), 0, s, a);
+  if (head_dim == 64) SEGKV_LAUNCH(combine_kernel<64>, grid, dim3(256), s, a);
+  else if (head_dim == 128) SEGKV_LAUNCH(combine_kernel<128>, grid, dim3(256), s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -260,11 +260,11 @@ struct PrefillLds {
 // unsupported pair returns hipErrorInvalidValue from the calling launcher.
 #define SEGKV_DISPATCH_DP(KERNEL, D, P, GRID, BLOCK, STREAM, ARGS)                                \
   do {                                                                                           \
-    if ((D) == 64 && (P) == 16) hipLaunchKernelGGL((KERNEL<64, 16>), GRID, BLOCK, 0, STREAM, ARGS); \
-    else if ((D) == 64 && (P) == 32) hipLaunchKernelGGL((KERNEL<64, 32>), GRID, BLOCK, 0, STREAM, ARGS); \
-    else if ((D) == 64 && (P) == 64) hipLaunchKernelGGL((KERNEL<64, 64>), GRID, BLOCK, 0, STREAM, ARGS); \
-    else if ((D) == 128 && (P) == 16) hipLaunchKernelGGL((KERNEL<128, 16>), GRID, BLOCK, 0, STREAM, ARGS); \
-    else if ((D) == 128 && (P) == 32) hipLaunchKernelGGL((KERNEL<128, 32>), GRID, BLOCK, 0, STREAM, ARGS); \
-    else if ((D) == 128 && (P) == 64) hipLaunchKernelGGL((KERNEL<128, 64>), GRID, BLOCK, 0, STREAM, ARGS); \
+    if ((D) == 64 && (P) == 16) SEGKV_LAUNCH((KERNEL<64, 16>), GRID, BLOCK, STREAM, ARGS); \
+    else if ((D) == 64 && (P) == 32) SEGKV_LAUNCH((KERNEL<64, 32>), GRID, BLOCK, STREAM, ARGS); \
+    else if ((D) == 64 && (P) == 64) SEGKV_LAUNCH((KERNEL<64, 64>), GRID, BLOCK, STREAM, ARGS); \
+    else if ((D) == 128 && (P) == 16) SEGKV_LAUNCH((KERNEL<128, 16>), GRID, BLOCK, STREAM, ARGS); \
+    else if ((D) == 128 && (P) == 32) SEGKV_LAUNCH((KERNEL<128, 32>), GRID, BLOCK, STREAM, ARGS); \
+    else if ((D) == 128 && (P) == 64) SEGKV_LAUNCH((KERNEL<128, 64>), GRID, BLOCK, STREAM, ARGS); \
     else return hipErrorInvalidValue;                                                            \
   } while (0)

@@ -88,8 +88,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
 
 hipError_t launch_merge(const MergeArgs &a, int n_wgs, int head_dim, hipStream_t s) {
   if (n_wgs <= 0 || a.n_pairs <= 0) return hipSuccess;
-  if (head_dim == 64) hipLaunchKernelGGL(merge_kernel<64>, dim3(n_wgs), dim3(kMergeThreads), 0, s, a);
-  else if (head_dim == 128) hipLaunchKernelGGL(merge_kernel<128>, dim3(n_wgs), dim3(kMergeThreads), 0, s, a);
+  if (head_dim == 64) SEGKV_LAUNCH(merge_kernel<64>, dim3(n_wgs), dim3(kMergeThreads), s, a);
+  else if (head_dim == 128) SEGKV_LAUNCH(merge_kernel<128>, dim3(n_wgs), dim3(kMergeThreads), s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

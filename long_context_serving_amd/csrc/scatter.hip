@@ -129,8 +129,8 @@ hipError_t launch_scatter(const ScatterArgs &a, int n_items, int head_dim, int p
 hipError_t launch_upload(void *dst, const void *src_pinned, size_t bytes, hipStream_t s) {
   const size_t n16 = (bytes + 15) / 16;
   if (n16 == 0) return hipSuccess;
-  hipLaunchKernelGGL(upload_kernel, dim3(static_cast<unsigned>((n16 + 255) / 256)), dim3(256), 0, s,
-                     static_cast<uint4 *>(dst), static_cast<const uint4 *>(src_pinned), n16);
+  SEGKV_LAUNCH(upload_kernel, dim3(static_cast<unsigned>((n16 + 255) / 256)), dim3(256), s,
+               static_cast<uint4 *>(dst), static_cast<const uint4 *>(src_pinned), n16);
   return hipGetLastError();
 }
 

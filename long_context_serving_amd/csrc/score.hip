@@ -535,13 +535,13 @@ hipError_t launch_score(const ScoreArgs &a, int n_wgs, int head_dim, int page_si
 
 hipError_t launch_score_reduce(const ScoreReduceArgs &a, hipStream_t s) {
   if (a.n_rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(score_reduce_kernel, dim3(a.n_rows), dim3(64 * kReduceWaves), 0, s, a);
+  SEGKV_LAUNCH(score_reduce_kernel, dim3(a.n_rows), dim3(64 * kReduceWaves), s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_topk(const TopkArgs &a, int n_seqs, hipStream_t s) {
   if (n_seqs <= 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_kernel, dim3(n_seqs), dim3(kTopkThreads), 0, s, a);
+  SEGKV_LAUNCH(topk_kernel, dim3(n_seqs), dim3(kTopkThreads), s, a);
   return hipGetLastError();
 }
 

@@ -29,6 +29,11 @@
 
 using namespace segkv;
 
+segkv::LaunchEvents &segkv::launch_events() {
+  static thread_local LaunchEvents ev;
+  return ev;
+}
+
 namespace {
 
 thread_local std::string g_create_error;
@@ -297,8 +302,13 @@ int upload(segkv_ctx *c, int slot, size_t bytes, char *dst) {
 
 // ---- timing --------------------------------------------------------------
 
+// A timed launch: timed_begin takes two events from the pool and hands them
+// to the next launch on this thread, whose dispatch stamps the kernel's own
+// start and end; timed_end takes them back (a launcher that had nothing to
+// launch leaves them unused, and they return to the pool).
 int timed_begin(segkv_ctx *c, TimedLaunch *t, int kernel) {
   t->kernel = -1;
+  launch_events() = LaunchEvents{};
   if (!(c->timing_mask & (1 << kernel))) return SEGKV_OK;
   t->kernel = kernel;
   for (hipEvent_t *ev : {&t->start, &t->stop}) {
@@ -310,16 +320,20 @@ int timed_begin(segkv_ctx *c, TimedLaunch *t, int kernel) {
       if (e != hipSuccess) return c->device_fail(e, "hipEventCreate");
     }
   }
-  hipError_t e = hipEventRecord(t->start, c->stream);
-  if (e != hipSuccess) return c->device_fail(e, "hipEventRecord");
+  launch_events() = LaunchEvents{t->start, t->stop, false};
   return SEGKV_OK;
 }
 
 int timed_end(segkv_ctx *c, TimedLaunch *t) {
+  const bool used = launch_events().used;
+  launch_events() = LaunchEvents{};
   if (t->kernel < 0) return SEGKV_OK;
-  hipError_t e = hipEventRecord(t->stop, c->stream);
-  if (e != hipSuccess) return c->device_fail(e, "hipEventRecord");
-  c->pending.push_back(*t);
+  if (used) {
+    c->pending.push_back(*t);
+  } else {
+    c->event_pool.push_back(t->start);
+    c->event_pool.push_back(t->stop);
+  }
   return SEGKV_OK;
 }
 

@@ -2,12 +2,32 @@
 // constants they take are in segkv_internal.h.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "segkv_internal.h"
 
 namespace segkv {
+
+// Timing events for the next launch on the calling thread.  When the host
+// times a kernel it sets them; the launch hands them to the dispatch itself
+// (hipExtLaunchKernelGGL), which stamps the kernel's own start and end, so
+// the elapsed time is the kernel's execution without the cost of separate
+// event-record commands.  `used` tells the host that a launch took them.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool used = false;
+};
+LaunchEvents &launch_events();
+
+// Every kernel of the library is launched through this.
+#define SEGKV_LAUNCH(KERNEL, GRID, BLOCK, STREAM, ...)                                                  \
+  do {                                                                                                 \
+    ::segkv::LaunchEvents &ev_ = ::segkv::launch_events();                                             \
+    ev_.used = ev_.start != nullptr;                                                                   \
+    hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, 0, STREAM, ev_.start, ev_.stop, 0, __VA_ARGS__);        \
+  } while (0)
 
 // Shape of the two-workgroup prefill variant (prefill_variants.hip): 4 waves
 // of 32 rows per workgroup, 128 rows per work item, two workgroups per CU.
