@@ -129,7 +129,13 @@ typedef struct segkv_config {
 size_t segkv_workspace_bytes(const segkv_config *cfg, int32_t max_batch_q_tokens);
 
 /*
- * Create a context.  k_pool and v_pool both NULL gives a planning-only
+ * Create a context: the head-class table (one window per (layer, KV head),
+ * 0 = global: "Xiaohongshu Open-Sources RedKnot" page, "What Happened",
+ * item 1, where each (layer, head) is classified offline as global or as
+ * local with a sliding window) and the page pool of the per-(layer, head)
+ * segmented storage (same page, item 3; "RedKnot: Head-Aware KV Reuse and
+ * SegPagedAttention" page, "The Three Core Mechanisms in Detail", third
+ * mechanism).  k_pool and v_pool both NULL gives a planning-only
  * context: it keeps the page allocator and tables on the host and makes no
  * HIP call at all (appends take k_new = v_new = NULL; prefill and decode
  * return SEGKV_E_STATE).  Returns SEGKV_OK and *out, or an error with *out =
@@ -142,7 +148,11 @@ void segkv_destroy(segkv_ctx *ctx);
 
 /*
  * Append new KV rows to n_seqs sequences of one layer and allocate their
- * pages.
+ * pages: each head's segment holds only the tokens that head needs
+ * ("Xiaohongshu Open-Sources RedKnot" page, "What Happened", item 3), and
+ * the kept blocks are paged without further copies ("RedKnot's Long-Context
+ * Speedup Matters for AI Workflows" page, "Head-level split changes cache
+ * behavior").
  *   seq_ids  host int32 [n_seqs], distinct, each in [0, max_seqs)
  *   cu_new   host int32 [n_seqs + 1], prefix sums of the new-token counts
  *   n_query  host int32 [n_seqs]: the last n_query[b] appended tokens of
@@ -170,7 +180,13 @@ int segkv_append_pages(segkv_ctx *ctx, int32_t layer, int32_t n_seqs, const int3
                        const void *v_new);
 
 /*
- * Varlen prefill attention of n_seqs sequences of one layer.
+ * Varlen prefill attention of n_seqs sequences of one layer: the fused
+ * variable-length attention over the per-head segment pages, global heads
+ * over the full causal context and local heads over their window only
+ * ("Xiaohongshu Open-Sources RedKnot" page, "What Happened", items 1 and 3).
+ * Result: o = softmax(scale q k^T) v per (query, query head) over the keys
+ * that head sees, lse = ln of that softmax's denominator (natural log, with
+ * the scale applied).
  *   seq_ids  host int32 [n_seqs]
  *   cu_q     host int32 [n_seqs + 1], prefix sums of q_len; q_len may be 0;
  *            each q_len must not reach before that sequence's earliest
@@ -184,7 +200,10 @@ int segkv_prefill(segkv_ctx *ctx, int32_t layer, int32_t n_seqs, const int32_t *
 
 /*
  * One-token decode of n_seqs sequences of one layer (the query is the last
- * cached token of each sequence).  The visible pages of all (sequence, KV
+ * cached token of each sequence): the same attention as segkv_prefill for
+ * one query row ("Xiaohongshu Open-Sources RedKnot" page, "What Happened",
+ * items 1 and 3).  The pages give no decode kernel; the split over
+ * workgroups and the combine below are this library's design.  The visible pages of all (sequence, KV
  * head) segments are split evenly over the GPU's workgroups (a segment may
  * be split across several); partial results are merged with a log-sum-exp
  * combine.  A work item takes up to 16 query heads of a KV group; a group of
